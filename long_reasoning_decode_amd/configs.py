@@ -1,0 +1,102 @@
+"""Workload shapes for the BeaconKV eviction step.
+
+Each workload is one eviction over every (layer, batch, KV head) unit of a
+model-shaped KV cache that has grown to ``n_len = budget + n_new`` rows.  The
+hyper-parameters follow the BeaconKV reading notes (liuzhao09.github.io,
+"BeaconKV：用历史查询代表保护长推理的远程回看"): 16 recent + 16 beacon queries
+(§2.2 Eq. 9, §3.3 Table 1), a query buffer that grows to 32 and is sampled back
+to 16 (§2.2), periodic eviction of a fixed-size block of new rows (§2.1,
+Fig. 5).  The model shapes are those of the evaluated models (§3.1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+
+@dataclass(frozen=True)
+class EvictConfig:
+    name: str
+    n_layers: int
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    theta: float
+    budget: int            # B_KV^min: rows kept
+    n_new: int             # rows added since the previous eviction
+    n_prefix: int          # forced prefix keep
+    n_recent_kv: int       # forced recent-window keep
+    n_beacon: int = 16     # B_Q^min
+    n_recent_q: int = 16   # recent queries; B_Q^max = n_beacon + n_recent_q
+    t_lo: int = 4096       # current step t per batch element ~ U[t_lo, t_hi]
+    t_hi: int = 32768
+    mix: str = "clusters8"  # query distribution, see synth.py
+    seed: int = 20261202
+    qcap: int = 32         # rows allocated per query buffer
+
+    @property
+    def n_len(self) -> int:
+        return self.budget + self.n_new
+
+    @property
+    def cap(self) -> int:
+        return self.n_len
+
+    @property
+    def G(self) -> int:
+        return self.hq // self.hkv
+
+    @property
+    def units(self) -> int:
+        return self.n_layers * self.batch * self.hkv
+
+    @property
+    def qbufs(self) -> int:
+        return self.n_layers * self.batch * self.hq
+
+    @property
+    def rope_rows(self) -> int:
+        return self.t_hi + 1
+
+    def scaled(self, **kw) -> "EvictConfig":
+        return replace(self, **kw)
+
+
+TINY = EvictConfig(
+    name="tiny", n_layers=1, batch=1, hq=4, hkv=2, d=64, theta=1e4,
+    budget=128, n_new=32, n_prefix=8, n_recent_kv=16,
+    t_lo=1000, t_hi=1000, mix="tight3", seed=20261202 + 100)
+
+QWEN3_4B = EvictConfig(
+    name="qwen3-4b", n_layers=36, batch=16, hq=32, hkv=8, d=128, theta=1e6,
+    budget=2048, n_new=128, n_prefix=4, n_recent_kv=16,
+    t_lo=4096, t_hi=32768, seed=20261202 + 200)
+
+R1_QWEN_7B = EvictConfig(
+    name="r1-distill-qwen-7b", n_layers=28, batch=64, hq=28, hkv=4, d=128, theta=1e4,
+    budget=1024, n_new=128, n_prefix=4, n_recent_kv=16,
+    t_lo=2048, t_hi=32768, seed=20261202 + 300)
+
+QWEN3_14B_1K = EvictConfig(
+    name="qwen3-14b-b1024", n_layers=40, batch=32, hq=40, hkv=8, d=128, theta=1e6,
+    budget=1024, n_new=128, n_prefix=4, n_recent_kv=16,
+    t_lo=4096, t_hi=32768, seed=20261202 + 400)
+
+QWEN3_14B_4K = EvictConfig(
+    name="qwen3-14b-b4096", n_layers=40, batch=32, hq=40, hkv=8, d=128, theta=1e6,
+    budget=4096, n_new=128, n_prefix=4, n_recent_kv=16,
+    t_lo=4223, t_hi=32768, seed=20261202 + 410)
+
+EVICT_CONFIGS = {c.name: c for c in (TINY, QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, QWEN3_14B_4K)}
+
+
+@dataclass(frozen=True)
+class StreamConfig:
+    """Streaming decode: per-step buffer update, eviction every n_new steps."""
+    name: str = "stream-qwen3-4b"
+    base: EvictConfig = replace(QWEN3_4B, batch=192, seed=20261202 + 500)
+    steps: int = 32768
+    drift_every: int = 2048
+
+
+STREAM = StreamConfig()

@@ -1,0 +1,236 @@
+"""CPU oracle for the BeaconKV eviction step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It wraps ``liboracle.so`` (plain C, see
+``bkv_oracle.c``) with ctypes and takes/returns numpy arrays; bf16 data is
+passed as ``uint16`` bit patterns.  It shares no code with the HIP library.
+
+Array layouts (unit-major; a unit is one (layer, batch, KV head), its G query
+heads follow it):
+    K, V        [U, cap, d]            uint16 (bf16), K holds post-RoPE keys
+    qbuf        [U, G, qcap, d]        uint16, pre-RoPE query buffers
+    qcount      [U, G]                 int32
+    q_recent    [U, G, n_recent_q, d]  uint16, pre-RoPE recent queries
+    pos_recent  [U, n_recent_q]        int32
+    t           [U]                    int32
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+class _Cfg(C.Structure):
+    _fields_ = [(n, C.c_int) for n in (
+        "n_layers", "batch", "hq", "hkv", "d", "cap", "budget", "n_prefix",
+        "n_recent_kv", "n_beacon", "n_recent_q", "causal", "qcap")] + [("theta", C.c_double)]
+
+
+@dataclass
+class OracleCfg:
+    hq: int
+    hkv: int
+    d: int
+    cap: int
+    budget: int
+    n_prefix: int
+    n_recent_kv: int
+    n_beacon: int
+    n_recent_q: int
+    theta: float
+    qcap: int = 32
+    causal: int = 1
+    n_layers: int = 1
+    batch: int = 1
+
+    def c(self) -> _Cfg:
+        return _Cfg(self.n_layers, self.batch, self.hq, self.hkv, self.d, self.cap,
+                    self.budget, self.n_prefix, self.n_recent_kv, self.n_beacon,
+                    self.n_recent_q, self.causal, self.qcap, float(self.theta))
+
+    @property
+    def G(self) -> int:
+        return self.hq // self.hkv
+
+
+def lib():
+    """Load liboracle.so, building it with gcc if it is not there yet."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = C.CDLL(_LIB_PATH)
+        P = C.c_void_p
+        i32 = C.c_int
+        L.bkvo_f32_to_bf16.argtypes = [C.c_float]
+        L.bkvo_f32_to_bf16.restype = C.c_uint16
+        L.bkvo_rope_table.argtypes = [C.c_double, i32, i32, i32, P]
+        L.bkvo_rope_row.argtypes = [P, i32, C.c_double, i32, P]
+        L.bkvo_fps.argtypes = [P, i32, i32, i32, P]
+        L.bkvo_fps.restype = i32
+        L.bkvo_fps_f64.argtypes = [P, i32, i32, i32, P, P]
+        L.bkvo_fps_f64.restype = i32
+        L.bkvo_fps_update.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
+        L.bkvo_row_weights.argtypes = [P, P, i32, i32, i32, P]
+        L.bkvo_row_weights.restype = C.c_double
+        L.bkvo_select.argtypes = [P, i32, i32, i32, i32, P]
+        L.bkvo_select.restype = i32
+        L.bkvo_score.argtypes = [P, i32, i32, P, P, P, P, P, P, P, i32]
+        L.bkvo_evict.argtypes = [P, i32, i32, P, P, P, P, P, P, P, P, P, P, P, i32]
+        L.bkvo_merge.argtypes = [P, i32, P, P, P, P]
+        L.bkvo_compact.argtypes = [P, i32, i32, P, P, P]
+        L.bkvo_cfg_size.restype = i32
+        assert L.bkvo_cfg_size() == C.sizeof(_Cfg), "oracle cfg struct mismatch"
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# --------------------------------------------------------------------------
+def f32_to_bf16(x) -> np.ndarray:
+    """Round fp32 values to bf16 codes (nearest, ties to even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = lib().bkvo_f32_to_bf16
+    out = np.fromiter((f(float(v)) for v in x.ravel()), dtype=np.uint16, count=x.size)
+    return out.reshape(x.shape)
+
+
+def bf16_to_f32(x) -> np.ndarray:
+    x = _u16(x)
+    return (x.astype(np.uint32) << 16).view(np.float32)
+
+
+def rope_table(theta: float, d: int, p0: int, p1: int) -> np.ndarray:
+    out = np.empty((p1 - p0, d // 2, 2), dtype=np.float32)
+    lib().bkvo_rope_table(float(theta), d, p0, p1, _p(out))
+    return out
+
+
+def rope_row(x, theta: float, p: int) -> np.ndarray:
+    x = _u16(x)
+    y = np.empty_like(x)
+    lib().bkvo_rope_row(_p(x), x.shape[-1], float(theta), int(p), _p(y))
+    return y
+
+
+def fps(X, m: int) -> list[int]:
+    X = _u16(X)
+    n, d = X.shape
+    sel = np.empty(max(n, 1), dtype=np.int32)
+    got = lib().bkvo_fps(_p(X), n, d, m, _p(sel))
+    return sel[:got].tolist()
+
+
+def fps_f64(X, m: int):
+    X = _u16(X)
+    n, d = X.shape
+    sel = np.empty(max(n, 1), dtype=np.int32)
+    mar = np.empty(max(n, 1), dtype=np.float64)
+    got = lib().bkvo_fps_f64(_p(X), n, d, m, _p(sel), _p(mar))
+    return sel[:got].tolist(), mar[:got].copy()
+
+
+def fps_update(qbuf, qcount, q_new, n_beacon: int, n_recent_q: int) -> np.ndarray:
+    """In place on qbuf [nbuf, qcap, d] and qcount [nbuf]; returns sel [nbuf, n_beacon]."""
+    assert qbuf.dtype == np.uint16 and qbuf.flags["C_CONTIGUOUS"]
+    assert qcount.dtype == np.int32 and qcount.flags["C_CONTIGUOUS"]
+    nbuf, qcap, d = qbuf.shape
+    q_new = _u16(q_new).reshape(nbuf, d)
+    sel = np.empty((nbuf, n_beacon), dtype=np.int32)
+    lib().bkvo_fps_update(nbuf, qcap, d, n_beacon, n_recent_q, _p(qbuf), _p(qcount), _p(q_new), _p(sel))
+    return sel
+
+
+def row_weights(q, K, vis: int | None = None):
+    """Softmax weights of one (already rotated) query row over K [N, d]."""
+    q = _u16(q)
+    K = _u16(K)
+    N, d = K.shape
+    w = np.empty(N, dtype=np.float64)
+    c = lib().bkvo_row_weights(_p(q), _p(K), N, d, N - 1 if vis is None else vis, _p(w))
+    return w, c
+
+
+def select(score, budget: int, n_prefix: int, n_recent_kv: int):
+    s = np.ascontiguousarray(score, dtype=np.float64)
+    idx = np.empty(budget, dtype=np.int32)
+    moved = lib().bkvo_select(_p(s), s.shape[0], budget, n_prefix, n_recent_kv, _p(idx))
+    return idx, moved
+
+
+def score(cfg: OracleCfg, K, qbuf, qcount, q_recent, pos_recent, t, n_len: int | None = None,
+          nthreads: int | None = None) -> np.ndarray:
+    K = _u16(K)
+    U = K.shape[0]
+    N = cfg.cap if n_len is None else n_len
+    out = np.empty((U, N), dtype=np.float64)
+    cc = cfg.c()
+    lib().bkvo_score(C.byref(cc), U, N, _p(K), _p(_u16(qbuf)), _p(_i32(qcount)), _p(_u16(q_recent)),
+                     _p(_i32(pos_recent)), _p(_i32(t)), _p(out), nthreads or default_threads())
+    return out
+
+
+def evict(cfg: OracleCfg, K, V, qbuf, qcount, q_recent, pos_recent, t, n_len: int | None = None,
+          nthreads: int | None = None) -> dict:
+    """Full eviction, in place on K, V, qbuf, qcount (numpy arrays, C-contiguous)."""
+    for a, dt in ((K, np.uint16), (V, np.uint16), (qbuf, np.uint16), (qcount, np.int32)):
+        assert a.dtype == dt and a.flags["C_CONTIGUOUS"]
+    U = K.shape[0]
+    N = cfg.cap if n_len is None else n_len
+    idx = np.empty((U, cfg.budget), dtype=np.int32)
+    scores = np.empty((U, N), dtype=np.float64)
+    moved = np.empty(U, dtype=np.int32)
+    fps_sel = np.empty((U, cfg.G, cfg.n_beacon), dtype=np.int32)
+    cc = cfg.c()
+    lib().bkvo_evict(C.byref(cc), U, N, _p(K), _p(V), _p(qbuf), _p(qcount), _p(_u16(q_recent)),
+                     _p(_i32(pos_recent)), _p(_i32(t)), _p(idx), _p(scores), _p(moved), _p(fps_sel),
+                     nthreads or default_threads())
+    return {"idx": idx, "scores": scores, "moved": moved, "fps_sel": fps_sel}
+
+
+def merge(cfg: OracleCfg, qbuf, qcount, q_recent) -> np.ndarray:
+    assert qbuf.dtype == np.uint16 and qbuf.flags["C_CONTIGUOUS"]
+    assert qcount.dtype == np.int32 and qcount.flags["C_CONTIGUOUS"]
+    U = qbuf.shape[0]
+    fps_sel = np.empty((U, cfg.G, cfg.n_beacon), dtype=np.int32)
+    cc = cfg.c()
+    lib().bkvo_merge(C.byref(cc), U, _p(qbuf), _p(qcount), _p(_u16(q_recent)), _p(fps_sel))
+    return fps_sel
+
+
+def compact(cfg: OracleCfg, K, V, idx, n_len: int | None = None) -> None:
+    U = K.shape[0]
+    N = cfg.cap if n_len is None else n_len
+    cc = cfg.c()
+    lib().bkvo_compact(C.byref(cc), U, N, _p(K), _p(V), _p(_i32(idx)))

@@ -1,0 +1,616 @@
+/*
+ * bkv_oracle.c -- CPU oracle for the BeaconKV eviction step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library under long_reasoning_decode_amd/) never calls it and shares no
+ * code, header, table or constant with it.
+ *
+ * Sources (cited by page title and section; "Notes" below means the reading
+ * notes "BeaconKV：用历史查询代表保护长推理的远程回看" on liuzhao09.github.io,
+ * "Summary" means the rcap.io post "BeaconKV: Key-Value Cache Compression
+ * Guided by Beacon Queries"):
+ *   Notes §2.1, Eq. 4-6     attention weights w_{tau,j}, max pooling s_j^max
+ *   Notes §2.2, App. Alg. 1 farthest point sampling (FPS)
+ *   Notes §2.2, Eq. 9       continual FPS buffer bounds B_Q^min / B_Q^max
+ *   Notes §2.2, App. Alg. 2 cycle: freeze beacons, collect recents, evict,
+ *                           merge beacons + recents by FPS
+ *   Notes §2.3, Eq. 7-8     RoPE realignment, GQA max-pool score, keep set
+ *   Summary, pseudocode     per-step order: append, FPS when >= 32, evict
+ *
+ * Precision.  Scores are computed in fp64 (their plain definition).  Two
+ * steps produce integers or bf16 codes from floating point, so they are
+ * specified in fp32 with a fixed operation order, which the GPU kernels
+ * reproduce exactly:
+ *   - RoPE rotation of a bf16 query, rounded to bf16 (round to nearest even);
+ *   - FPS cosines, mean cosines and argmin decisions.
+ * This file must be compiled with -ffp-contract=off (see oracle/build.py).
+ *
+ * Pins: every function here is checked in tests/test_oracle_*.py against
+ * closed forms, hand-derived cases, library routines or brute force.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Configuration of one call: its own definition, not the library's struct. */
+typedef struct {
+    int n_layers, batch, hq, hkv, d;
+    int cap;          /* rows allocated per unit's K/V */
+    int budget;       /* B_KV^min: rows kept */
+    int n_prefix;     /* forced prefix keep */
+    int n_recent_kv;  /* forced recent-window keep */
+    int n_beacon;     /* B_Q^min */
+    int n_recent_q;   /* recent queries; B_Q^max = n_beacon + n_recent_q */
+    int causal;       /* recent query i sees only slots <= N - n_recent_q + i */
+    int qcap;         /* rows allocated per query buffer (>= B_Q^max) */
+    double theta;     /* RoPE base */
+} bkvo_cfg;
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> fp32.                                                            */
+
+static float bf2f(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t f2u(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/* Round an fp32 value to the nearest bf16, ties to the even code.
+ * Written from the definition: the two bf16 neighbours are the truncation
+ * and the next code away from zero; pick the nearer in exact (fp64)
+ * arithmetic, on a tie the one whose last mantissa bit is 0.  NaN maps to a
+ * quiet NaN of the same sign; values that round beyond the largest finite
+ * bf16 become infinity (the next code above 0x7F7F is 0x7F80). */
+uint16_t bkvo_f32_to_bf16(float f)
+{
+    uint32_t u = f2u(f);
+    if (isnan(f))
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+    uint16_t lo = (uint16_t)(u >> 16);          /* truncation toward zero */
+    if ((u & 0xFFFFu) == 0)
+        return lo;                               /* exact */
+    uint16_t hi = (uint16_t)(lo + 1);            /* next code away from zero */
+    double x = fabs((double)f);
+    double vlo = fabs((double)bf2f(lo));
+    double vhi;
+    if ((hi & 0x7FFFu) == 0x7F80u)               /* rounding up reaches inf */
+        vhi = ldexp(1.0, 128);                   /* the value inf stands for */
+    else
+        vhi = fabs((double)bf2f(hi));
+    double dlo = x - vlo, dhi = vhi - x;
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return hi;
+    return (lo & 1u) ? hi : lo;                  /* tie: even code */
+}
+
+/* ------------------------------------------------------------------------ */
+/* RoPE (Notes §2.3: beacons rotated to step t, recents to their own
+ * positions).  The pages only name RoPE(q, t); the convention taken is the
+ * one of the model families they evaluate: pairs (i, i + d/2) rotated by the
+ * angle p * theta^(-2i/d), i < d/2.                                         */
+
+/* cs[((p - p0) * (d/2) + i) * 2 + {0,1}] = {cos, sin} of p * theta^(-2i/d),
+ * computed in fp64 and rounded to fp32. */
+void bkvo_rope_table(double theta, int d, int p0, int p1, float *cs)
+{
+    int h = d / 2;
+    for (int p = p0; p < p1; ++p) {
+        for (int i = 0; i < h; ++i) {
+            double freq = pow(theta, -2.0 * (double)i / (double)d);
+            double ang = (double)p * freq;
+            float *o = cs + ((size_t)(p - p0) * h + i) * 2;
+            o[0] = (float)cos(ang);
+            o[1] = (float)sin(ang);
+        }
+    }
+}
+
+/* Rotate one bf16 row by the fp32 table row cs_p (d/2 {cos, sin} pairs), in
+ * fp32 with each product and sum rounded separately, then round to bf16. */
+static void rope_row_with(const uint16_t *x, int d, const float *cs_p, uint16_t *y)
+{
+    int h = d / 2;
+    for (int i = 0; i < h; ++i) {
+        float c = cs_p[2 * i], s = cs_p[2 * i + 1];
+        float a = bf2f(x[i]), b = bf2f(x[i + h]);
+        float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+        float y0 = ac - bs;
+        float y1 = bc + as;
+        y[i] = bkvo_f32_to_bf16(y0);
+        y[i + h] = bkvo_f32_to_bf16(y1);
+    }
+}
+
+/* Rotate one row at position p (table row computed on the spot). */
+void bkvo_rope_row(const uint16_t *x, int d, double theta, int p, uint16_t *y)
+{
+    float *cs = (float *)malloc(sizeof(float) * (size_t)d);
+    bkvo_rope_table(theta, d, p, p + 1, cs);
+    rope_row_with(x, d, cs, y);
+    free(cs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* FPS (Notes §2.2, App. Alg. 1).
+ *   a_i = (1/n) sum_j cos(q_i, q_j);  p = argmin_i a_i;  I = {p};
+ *   S_j = cos(q_j, q_p);  repeat: r = argmin_{j not in I} S_j,
+ *   I <- I + {r},  S_j <- max(S_j, cos(q_j, q_r)),  until |I| = m.
+ * fp32, fixed order:
+ *   dot_ij = fmaf over k = 0..d-1 ascending, starting from +0;
+ *   nrm_i  = sqrtf(dot_ii);
+ *   cos_ij = 0 if nrm_i or nrm_j is 0, else dot_ij / (nrm_i * nrm_j);
+ *   a_i    = (cos_i0 + cos_i1 + ... + cos_i(n-1), left to right) / n;
+ * the sum in a_i includes j = i (the page's sum runs over all N); every
+ * argmin takes the lowest index among equal values.  If n <= m no sampling
+ * happens and the selection is 0..n-1.
+ * Writes the selected indices in selection order; returns their count.     */
+int bkvo_fps(const uint16_t *X, int n, int d, int m, int *sel)
+{
+    if (n <= 0 || m <= 0) return 0;
+    if (n <= m) {
+        for (int i = 0; i < n; ++i) sel[i] = i;
+        return n;
+    }
+    float *x = (float *)malloc(sizeof(float) * (size_t)n * d);
+    float *cs = (float *)malloc(sizeof(float) * (size_t)n * n);
+    float *nrm = (float *)malloc(sizeof(float) * (size_t)n);
+    float *S = (float *)malloc(sizeof(float) * (size_t)n);
+    char *taken = (char *)calloc((size_t)n, 1);
+    for (int i = 0; i < n * d; ++i) x[i] = bf2f(X[i]);
+
+    for (int i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (int k = 0; k < d; ++k) acc = fmaf(x[i * d + k], x[i * d + k], acc);
+        nrm[i] = sqrtf(acc);
+    }
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < n; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < d; ++k) acc = fmaf(x[i * d + k], x[j * d + k], acc);
+            float c;
+            if (nrm[i] == 0.0f || nrm[j] == 0.0f) c = 0.0f;
+            else c = acc / (nrm[i] * nrm[j]);
+            cs[i * n + j] = c;
+        }
+    }
+    /* seed: lowest mean cosine */
+    int p = 0;
+    float best = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float s = 0.0f;
+        for (int j = 0; j < n; ++j) s = s + cs[i * n + j];
+        float a = s / (float)n;
+        if (i == 0 || a < best) { best = a; p = i; }
+    }
+    int cnt = 0;
+    sel[cnt++] = p;
+    taken[p] = 1;
+    for (int j = 0; j < n; ++j) S[j] = cs[j * n + p];
+    while (cnt < m) {
+        int r = -1;
+        float bv = 0.0f;
+        for (int j = 0; j < n; ++j) {
+            if (taken[j]) continue;
+            if (r < 0 || S[j] < bv) { r = j; bv = S[j]; }
+        }
+        sel[cnt++] = r;
+        taken[r] = 1;
+        for (int j = 0; j < n; ++j) {
+            float c = cs[j * n + r];
+            if (c > S[j]) S[j] = c;
+        }
+    }
+    free(x); free(cs); free(nrm); free(S); free(taken);
+    return cnt;
+}
+
+/* Diagnostic twin of bkvo_fps in fp64 (same steps, fp64 arithmetic).  For
+ * each pick it also reports the margin: the gap between the chosen value and
+ * the next-best candidate (a_i for the seed, S_j afterwards).  A pick whose
+ * margin is tiny is one where rounding may legitimately decide. */
+int bkvo_fps_f64(const uint16_t *X, int n, int d, int m, int *sel, double *margin)
+{
+    if (n <= 0 || m <= 0) return 0;
+    if (n <= m) {
+        for (int i = 0; i < n; ++i) { sel[i] = i; if (margin) margin[i] = INFINITY; }
+        return n;
+    }
+    double *x = (double *)malloc(sizeof(double) * (size_t)n * d);
+    double *cs = (double *)malloc(sizeof(double) * (size_t)n * n);
+    double *nrm = (double *)malloc(sizeof(double) * (size_t)n);
+    double *S = (double *)malloc(sizeof(double) * (size_t)n);
+    char *taken = (char *)calloc((size_t)n, 1);
+    for (int i = 0; i < n * d; ++i) x[i] = (double)bf2f(X[i]);
+    for (int i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += x[i * d + k] * x[i * d + k];
+        nrm[i] = sqrt(acc);
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += x[i * d + k] * x[j * d + k];
+            cs[i * n + j] = (nrm[i] == 0.0 || nrm[j] == 0.0) ? 0.0 : acc / (nrm[i] * nrm[j]);
+        }
+    double *a = (double *)malloc(sizeof(double) * (size_t)n);
+    for (int i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < n; ++j) s += cs[i * n + j];
+        a[i] = s / n;
+    }
+    int p = 0;
+    for (int i = 1; i < n; ++i) if (a[i] < a[p]) p = i;
+    double second = INFINITY;
+    for (int i = 0; i < n; ++i) if (i != p && a[i] < second) second = a[i];
+    int cnt = 0;
+    if (margin) margin[cnt] = second - a[p];
+    sel[cnt++] = p;
+    taken[p] = 1;
+    for (int j = 0; j < n; ++j) S[j] = cs[j * n + p];
+    while (cnt < m) {
+        int r = -1;
+        for (int j = 0; j < n; ++j) {
+            if (taken[j]) continue;
+            if (r < 0 || S[j] < S[r]) r = j;
+        }
+        double sec = INFINITY;
+        for (int j = 0; j < n; ++j) if (!taken[j] && j != r && S[j] < sec) sec = S[j];
+        if (margin) margin[cnt] = sec - S[r];
+        sel[cnt++] = r;
+        taken[r] = 1;
+        for (int j = 0; j < n; ++j) if (cs[j * n + r] > S[j]) S[j] = cs[j * n + r];
+    }
+    free(x); free(cs); free(nrm); free(S); free(taken); free(a);
+    return cnt;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Continual FPS buffer update (Notes §2.2, Eq. 9; Summary, pseudocode).
+ * For each query buffer b: append q_new[b] at slot qcount[b] and increment;
+ * if the count reaches B_Q^max = n_beacon + n_recent_q, replace the buffer
+ * by FPS(buffer, n_beacon), survivors kept in ascending slot order, and set
+ * the count to n_beacon.  sel_out[b][0..n_beacon) receives the selection
+ * order, or -1 when no sampling ran (sel_out may be NULL).
+ * qbuf: [nbuf][qcap][d] bf16; qcount: [nbuf]; q_new: [nbuf][d].            */
+void bkvo_fps_update(int nbuf, int qcap, int d, int n_beacon, int n_recent_q,
+                     uint16_t *qbuf, int32_t *qcount, const uint16_t *q_new,
+                     int32_t *sel_out)
+{
+    int bqmax = n_beacon + n_recent_q;
+    int *sel = (int *)malloc(sizeof(int) * (size_t)(bqmax + 1));
+    uint16_t *tmp = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)qcap * d);
+    for (int b = 0; b < nbuf; ++b) {
+        uint16_t *buf = qbuf + (size_t)b * qcap * d;
+        int c = qcount[b];
+        /* a valid buffer holds fewer than B_Q^max rows between calls */
+        if (c < 0) c = 0;
+        if (c > bqmax - 1) c = bqmax - 1;
+        memcpy(buf + (size_t)c * d, q_new + (size_t)b * d, sizeof(uint16_t) * (size_t)d);
+        c += 1;
+        if (sel_out)
+            for (int i = 0; i < n_beacon; ++i) sel_out[(size_t)b * n_beacon + i] = -1;
+        if (c >= bqmax) {
+            int got = bkvo_fps(buf, c, d, n_beacon, sel);
+            if (sel_out)
+                for (int i = 0; i < got; ++i) sel_out[(size_t)b * n_beacon + i] = sel[i];
+            /* survivors in ascending slot order */
+            char *keep = (char *)calloc((size_t)c, 1);
+            for (int i = 0; i < got; ++i) keep[sel[i]] = 1;
+            int w = 0;
+            for (int i = 0; i < c; ++i)
+                if (keep[i]) {
+                    memcpy(tmp + (size_t)w * d, buf + (size_t)i * d, sizeof(uint16_t) * (size_t)d);
+                    ++w;
+                }
+            memcpy(buf, tmp, sizeof(uint16_t) * (size_t)w * d);
+            free(keep);
+            c = w;
+        }
+        qcount[b] = c;
+    }
+    free(sel);
+    free(tmp);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention weights of one observation row (Notes §2.1, Eq. 4), fp64:
+ *   z_j = (q . k_j) / sqrt(d) for visible j <= vis (j < N);
+ *   w_j = exp(z_j - c),  c = m + ln sum_l exp(z_l - m),  m = max_l z_l;
+ *   w_j = 0 for j > vis.  Returns c (or -inf if nothing is visible).      */
+double bkvo_row_weights(const uint16_t *q, const uint16_t *K, int N, int d, int vis, double *w)
+{
+    int last = vis < N - 1 ? vis : N - 1;
+    double inv = 1.0 / sqrt((double)d);
+    double m = -INFINITY;
+    for (int j = 0; j <= last; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += (double)bf2f(q[k]) * (double)bf2f(K[(size_t)j * d + k]);
+        w[j] = acc * inv;
+        if (w[j] > m) m = w[j];
+    }
+    if (last < 0) {
+        for (int j = 0; j < N; ++j) w[j] = 0.0;
+        return -INFINITY;
+    }
+    double l = 0.0;
+    for (int j = 0; j <= last; ++j) l += exp(w[j] - m);
+    double c = m + log(l);
+    for (int j = 0; j <= last; ++j) w[j] = exp(w[j] - c);
+    for (int j = last + 1; j < N; ++j) w[j] = 0.0;
+    return c;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-unit arrays.  A unit is one (layer, batch, KV head); its q-heads are
+ * the G = hq / hkv heads h with h / G equal to the KV head.  All per-unit
+ * inputs are passed unit-major:
+ *   K, V       [U][cap][d]           bf16, K holds post-RoPE keys
+ *   qbuf       [U][G][qcap][d]       pre-RoPE buffers (modified by merge)
+ *   qcount     [U][G]                (modified by merge)
+ *   q_recent   [U][G][n_recent_q][d] pre-RoPE recent queries
+ *   pos_recent [U][n_recent_q]       positions of the recent queries
+ *   t          [U]                   current step (beacons are rotated to it)
+ * Outputs: scores [U][N] fp64, idx [U][budget] (-1 beyond min(N, budget)),
+ * moved [U] (#{r : idx[r] != r}), fps_sel [U][G][n_beacon].               */
+
+typedef struct {
+    const bkvo_cfg *cfg;
+    int N;
+    uint16_t *K, *V, *qbuf;
+    int32_t *qcount;
+    const uint16_t *q_recent;
+    const int32_t *pos_recent, *t;
+    double *scores;
+    int32_t *idx, *moved, *fps_sel;
+    int do_score, do_select, do_compact, do_merge;
+    int u0, u1;
+} unit_job;
+
+/* Beacons at an eviction are the current representatives: the first
+ * min(qcount, n_beacon) buffer rows, which hold the last FPS or merge output.
+ * Rows appended after it (slots >= n_beacon) form the buffer's recent set,
+ * which the cycle clears when the beacons are frozen (Notes §2.2, App. Alg. 2). */
+static int n_beacons_of(const bkvo_cfg *c, int qcount)
+{
+    int nb = qcount < c->n_beacon ? qcount : c->n_beacon;
+    return nb < 0 ? 0 : nb;
+}
+
+/* Score of one unit (Notes §2.3, Eq. 7): max over the group's heads and all
+ * their observation rows of the row's attention weight. */
+static void score_unit(const bkvo_cfg *c, int N, int u, const uint16_t *K,
+                       const uint16_t *qbuf, const int32_t *qcount,
+                       const uint16_t *q_recent, const int32_t *pos_recent,
+                       const int32_t *t, double *score)
+{
+    int d = c->d, G = c->hq / c->hkv;
+    double *w = (double *)malloc(sizeof(double) * (size_t)N);
+    uint16_t *qh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+    for (int j = 0; j < N; ++j) score[j] = 0.0;
+    const uint16_t *Ku = K + (size_t)u * c->cap * d;
+    for (int h = 0; h < G; ++h) {
+        const uint16_t *buf = qbuf + ((size_t)u * G + h) * c->qcap * d;
+        int nb = n_beacons_of(c, qcount[(size_t)u * G + h]);
+        for (int s = 0; s < nb; ++s) {
+            bkvo_rope_row(buf + (size_t)s * d, d, c->theta, t[u], qh);
+            bkvo_row_weights(qh, Ku, N, d, N - 1, w);
+            for (int j = 0; j < N; ++j) if (w[j] > score[j]) score[j] = w[j];
+        }
+        const uint16_t *rec = q_recent + ((size_t)u * G + h) * c->n_recent_q * d;
+        for (int i = 0; i < c->n_recent_q; ++i) {
+            int vis = c->causal ? N - c->n_recent_q + i : N - 1;
+            if (vis < 0) continue;
+            bkvo_rope_row(rec + (size_t)i * d, d, c->theta,
+                          pos_recent[(size_t)u * c->n_recent_q + i], qh);
+            bkvo_row_weights(qh, Ku, N, d, vis, w);
+            for (int j = 0; j < N; ++j) if (w[j] > score[j]) score[j] = w[j];
+        }
+    }
+    free(w);
+    free(qh);
+}
+
+typedef struct { double s; int j; } cand;
+
+static int cand_cmp(const void *a, const void *b)
+{
+    const cand *x = (const cand *)a, *y = (const cand *)b;
+    if (x->s > y->s) return -1;     /* higher score first */
+    if (x->s < y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);  /* then lower index */
+}
+
+/* Keep set (Notes §2.3, Eq. 8), 0-based:
+ *   I_keep = [0, n_prefix) U [N - n_recent_kv, N);
+ *   k_sel = budget - |I_keep|;  I_final = sort(I_keep U TopK(score, k_sel,
+ *   excluding I_keep)), ranking by score descending, then index ascending.
+ * If N <= budget everything is kept.  Writes idx[0..min(N,budget)) ascending
+ * and -1 after that.  Returns #{r : idx[r] != r}. */
+int bkvo_select(const double *score, int N, int budget, int n_prefix, int n_recent_kv, int32_t *idx)
+{
+    if (N <= budget) {
+        for (int r = 0; r < budget; ++r) idx[r] = r < N ? r : -1;
+        return 0;
+    }
+    char *keep = (char *)calloc((size_t)N, 1);
+    int np = n_prefix < N ? n_prefix : N;
+    int rs = N - n_recent_kv < 0 ? 0 : N - n_recent_kv;
+    int nk = 0;
+    for (int j = 0; j < N; ++j)
+        if (j < np || j >= rs) { keep[j] = 1; ++nk; }
+    int k_sel = budget - nk;
+    cand *cs = (cand *)malloc(sizeof(cand) * (size_t)N);
+    int nc = 0;
+    for (int j = 0; j < N; ++j)
+        if (!keep[j]) { cs[nc].s = score[j]; cs[nc].j = j; ++nc; }
+    qsort(cs, (size_t)nc, sizeof(cand), cand_cmp);
+    for (int i = 0; i < k_sel && i < nc; ++i) keep[cs[i].j] = 1;
+    int r = 0, moved = 0;
+    for (int j = 0; j < N && r < budget; ++j)
+        if (keep[j]) { idx[r] = j; if (j != r) ++moved; ++r; }
+    for (; r < budget; ++r) idx[r] = -1;
+    free(keep);
+    free(cs);
+    return moved;
+}
+
+/* In-place compaction (Notes §2.3, Eq. 8: K^ = K[:, I_final, :], same for V):
+ * row r of the result is row idx[r] of the input, r < count of valid idx. */
+static void compact_rows(uint16_t *X, int d, int N, const int32_t *idx, int budget)
+{
+    uint16_t *tmp = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)budget * d);
+    int n = 0;
+    for (int r = 0; r < budget; ++r) {
+        if (idx[r] < 0 || idx[r] >= N) break;
+        memcpy(tmp + (size_t)r * d, X + (size_t)idx[r] * d, sizeof(uint16_t) * (size_t)d);
+        ++n;
+    }
+    memcpy(X, tmp, sizeof(uint16_t) * (size_t)n * d);
+    free(tmp);
+}
+
+/* Merge at the end of a cycle (Notes §2.2, App. Alg. 2): the beacons and the
+ * recent queries, both pre-RoPE, are joined (beacons first, then recents in
+ * order) and FPS(., n_beacon) gives the next cycle's buffer, survivors in
+ * candidate order; the count becomes their number. */
+static void merge_unit(const bkvo_cfg *c, int u, uint16_t *qbuf, int32_t *qcount,
+                       const uint16_t *q_recent, int32_t *fps_sel)
+{
+    int d = c->d, G = c->hq / c->hkv;
+    int nmax = c->n_beacon + c->n_recent_q;
+    uint16_t *X = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(nmax + 1) * d);
+    int *sel = (int *)malloc(sizeof(int) * (size_t)(nmax + 1));
+    for (int h = 0; h < G; ++h) {
+        size_t b = (size_t)u * G + h;
+        uint16_t *buf = qbuf + b * c->qcap * d;
+        int nb = n_beacons_of(c, qcount[b]);
+        memcpy(X, buf, sizeof(uint16_t) * (size_t)nb * d);
+        memcpy(X + (size_t)nb * d, q_recent + b * c->n_recent_q * d,
+               sizeof(uint16_t) * (size_t)c->n_recent_q * d);
+        int n = nb + c->n_recent_q;
+        int got = bkvo_fps(X, n, d, c->n_beacon, sel);
+        if (fps_sel) {
+            for (int i = 0; i < c->n_beacon; ++i)
+                fps_sel[b * c->n_beacon + i] = i < got ? sel[i] : -1;
+        }
+        char *keep = (char *)calloc((size_t)(n > 0 ? n : 1), 1);
+        for (int i = 0; i < got; ++i) keep[sel[i]] = 1;
+        int w = 0;
+        for (int i = 0; i < n; ++i)
+            if (keep[i]) { memcpy(buf + (size_t)w * d, X + (size_t)i * d, sizeof(uint16_t) * (size_t)d); ++w; }
+        qcount[b] = w;
+        free(keep);
+    }
+    free(X);
+    free(sel);
+}
+
+static void *run_units(void *arg)
+{
+    unit_job *J = (unit_job *)arg;
+    const bkvo_cfg *c = J->cfg;
+    int N = J->N, d = c->d;
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    int32_t *ix = (int32_t *)malloc(sizeof(int32_t) * (size_t)c->budget);
+    for (int u = J->u0; u < J->u1; ++u) {
+        double *s = J->scores ? J->scores + (size_t)u * N : sc;
+        int32_t *ii = J->idx ? J->idx + (size_t)u * c->budget : ix;
+        if (J->do_score)
+            score_unit(c, N, u, J->K, J->qbuf, J->qcount, J->q_recent, J->pos_recent, J->t, s);
+        if (J->do_select) {
+            int mv = bkvo_select(s, N, c->budget, c->n_prefix, c->n_recent_kv, ii);
+            if (J->moved) J->moved[u] = mv;
+        }
+        if (J->do_compact) {
+            compact_rows(J->K + (size_t)u * c->cap * d, d, N, ii, c->budget);
+            compact_rows(J->V + (size_t)u * c->cap * d, d, N, ii, c->budget);
+        }
+        if (J->do_merge)
+            merge_unit(c, u, J->qbuf, J->qcount, J->q_recent, J->fps_sel);
+    }
+    free(sc);
+    free(ix);
+    return NULL;
+}
+
+static void run_parallel(unit_job base, int U, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > U) nthreads = U > 0 ? U : 1;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    unit_job *jobs = (unit_job *)malloc(sizeof(unit_job) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = base;
+        jobs[i].u0 = (int)((long)U * i / nthreads);
+        jobs[i].u1 = (int)((long)U * (i + 1) / nthreads);
+        pthread_create(&th[i], NULL, run_units, &jobs[i]);
+    }
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+}
+
+/* Scores only: scores[U][N] (fp64). */
+void bkvo_score(const bkvo_cfg *cfg, int U, int N, const uint16_t *K,
+                const uint16_t *qbuf, const int32_t *qcount, const uint16_t *q_recent,
+                const int32_t *pos_recent, const int32_t *t, double *scores, int nthreads)
+{
+    unit_job J;
+    memset(&J, 0, sizeof J);
+    J.cfg = cfg; J.N = N;
+    J.K = (uint16_t *)K; J.qbuf = (uint16_t *)qbuf; J.qcount = (int32_t *)qcount;
+    J.q_recent = q_recent; J.pos_recent = pos_recent; J.t = t;
+    J.scores = scores;
+    J.do_score = 1;
+    run_parallel(J, U, nthreads);
+}
+
+/* The whole eviction of Notes §2.2 App. Alg. 2 / §2.3 Eq. 7-8 for U units:
+ * score, keep set, in-place compaction of K and V, then the merge FPS of the
+ * buffers.  Any output pointer may be NULL. */
+void bkvo_evict(const bkvo_cfg *cfg, int U, int N, uint16_t *K, uint16_t *V,
+                uint16_t *qbuf, int32_t *qcount, const uint16_t *q_recent,
+                const int32_t *pos_recent, const int32_t *t,
+                int32_t *idx, double *scores, int32_t *moved, int32_t *fps_sel,
+                int nthreads)
+{
+    unit_job J;
+    memset(&J, 0, sizeof J);
+    J.cfg = cfg; J.N = N;
+    J.K = K; J.V = V; J.qbuf = qbuf; J.qcount = qcount;
+    J.q_recent = q_recent; J.pos_recent = pos_recent; J.t = t;
+    J.scores = scores; J.idx = idx; J.moved = moved; J.fps_sel = fps_sel;
+    J.do_score = J.do_select = J.do_compact = J.do_merge = 1;
+    run_parallel(J, U, nthreads);
+}
+
+/* Merge step alone (for checking the buffer update in isolation). */
+void bkvo_merge(const bkvo_cfg *cfg, int U, uint16_t *qbuf, int32_t *qcount,
+                const uint16_t *q_recent, int32_t *fps_sel)
+{
+    for (int u = 0; u < U; ++u) merge_unit(cfg, u, qbuf, qcount, q_recent, fps_sel);
+}
+
+/* Compaction alone, given keep indices (idx[U][budget], -1 terminated). */
+void bkvo_compact(const bkvo_cfg *cfg, int U, int N, uint16_t *K, uint16_t *V, const int32_t *idx)
+{
+    for (int u = 0; u < U; ++u) {
+        compact_rows(K + (size_t)u * cfg->cap * cfg->d, cfg->d, N, idx + (size_t)u * cfg->budget, cfg->budget);
+        compact_rows(V + (size_t)u * cfg->cap * cfg->d, cfg->d, N, idx + (size_t)u * cfg->budget, cfg->budget);
+    }
+}
+
+int bkvo_cfg_size(void) { return (int)sizeof(bkvo_cfg); }
