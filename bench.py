@@ -1,0 +1,188 @@
+"""Benchmark of the BeaconKV eviction step on one MI355X.
+
+One step = one bkv_evict call over every (layer, batch, KV head) unit of the
+Qwen3-4B-shaped cache: 36 layers x batch 16 x 8 KV heads = 4608 units, cache
+length 2176 -> budget 2048, head_dim 128, 32 query heads (G = 4), 16 beacons
++ 16 recent queries per query head.  Steps run back to back, in place, on one
+stream: each step evicts 128 rows from the cache the previous step left
+(its rows [budget, n_len) still hold the earlier tail rows), so every step
+does a full eviction's work.
+
+Prints one JSON line (see the keys below); `value` is eviction steps/s with
+all inputs resident in HBM.  `roofline` is for the dominant kernel (the K/V
+compaction), `step_hbm` for the whole step, both from algorithmic bytes and
+HIP-event durations measured here.  `cpu_baseline` times the CPU oracle on a
+bounded sample of the same units.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from long_reasoning_decode_amd import lib as L
+from long_reasoning_decode_amd import synth
+from long_reasoning_decode_amd.configs import EVICT_CONFIGS, QWEN3_4B
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+METRIC = "eviction steps/s (all layers x KV heads) at Qwen3-4B shape; % of HBM peak"
+
+
+def alg_bytes(cfg, qcount: np.ndarray, idx: np.ndarray, n_len: int) -> dict:
+    """Algorithmic bytes of one eviction: K read once for scoring, the
+    observation rows read, moved K and V rows read and written, the new
+    buffers written.  qcount [units, G] before the call; idx [units, budget]."""
+    d2 = cfg.d * 2
+    B = min(cfg.budget, n_len)
+    moved = (idx[:, :B] != np.arange(B)[None, :]).sum(axis=1).astype(np.int64)
+    rows = (np.minimum(qcount, cfg.n_beacon) + cfg.n_recent_q).sum(axis=1).astype(np.int64)
+    k_read = cfg.units * n_len * d2
+    q_read = int(rows.sum()) * d2
+    compact = int(4 * moved.sum()) * d2
+    buf = cfg.qbufs * cfg.n_beacon * d2
+    return {"k_read": k_read, "q_read": q_read, "compact": compact, "buffers": buf,
+            "total": k_read + q_read + compact + buf, "moved_rows": int(moved.sum())}
+
+
+def cpu_baseline(cfg, inp, target_s: float = 10.0) -> dict:
+    """The CPU oracle (as it stands) on a bounded sample of units."""
+    import oracle as O
+    threads = O.default_threads()
+    oc = O.OracleCfg(hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, cap=cfg.n_len, budget=cfg.budget, n_prefix=cfg.n_prefix,
+                     n_recent_kv=cfg.n_recent_kv, n_beacon=cfg.n_beacon, n_recent_q=cfg.n_recent_q,
+                     theta=cfg.theta, qcap=cfg.qcap)
+    n = max(threads, 8)
+    while True:
+        v = synth.oracle_views(cfg, inp, list(range(n)))
+        t0 = time.perf_counter()
+        O.evict(oc, v["K"], v["V"], v["qbuf"], v["qcount"], v["q_recent"], v["pos_recent"], v["t"],
+                nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= cfg.units:
+            break
+        n = min(cfg.units, max(n + threads, int(n * target_s / max(dt, 1e-3) * 1.05)))
+    units_per_s = n / dt
+    return {"value": units_per_s / cfg.units, "unit": "eviction steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {cfg.units} units of the same workload, one eviction each, {dt:.1f} s wall "
+                      f"on {threads} threads; scaled to whole steps"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=QWEN3_4B.name, choices=sorted(EVICT_CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: runs on one GPU only; every (layer, batch, KV head) unit is independent, so "
+              "a multi-GPU step would shard units by batch or KV head with no exchange; --gpus must be 1",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    cfg = EVICT_CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    L.load()
+    N = cfg.n_len
+    print(f"# generating {cfg.name}: {cfg.units} units, N={N}", file=sys.stderr, flush=True)
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    rope = torch.from_numpy(L.rope_table(cfg.theta, cfg.d, 0, cfg.rope_rows)).cuda()
+    shape = L.shape_of(cfg)
+    ws = torch.empty(L.workspace_bytes(shape, N), dtype=torch.uint8, device="cuda")
+    K, V, qbuf, qcount = inp["K"].clone(), inp["V"].clone(), inp["qbuf"].clone(), inp["qcount"].clone()
+    stream = torch.cuda.current_stream()
+    total_steps = args.warmup + args.steps
+    idx_steps = [torch.empty((cfg.units, cfg.budget), dtype=torch.int32, device="cuda") for _ in range(total_steps)]
+
+    def step(i):
+        L.evict(shape, K, V, N, qbuf, qcount, inp["q_recent"], inp["pos_recent"], inp["t"], rope,
+                idx_out=idx_steps[i], ws=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.warmup, total_steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # algorithmic bytes of the timed steps (qcount is n_beacon before every step)
+    qc0 = np.full((cfg.units, cfg.G), cfg.n_beacon, np.int64)
+    ab = [alg_bytes(cfg, qc0, idx_steps[i].cpu().numpy(), N) for i in range(args.warmup, total_steps)]
+    step_bytes = float(np.mean([a["total"] for a in ab]))
+    compact_bytes = float(np.mean([a["compact"] for a in ab]))
+
+    # per-kernel breakdown: the same four launches as bkv_evict, separated by events
+    print("# per-kernel breakdown", file=sys.stderr, flush=True)
+    scores = torch.empty((cfg.units, N), dtype=torch.float32, device="cuda")
+    idx_b = torch.empty((cfg.units, cfg.budget), dtype=torch.int32, device="cuda")
+    names = ["score", "select", "compact", "fps_merge"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    kb = []
+    for s in range(args.steps):
+        e = evs[s]
+        e[0].record(stream)
+        L.score(shape, K, N, qbuf, qcount, inp["q_recent"], inp["pos_recent"], inp["t"], rope, scores, stream)
+        e[1].record(stream)
+        L.select(shape, scores, N, idx_b, stream)
+        e[2].record(stream)
+        L.compact(shape, K, V, N, idx_b, stream)
+        e[3].record(stream)
+        L.fps_merge(shape, qbuf, qcount, inp["q_recent"], None, stream)
+        e[4].record(stream)
+        torch.cuda.synchronize()
+        kb.append(alg_bytes(cfg, qc0, idx_b.cpu().numpy(), N)["compact"])
+    kern_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+               for i, n in enumerate(names)}
+    compact_ach = float(np.mean(kb)) / (kern_ms["compact"] * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / ms_step,
+        "unit": "eviction steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} eviction step: {cfg.n_layers} layers x batch {cfg.batch} x "
+                               f"{cfg.hkv} KV heads ({cfg.units} units), {cfg.hq} query heads, head_dim {cfg.d}, "
+                               f"cache {N} -> budget {cfg.budget}, prefix {cfg.n_prefix}, recent window "
+                               f"{cfg.n_recent_kv}, {cfg.n_beacon} beacons + {cfg.n_recent_q} recent queries",
+                   "units": cfg.units, "n_len": N, "budget": cfg.budget},
+        "roofline": {"bound": "hbm", "kernel": "compact", "achieved": compact_ach, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": compact_ach / HBM_PEAK_GBS, "traffic": None},
+        "step_hbm": {"alg_bytes": step_bytes, "achieved_GBs": step_bytes / (ms_step * 1e-3) / 1e9,
+                     "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "compact_alg_bytes": compact_bytes},
+        "kernels_ms": kern_ms,
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,174 @@
+/*
+ * bkv.h -- C ABI of the BeaconKV eviction-step library (libbkv.so, gfx950).
+ *
+ * BeaconKV keeps, per attention head, a bounded buffer of pre-RoPE queries
+ * maintained by continual farthest point sampling (FPS).  At each eviction it
+ * scores every cached key with the buffered "beacon" queries rotated to the
+ * current step plus the recent queries at their own positions, max-pools the
+ * attention weights over queries and over the GQA group, keeps the prefix,
+ * the recent window and the top-k keys, and compacts K/V in place.
+ *
+ * Citations name the reading notes "BeaconKV：用历史查询代表保护长推理的远程回看"
+ * (liuzhao09.github.io, "Notes") and the rcap.io post "BeaconKV: Key-Value
+ * Cache Compression Guided by Beacon Queries" ("Summary").
+ *
+ * Layout.  A unit is one (layer, batch element, KV head):
+ *     u  = (l * batch + b) * n_kv_heads + g
+ * and a query buffer is one (layer, batch element, query head):
+ *     uq = (l * batch + b) * n_q_heads + h,   query head h reads KV head h / G,
+ * G = n_q_heads / n_kv_heads.  Dense row-major arrays:
+ *     K, V        bf16  [units][cap][head_dim]       K holds post-RoPE keys
+ *     qbuf        bf16  [qbufs][qcap][head_dim]      pre-RoPE query buffers
+ *     qcount      int32 [qbufs]                      valid rows per buffer
+ *     q_new       bf16  [qbufs][head_dim]            this step's pre-RoPE query
+ *     q_recent    bf16  [qbufs][n_recent_q][head_dim] pre-RoPE recent queries
+ *     pos_recent  int32 [batch][n_recent_q]          their positions
+ *     t           int32 [batch]                      current step per sequence
+ *     rope_cs     fp32  [rope_rows][head_dim/2][2]   {cos, sin} table
+ *     scores      fp32  [units][n_len]
+ *     idx         int32 [units][budget]
+ *     fps_sel     int32 [qbufs][n_beacon]
+ * i.e. per layer the usual [batch][heads][seq][head_dim] cache layout, with
+ * layers outermost.  Device pointers must be 16-byte aligned.
+ *
+ * Ownership.  The caller owns all memory; the library never allocates, frees
+ * or keeps a pointer after a call returns.  In/out arguments are modified in
+ * place as documented per call.
+ *
+ * Execution.  Every device call only enqueues kernels on `stream` (a
+ * hipStream_t; NULL is the null stream) and returns without synchronising.
+ * The library has no global mutable state and is re-entrant; calls that
+ * overlap on the same buffers race.
+ *
+ * Errors.  Calls return BKV_OK or a negative code; on error nothing has been
+ * enqueued.  Host-side validation covers shapes, null and misaligned
+ * pointers.  Device data (qcount, positions, idx) is clamped into the range
+ * the buffers allow, never trusted for addressing.  Faults of a launched
+ * kernel surface at the caller's next synchronisation.  No C++ exception
+ * crosses this interface.
+ */
+#ifndef BKV_H
+#define BKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BKV_ABI_VERSION 1
+
+typedef uint16_t bkv_bf16; /* raw bf16 bits */
+
+enum {
+    BKV_OK = 0,
+    BKV_EINVAL = -1,       /* null/misaligned pointer, inconsistent shape */
+    BKV_EUNSUPPORTED = -2, /* shape outside what the kernels implement */
+    BKV_ERANGE = -3,       /* sizes out of range (n_len > cap, budget too small, ...) */
+    BKV_EHIP = -4          /* a kernel launch failed */
+};
+
+/* flags */
+#define BKV_CAUSAL_RECENT 1u /* recent query i sees only slots <= n_len - n_recent_q + i */
+
+typedef struct bkv_shape {
+    int32_t n_layers, batch, n_q_heads, n_kv_heads, head_dim; /* head_dim in {64, 128}; G <= 8 */
+    int32_t cap;          /* rows allocated per unit in K and V */
+    int32_t budget;       /* B_KV^min: rows kept by an eviction */
+    int32_t n_prefix;     /* forced keep of the first rows */
+    int32_t n_recent_kv;  /* forced keep of the last rows */
+    int32_t n_beacon;     /* B_Q^min: beacons kept by FPS */
+    int32_t n_recent_q;   /* recent queries; B_Q^max = n_beacon + n_recent_q <= 32 */
+    int32_t qcap;         /* rows allocated per query buffer, >= B_Q^max */
+    uint32_t flags;       /* BKV_CAUSAL_RECENT */
+} bkv_shape;
+
+/* ABI version (BKV_ABI_VERSION). */
+int bkv_version(void);
+
+/* Static text for an error code. */
+const char *bkv_strerror(int code);
+
+/* Host only.  RoPE table for positions [p0, p1):
+ *   host_out[((p - p0) * head_dim/2 + i) * 2 + {0, 1}] = {cos, sin}(p * theta^(-2i/head_dim)),
+ * angles in fp64, rounded to fp32; pairs are (i, i + head_dim/2), the
+ * convention of the model families the Notes evaluate (§3.1).  The caller
+ * uploads it once and passes it to bkv_score / bkv_evict with rope_rows =
+ * p1 when p0 = 0.  Errors: BKV_EINVAL (null, odd or non-positive head_dim,
+ * p0 < 0 or p1 <= p0). */
+int bkv_rope_table(double theta, int32_t head_dim, int32_t p0, int32_t p1, float *host_out);
+
+/* Workspace bytes that bkv_evict needs for n_len when both idx_out and
+ * scores_out are NULL (an upper bound otherwise).  0 on invalid input. */
+size_t bkv_workspace_bytes(const bkv_shape *shape, int32_t n_len);
+
+/* Continual FPS buffer update, one decode step (Notes §2.2 Eq. 9 and App.
+ * Alg. 1; Summary, pseudocode).  For every buffer uq: append q_new[uq] at
+ * slot qcount[uq]; if the count reaches B_Q^max, replace the buffer by
+ * FPS(buffer, n_beacon) -- seed at the lowest mean cosine, then repeatedly
+ * the row whose largest cosine to the rows taken is smallest, ties to the
+ * lowest slot, cosines in a fixed fp32 order -- with the survivors in
+ * ascending slot order, and set qcount to n_beacon.
+ * In/out: qbuf (rows [0, qcount) valid afterwards), qcount.  fps_sel may be
+ * NULL; else it receives the selection order, or -1s where no sampling ran.
+ * qcount is clamped to [0, B_Q^max - 1] on entry. */
+int bkv_fps_update(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
+                   const bkv_bf16 *q_new, int32_t *fps_sel, void *stream);
+
+/* Scores of every cached key (Notes §2.1 Eq. 4-5, §2.3 Eq. 7).  Per unit,
+ * the observation rows of each of its G query heads are the beacons
+ * qbuf[uq][0 : min(qcount, n_beacon)) rotated to t[b] and the recent queries
+ * q_recent[uq][i] rotated to pos_recent[b][i] (rotation in fp32 with each
+ * product and sum rounded, result rounded to bf16).  With z = q.k / sqrt(d)
+ * over the keys a row sees (all n_len keys for beacons; for recent row i,
+ * under BKV_CAUSAL_RECENT, keys <= n_len - n_recent_q + i):
+ *   scores[u][j] = max over rows r of exp(z_rj - logsumexp_j' z_rj').
+ * bf16 MFMA products with fp32 accumulation.  Positions are clamped to
+ * [0, rope_rows).  Out: scores [units][n_len]. */
+int bkv_score(const bkv_shape *shape, const bkv_bf16 *K, int32_t n_len,
+              const bkv_bf16 *qbuf, const int32_t *qcount, const bkv_bf16 *q_recent,
+              const int32_t *pos_recent, const int32_t *t,
+              const float *rope_cs, int32_t rope_rows, float *scores, void *stream);
+
+/* Keep set (Notes §2.3 Eq. 8, 0-based): I_keep = [0, n_prefix) U
+ * [n_len - n_recent_kv, n_len); the budget - |I_keep| highest-scoring other
+ * keys (ties to the lower index) join it; idx[u] lists the kept slots in
+ * ascending order.  If n_len <= budget, idx[u] = 0..n_len-1 then -1s.
+ * Scores must be >= 0 (weights are).  Out: idx [units][budget]. */
+int bkv_select(const bkv_shape *shape, const float *scores, int32_t n_len,
+               int32_t *idx, void *stream);
+
+/* In-place compaction (Notes §2.3 Eq. 8: K^ = K[:, I_final, :], V^ likewise):
+ * row r of K and V becomes row idx[u][r], r < min(n_len, budget).  idx[u]
+ * must be strictly ascending (as bkv_select writes it); rows >= budget keep
+ * stale data.  In/out: K, V. */
+int bkv_compact(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t n_len,
+                const int32_t *idx, void *stream);
+
+/* End-of-cycle merge (Notes §2.2, App. Alg. 2): per buffer, the beacons
+ * qbuf[uq][0 : min(qcount, n_beacon)) followed by q_recent[uq] are reduced
+ * by FPS to n_beacon rows (all of them if there are no more), written in
+ * candidate order to qbuf[uq], and qcount becomes their number.  fps_sel
+ * (nullable) receives the selection order (-1 padded). */
+int bkv_fps_merge(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
+                  const bkv_bf16 *q_recent, int32_t *fps_sel, void *stream);
+
+/* One whole eviction (Notes §2.2 App. Alg. 2 and §2.3; Summary,
+ * pseudocode): bkv_score, bkv_select, bkv_compact, then bkv_fps_merge, over
+ * all units.  idx_out, scores_out and fps_sel_out are optional outputs
+ * (NULL: kept in the workspace or not written).  ws must hold
+ * bkv_workspace_bytes(shape, n_len) bytes (it may be NULL when both idx_out
+ * and scores_out are given).  In/out: K, V, qbuf, qcount. */
+int bkv_evict(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t n_len,
+              bkv_bf16 *qbuf, int32_t *qcount, const bkv_bf16 *q_recent,
+              const int32_t *pos_recent, const int32_t *t,
+              const float *rope_cs, int32_t rope_rows,
+              int32_t *idx_out, float *scores_out, int32_t *fps_sel_out,
+              void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BKV_H */

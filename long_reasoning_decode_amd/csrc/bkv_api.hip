@@ -1,0 +1,281 @@
+// bkv_api.hip -- the C ABI of include/bkv.h: validation and launches.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "bkv.h"
+#include "bkv_internal.hpp"
+
+namespace {
+
+constexpr int32_t kMaxLen = 8192;    // scores of one unit live in LDS
+constexpr int32_t kMaxBq = 32;       // B_Q^max: one FPS wave holds 32 candidates
+constexpr int32_t kMaxGroup = 8;     // query heads per KV head
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+int check_shape(const bkv_shape* s) {
+    if (!s) return BKV_EINVAL;
+    if (s->n_layers <= 0 || s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0) return BKV_EINVAL;
+    if (s->n_q_heads % s->n_kv_heads) return BKV_EINVAL;
+    if (s->n_q_heads / s->n_kv_heads > kMaxGroup) return BKV_EUNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128) return BKV_EUNSUPPORTED;
+    if (s->n_beacon < 0 || s->n_recent_q < 0 || s->n_beacon + s->n_recent_q < 1) return BKV_EINVAL;
+    if (s->n_beacon + s->n_recent_q > kMaxBq) return BKV_EUNSUPPORTED;
+    if (s->qcap < s->n_beacon + s->n_recent_q) return BKV_EINVAL;
+    if (s->cap <= 0 || s->budget < 0 || s->n_prefix < 0 || s->n_recent_kv < 0) return BKV_EINVAL;
+    if (s->flags & ~BKV_CAUSAL_RECENT) return BKV_EINVAL;
+    const int64_t units = (int64_t)s->n_layers * s->batch * s->n_kv_heads;
+    const int64_t qbufs = (int64_t)s->n_layers * s->batch * s->n_q_heads;
+    if (units > INT32_MAX || qbufs > INT32_MAX) return BKV_ERANGE;
+    return BKV_OK;
+}
+
+int check_len(const bkv_shape* s, int32_t n_len) {
+    if (n_len <= 0) return BKV_ERANGE;
+    if (n_len > s->cap) return BKV_ERANGE;
+    if (n_len > kMaxLen) return BKV_EUNSUPPORTED;
+    return BKV_OK;
+}
+
+int check_keep(const bkv_shape* s, int32_t n_len) {
+    if (n_len > s->budget && s->budget < s->n_prefix + s->n_recent_kv) return BKV_ERANGE;
+    return BKV_OK;
+}
+
+int units_of(const bkv_shape* s) { return s->n_layers * s->batch * s->n_kv_heads; }
+int qbufs_of(const bkv_shape* s) { return s->n_layers * s->batch * s->n_q_heads; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
+
+bkv::ScoreArgs score_args(const bkv_shape* s, const bkv_bf16* K, int32_t n_len, const bkv_bf16* qbuf,
+                          const int32_t* qcount, const bkv_bf16* q_recent, const int32_t* pos_recent,
+                          const int32_t* t, const float* rope_cs, int32_t rope_rows, float* scores) {
+    bkv::ScoreArgs a;
+    a.K = K;
+    a.qbuf = qbuf;
+    a.qcount = qcount;
+    a.q_recent = q_recent;
+    a.pos_recent = pos_recent;
+    a.t = t;
+    a.rope_cs = rope_cs;
+    a.scores = scores;
+    a.units = units_of(s);
+    a.n_len = n_len;
+    a.cap = s->cap;
+    a.batch = s->batch;
+    a.hkv = s->n_kv_heads;
+    a.G = s->n_q_heads / s->n_kv_heads;
+    a.qcap = s->qcap;
+    a.n_beacon = s->n_beacon;
+    a.n_recent_q = s->n_recent_q;
+    a.causal = (s->flags & BKV_CAUSAL_RECENT) ? 1 : 0;
+    a.rope_rows = rope_rows;
+    return a;
+}
+
+int check_score_ptrs(const bkv_bf16* K, const bkv_bf16* qbuf, const int32_t* qcount,
+                     const bkv_bf16* q_recent, const int32_t* pos_recent, const int32_t* t,
+                     const float* rope_cs, int32_t rope_rows, const bkv_shape* s) {
+    if (!K || !qbuf || !qcount || !t || !rope_cs) return BKV_EINVAL;
+    if (s->n_recent_q > 0 && (!q_recent || !pos_recent)) return BKV_EINVAL;
+    if (!aligned16(K) || !aligned16(qbuf) || !aligned16(rope_cs)) return BKV_EINVAL;
+    if (q_recent && !aligned16(q_recent)) return BKV_EINVAL;
+    if (!aligned4(qcount) || !aligned4(t) || (pos_recent && !aligned4(pos_recent))) return BKV_EINVAL;
+    if (rope_rows <= 0) return BKV_ERANGE;
+    return BKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bkv_version(void) { return BKV_ABI_VERSION; }
+
+const char* bkv_strerror(int code) {
+    switch (code) {
+        case BKV_OK: return "ok";
+        case BKV_EINVAL: return "invalid argument (null or misaligned pointer, inconsistent shape)";
+        case BKV_EUNSUPPORTED: return "unsupported shape (head_dim, group size, buffer or length limits)";
+        case BKV_ERANGE: return "size out of range (n_len vs cap, budget vs forced keeps, table rows)";
+        case BKV_EHIP: return "HIP kernel launch failed";
+        default: return "unknown error";
+    }
+}
+
+int bkv_rope_table(double theta, int32_t head_dim, int32_t p0, int32_t p1, float* host_out) {
+    if (!host_out || head_dim <= 0 || (head_dim & 1) || p0 < 0 || p1 <= p0) return BKV_EINVAL;
+    const int32_t h = head_dim / 2;
+    for (int32_t i = 0; i < h; ++i) {
+        const double f = pow(theta, -(double)(2 * i) / (double)head_dim);
+        for (int32_t p = p0; p < p1; ++p) {
+            const double ang = (double)p * f;
+            float* o = host_out + ((size_t)(p - p0) * h + i) * 2;
+            o[0] = (float)cos(ang);
+            o[1] = (float)sin(ang);
+        }
+    }
+    return BKV_OK;
+}
+
+size_t bkv_workspace_bytes(const bkv_shape* s, int32_t n_len) {
+    if (check_shape(s) != BKV_OK || n_len <= 0) return 0;
+    const size_t units = (size_t)units_of(s);
+    return round256(units * (size_t)n_len * 4) + round256(units * (size_t)(s->budget > 0 ? s->budget : 1) * 4);
+}
+
+int bkv_fps_update(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const bkv_bf16* q_new,
+                   int32_t* fps_sel, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (!qbuf || !qcount || !q_new) return BKV_EINVAL;
+    if (!aligned16(qbuf) || !aligned16(q_new) || !aligned4(qcount)) return BKV_EINVAL;
+    if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
+    bkv::FpsArgs a;
+    a.qbuf = qbuf;
+    a.qcount = qcount;
+    a.q_new = q_new;
+    a.q_recent = nullptr;
+    a.fps_sel = fps_sel;
+    a.nbuf = qbufs_of(s);
+    a.qcap = s->qcap;
+    a.n_beacon = s->n_beacon;
+    a.n_recent_q = s->n_recent_q;
+    return hip_status(bkv::launch_fps(a, s->head_dim, false, (hipStream_t)stream));
+}
+
+int bkv_fps_merge(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const bkv_bf16* q_recent,
+                  int32_t* fps_sel, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (!qbuf || !qcount || (s->n_recent_q > 0 && !q_recent)) return BKV_EINVAL;
+    if (!aligned16(qbuf) || (q_recent && !aligned16(q_recent)) || !aligned4(qcount)) return BKV_EINVAL;
+    if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
+    bkv::FpsArgs a;
+    a.qbuf = qbuf;
+    a.qcount = qcount;
+    a.q_new = nullptr;
+    a.q_recent = q_recent;
+    a.fps_sel = fps_sel;
+    a.nbuf = qbufs_of(s);
+    a.qcap = s->qcap;
+    a.n_beacon = s->n_beacon;
+    a.n_recent_q = s->n_recent_q;
+    return hip_status(bkv::launch_fps(a, s->head_dim, true, (hipStream_t)stream));
+}
+
+int bkv_score(const bkv_shape* s, const bkv_bf16* K, int32_t n_len, const bkv_bf16* qbuf,
+              const int32_t* qcount, const bkv_bf16* q_recent, const int32_t* pos_recent, const int32_t* t,
+              const float* rope_cs, int32_t rope_rows, float* scores, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if ((e = check_len(s, n_len))) return e;
+    if ((e = check_score_ptrs(K, qbuf, qcount, q_recent, pos_recent, t, rope_cs, rope_rows, s))) return e;
+    if (!scores || !aligned4(scores)) return BKV_EINVAL;
+    bkv::ScoreArgs a = score_args(s, K, n_len, qbuf, qcount, q_recent, pos_recent, t, rope_cs, rope_rows, scores);
+    return hip_status(bkv::launch_score(a, s->head_dim, (hipStream_t)stream));
+}
+
+int bkv_select(const bkv_shape* s, const float* scores, int32_t n_len, int32_t* idx, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if ((e = check_len(s, n_len))) return e;
+    if ((e = check_keep(s, n_len))) return e;
+    if (!scores || !idx || !aligned4(scores) || !aligned4(idx)) return BKV_EINVAL;
+    bkv::SelectArgs a;
+    a.scores = scores;
+    a.idx = idx;
+    a.units = units_of(s);
+    a.n_len = n_len;
+    a.budget = s->budget;
+    a.n_prefix = s->n_prefix;
+    a.n_recent_kv = s->n_recent_kv;
+    return hip_status(bkv::launch_select(a, (hipStream_t)stream));
+}
+
+int bkv_compact(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, const int32_t* idx, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if ((e = check_len(s, n_len))) return e;
+    if (!K || !V || !idx || !aligned16(K) || !aligned16(V) || !aligned4(idx)) return BKV_EINVAL;
+    bkv::CompactArgs a;
+    a.K = K;
+    a.V = V;
+    a.idx = idx;
+    a.units = units_of(s);
+    a.n_len = n_len;
+    a.cap = s->cap;
+    a.budget = s->budget;
+    return hip_status(bkv::launch_compact(a, s->head_dim, (hipStream_t)stream));
+}
+
+int bkv_evict(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, bkv_bf16* qbuf, int32_t* qcount,
+              const bkv_bf16* q_recent, const int32_t* pos_recent, const int32_t* t, const float* rope_cs,
+              int32_t rope_rows, int32_t* idx_out, float* scores_out, int32_t* fps_sel_out, void* ws,
+              size_t ws_bytes, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if ((e = check_len(s, n_len))) return e;
+    if ((e = check_keep(s, n_len))) return e;
+    if ((e = check_score_ptrs(K, qbuf, qcount, q_recent, pos_recent, t, rope_cs, rope_rows, s))) return e;
+    if (!V || !aligned16(V)) return BKV_EINVAL;
+    if ((idx_out && !aligned4(idx_out)) || (scores_out && !aligned4(scores_out)) ||
+        (fps_sel_out && !aligned4(fps_sel_out)))
+        return BKV_EINVAL;
+    const size_t units = (size_t)units_of(s);
+    const size_t sc_bytes = round256(units * (size_t)n_len * 4);
+    size_t need = 0;
+    if (!scores_out) need += sc_bytes;
+    if (!idx_out) need += round256(units * (size_t)(s->budget > 0 ? s->budget : 1) * 4);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return BKV_EINVAL;
+    unsigned char* w = (unsigned char*)ws;
+    float* scores = scores_out;
+    if (!scores) {
+        scores = (float*)w;
+        w += sc_bytes;
+    }
+    int32_t* idx = idx_out ? idx_out : (int32_t*)w;
+    hipStream_t st = (hipStream_t)stream;
+
+    bkv::ScoreArgs sa = score_args(s, K, n_len, qbuf, qcount, q_recent, pos_recent, t, rope_cs, rope_rows, scores);
+    if ((e = hip_status(bkv::launch_score(sa, s->head_dim, st)))) return e;
+
+    bkv::SelectArgs la;
+    la.scores = scores;
+    la.idx = idx;
+    la.units = (int)units;
+    la.n_len = n_len;
+    la.budget = s->budget;
+    la.n_prefix = s->n_prefix;
+    la.n_recent_kv = s->n_recent_kv;
+    if ((e = hip_status(bkv::launch_select(la, st)))) return e;
+
+    bkv::CompactArgs ca;
+    ca.K = K;
+    ca.V = V;
+    ca.idx = idx;
+    ca.units = (int)units;
+    ca.n_len = n_len;
+    ca.cap = s->cap;
+    ca.budget = s->budget;
+    if ((e = hip_status(bkv::launch_compact(ca, s->head_dim, st)))) return e;
+
+    bkv::FpsArgs fa;
+    fa.qbuf = qbuf;
+    fa.qcount = qcount;
+    fa.q_new = nullptr;
+    fa.q_recent = q_recent;
+    fa.fps_sel = fps_sel_out;
+    fa.nbuf = qbufs_of(s);
+    fa.qcap = s->qcap;
+    fa.n_beacon = s->n_beacon;
+    fa.n_recent_q = s->n_recent_q;
+    return hip_status(bkv::launch_fps(fa, s->head_dim, true, st));
+}
+
+}  // extern "C"

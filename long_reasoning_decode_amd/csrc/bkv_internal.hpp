@@ -1,0 +1,50 @@
+// bkv_internal.hpp -- kernel argument blocks and launchers (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bkv.h"
+
+namespace bkv {
+
+struct FpsArgs {
+    bkv_bf16* qbuf;            // [nbuf][qcap][d]
+    int32_t* qcount;           // [nbuf]
+    const bkv_bf16* q_new;     // [nbuf][d]          (update)
+    const bkv_bf16* q_recent;  // [nbuf][n_recent_q][d] (merge)
+    int32_t* fps_sel;          // [nbuf][n_beacon] or null
+    int nbuf, qcap, n_beacon, n_recent_q;
+};
+
+struct ScoreArgs {
+    const bkv_bf16* K;         // [units][cap][d]
+    const bkv_bf16* qbuf;      // [qbufs][qcap][d]
+    const int32_t* qcount;     // [qbufs]
+    const bkv_bf16* q_recent;  // [qbufs][n_recent_q][d]
+    const int32_t* pos_recent; // [batch][n_recent_q]
+    const int32_t* t;          // [batch]
+    const float* rope_cs;      // [rope_rows][d/2][2]
+    float* scores;             // [units][n_len]
+    int units, n_len, cap, batch, hkv, G, qcap, n_beacon, n_recent_q, causal, rope_rows;
+};
+
+struct SelectArgs {
+    const float* scores;       // [units][n_len]
+    int32_t* idx;              // [units][budget]
+    int units, n_len, budget, n_prefix, n_recent_kv;
+};
+
+struct CompactArgs {
+    bkv_bf16* K;               // [units][cap][d]
+    bkv_bf16* V;
+    const int32_t* idx;        // [units][budget]
+    int units, n_len, cap, budget;
+};
+
+hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st);
+hipError_t launch_score(const ScoreArgs& a, int d, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+hipError_t launch_compact(const CompactArgs& a, int d, hipStream_t st);
+
+}  // namespace bkv

@@ -1,0 +1,166 @@
+"""Thin Python binding of libbkv.so (include/bkv.h): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks dtype,
+device and contiguity, and passes raw pointers and the current HIP stream to
+the C entry point of the same name.  All computation happens in the library's
+HIP kernels; there is no fallback.  If the library has not been built, the
+first call raises ``ImportError``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+from .configs import EvictConfig
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbkv.so")
+
+BKV_CAUSAL_RECENT = 1
+ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE", -4: "BKV_EHIP"}
+
+EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_workspace_bytes", "bkv_fps_update",
+           "bkv_fps_merge", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict")
+
+
+class Shape(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim", "cap", "budget", "n_prefix",
+        "n_recent_kv", "n_beacon", "n_recent_q", "qcap")] + [("flags", C.c_uint32)]
+
+
+class BkvError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ERRORS.get(code, code)} ({strerror(code)})")
+
+
+_lib = None
+
+
+def load():
+    """Load libbkv.so (built in-tree by build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m long_reasoning_decode_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, i32, st = C.c_void_p, C.c_int32, C.c_void_p
+        SP = C.POINTER(Shape)
+        L.bkv_version.restype = C.c_int
+        L.bkv_strerror.argtypes = [C.c_int]
+        L.bkv_strerror.restype = C.c_char_p
+        L.bkv_rope_table.argtypes = [C.c_double, i32, i32, i32, P]
+        L.bkv_workspace_bytes.argtypes = [SP, i32]
+        L.bkv_workspace_bytes.restype = C.c_size_t
+        L.bkv_fps_update.argtypes = [SP, P, P, P, P, st]
+        L.bkv_fps_merge.argtypes = [SP, P, P, P, P, st]
+        L.bkv_score.argtypes = [SP, P, i32, P, P, P, P, P, P, i32, P, st]
+        L.bkv_select.argtypes = [SP, P, i32, P, st]
+        L.bkv_compact.argtypes = [SP, P, P, i32, P, st]
+        L.bkv_evict.argtypes = [SP, P, P, i32, P, P, P, P, P, P, i32, P, P, P, P, C.c_size_t, st]
+        for f in EXPORTS[4:]:
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load().bkv_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return load().bkv_version()
+
+
+def shape_of(cfg: EvictConfig, cap: Optional[int] = None, flags: int = BKV_CAUSAL_RECENT) -> Shape:
+    return Shape(cfg.n_layers, cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.cap if cap is None else cap,
+                 cfg.budget, cfg.n_prefix, cfg.n_recent_kv, cfg.n_beacon, cfg.n_recent_q, cfg.qcap, flags)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(code: int, where: str) -> None:
+    if code != 0:
+        raise BkvError(code, where)
+
+
+bf16, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+
+
+def rope_table(theta: float, head_dim: int, p0: int, p1: int) -> np.ndarray:
+    """Host-built {cos, sin} table [p1 - p0, head_dim/2, 2] (float32)."""
+    out = np.empty((p1 - p0, head_dim // 2, 2), dtype=np.float32)
+    _check(load().bkv_rope_table(float(theta), head_dim, p0, p1, out.ctypes.data_as(C.c_void_p)),
+           "bkv_rope_table")
+    return out
+
+
+def workspace_bytes(shape: Shape, n_len: int) -> int:
+    return int(load().bkv_workspace_bytes(C.byref(shape), int(n_len)))
+
+
+def fps_update(shape: Shape, qbuf, qcount, q_new, fps_sel=None, stream=None) -> None:
+    _check(load().bkv_fps_update(C.byref(shape), _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"),
+                                 _ptr(q_new, bf16, "q_new"), _ptr(fps_sel, i32, "fps_sel"), _stream(stream)),
+           "bkv_fps_update")
+
+
+def fps_merge(shape: Shape, qbuf, qcount, q_recent, fps_sel=None, stream=None) -> None:
+    _check(load().bkv_fps_merge(C.byref(shape), _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"),
+                                _ptr(q_recent, bf16, "q_recent"), _ptr(fps_sel, i32, "fps_sel"), _stream(stream)),
+           "bkv_fps_merge")
+
+
+def score(shape: Shape, K, n_len: int, qbuf, qcount, q_recent, pos_recent, t, rope_cs, scores,
+          stream=None) -> None:
+    _check(load().bkv_score(C.byref(shape), _ptr(K, bf16, "K"), int(n_len), _ptr(qbuf, bf16, "qbuf"),
+                            _ptr(qcount, i32, "qcount"), _ptr(q_recent, bf16, "q_recent"),
+                            _ptr(pos_recent, i32, "pos_recent"), _ptr(t, i32, "t"),
+                            _ptr(rope_cs, f32, "rope_cs"), int(rope_cs.shape[0]), _ptr(scores, f32, "scores"),
+                            _stream(stream)), "bkv_score")
+
+
+def select(shape: Shape, scores, n_len: int, idx, stream=None) -> None:
+    _check(load().bkv_select(C.byref(shape), _ptr(scores, f32, "scores"), int(n_len), _ptr(idx, i32, "idx"),
+                             _stream(stream)), "bkv_select")
+
+
+def compact(shape: Shape, K, V, n_len: int, idx, stream=None) -> None:
+    _check(load().bkv_compact(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(n_len),
+                              _ptr(idx, i32, "idx"), _stream(stream)), "bkv_compact")
+
+
+def evict(shape: Shape, K, V, n_len: int, qbuf, qcount, q_recent, pos_recent, t, rope_cs,
+          idx_out=None, scores_out=None, fps_sel_out=None, ws=None, stream=None) -> None:
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().bkv_evict(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(n_len),
+                            _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(q_recent, bf16, "q_recent"),
+                            _ptr(pos_recent, i32, "pos_recent"), _ptr(t, i32, "t"), _ptr(rope_cs, f32, "rope_cs"),
+                            int(rope_cs.shape[0]), _ptr(idx_out, i32, "idx_out"), _ptr(scores_out, f32, "scores_out"),
+                            _ptr(fps_sel_out, i32, "fps_sel_out"),
+                            None if ws is None else C.c_void_p(ws.data_ptr()), C.c_size_t(ws_bytes),
+                            _stream(stream)), "bkv_evict")

@@ -1,0 +1,133 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every entry point that include/bkv.h declares,
+and reject invalid arguments before touching a device.  Its host-built RoPE
+table must equal the oracle's bit for bit (both follow the same formula,
+written independently).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from long_reasoning_decode_amd import lib as L
+from long_reasoning_decode_amd.configs import EVICT_CONFIGS, QWEN3_4B, TINY
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def so():
+    if not os.path.exists(L.LIB_PATH):
+        from long_reasoning_decode_amd import build
+        build.build()
+    return L.load()
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "bkv.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(bkv_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(so):
+    names = header_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_version_and_strerror(so):
+    assert L.version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert len(L.strerror(code)) > 0
+    assert L.strerror(-99) == "unknown error"
+
+
+def test_shape_struct_layout():
+    # 12 int32 fields and one uint32, no padding
+    assert C.sizeof(L.Shape) == 13 * 4
+
+
+def test_rope_table_matches_oracle(so):
+    import oracle as O
+    for theta, d in ((1e4, 64), (1e6, 128), (1e4, 128)):
+        ours = L.rope_table(theta, d, 0, 2000)
+        ref = O.rope_table(theta, d, 0, 2000)
+        assert ours.dtype == np.float32 and np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+        assert np.array_equal(L.rope_table(theta, d, 30000, 30100).view(np.uint32),
+                              O.rope_table(theta, d, 30000, 30100).view(np.uint32))
+
+
+def test_rope_table_rejects_bad_args(so):
+    buf = np.zeros(64, np.float32)
+    p = buf.ctypes.data_as(C.c_void_p)
+    assert so.bkv_rope_table(1e4, 63, 0, 1, p) == -1
+    assert so.bkv_rope_table(1e4, 64, 5, 5, p) == -1
+    assert so.bkv_rope_table(1e4, 64, -1, 1, p) == -1
+    assert so.bkv_rope_table(1e4, 64, 0, 1, None) == -1
+
+
+def _shape(**kw):
+    s = L.shape_of(TINY)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+FAKE = C.c_void_p(0x10000)       # 16-byte aligned, never dereferenced: validation fails first
+MISALIGNED = C.c_void_p(0x10002)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, -2), ("n_q_heads", 5, -1), ("n_kv_heads", 0, -1), ("n_q_heads", 18, -2),
+    ("n_beacon", 20, -2), ("qcap", 16, -1), ("flags", 4, -1), ("cap", 0, -1), ("n_beacon", -1, -1),
+])
+def test_shape_validation(so, field, value, code):
+    s = _shape(**{field: value})
+    assert so.bkv_fps_update(C.byref(s), FAKE, FAKE, FAKE, None, None) == code
+    assert so.bkv_workspace_bytes(C.byref(s), 100) == 0
+
+
+def test_pointer_and_range_validation(so):
+    s = _shape()
+    # null / misaligned pointers
+    assert so.bkv_fps_update(C.byref(s), None, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_update(C.byref(s), MISALIGNED, FAKE, FAKE, None, None) == -1
+    assert so.bkv_compact(C.byref(s), FAKE, None, 100, FAKE, None) == -1
+    # n_len beyond cap, non-positive, beyond the supported maximum
+    assert so.bkv_compact(C.byref(s), FAKE, FAKE, s.cap + 1, FAKE, None) == -3
+    assert so.bkv_select(C.byref(s), FAKE, 0, FAKE, None) == -3
+    big = _shape(cap=9000)
+    assert so.bkv_select(C.byref(big), FAKE, 9000, FAKE, None) == -2
+    # budget below the forced keeps when an eviction is due
+    tight = _shape(budget=10, n_prefix=8, n_recent_kv=16)
+    assert so.bkv_select(C.byref(tight), FAKE, 100, FAKE, None) == -3
+    # score: table rows must be positive; recent queries need their arrays
+    assert so.bkv_score(C.byref(s), FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == -3
+    assert so.bkv_score(C.byref(s), FAKE, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, FAKE, None) == -1
+    # evict without workspace or outputs
+    assert so.bkv_evict(C.byref(s), FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
+                        None, None, None, None, 0, None) == -1
+    need = so.bkv_workspace_bytes(C.byref(s), 100)
+    assert so.bkv_evict(C.byref(s), FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
+                        None, None, None, FAKE, need - 1, None) == -1
+
+
+def test_workspace_bytes_monotone(so):
+    s = L.shape_of(QWEN3_4B)
+    a = so.bkv_workspace_bytes(C.byref(s), 1000)
+    b = so.bkv_workspace_bytes(C.byref(s), 2176)
+    assert 0 < a < b
+    assert b >= QWEN3_4B.units * (2176 + QWEN3_4B.budget) * 4
+
+
+def test_all_configs_are_supported_shapes():
+    for cfg in EVICT_CONFIGS.values():
+        assert cfg.d in (64, 128) and cfg.hq % cfg.hkv == 0 and cfg.G <= 8
+        assert cfg.n_beacon + cfg.n_recent_q <= 32 <= cfg.qcap
+        assert cfg.n_len <= 8192 and cfg.budget >= cfg.n_prefix + cfg.n_recent_kv

@@ -1,0 +1,297 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: FPS selections and merged buffers bit-exact; kept-index sets exact
+except for keys tied with the k-th score (|s - s_k| <= 1e-6 and <= 2e-4 s_k);
+scores within 1e-4 relative (+1e-30); compacted K/V rows byte-identical to the
+gather of the original rows by the kept indices.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from long_reasoning_decode_amd import lib as L
+from long_reasoning_decode_amd import synth
+from long_reasoning_decode_amd.configs import (QWEN3_4B, QWEN3_14B_1K, QWEN3_14B_4K, R1_QWEN_7B, TINY,
+                                               EvictConfig)
+
+import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+    yield
+
+
+def _flush(msg: str) -> None:
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Continual FPS update and merge.
+
+def _adversarial_buffers(nbuf: int, d: int, qcap: int, rng: np.random.Generator) -> np.ndarray:
+    X = rng.standard_normal((nbuf, qcap, d)).astype(np.float32)
+    for b in range(nbuf):
+        kind = b % 6
+        if kind == 1:    # duplicated rows
+            X[b, 5] = X[b, 9]
+            X[b, 20] = X[b, 9]
+        elif kind == 2:  # +- basis vectors: exact cosine ties
+            X[b, :8] = 0
+            for i in range(8):
+                X[b, i, i // 2] = 1.0 if i % 2 == 0 else -1.0
+        elif kind == 3:  # power-of-two scaled rows
+            X[b] *= 2.0 ** rng.integers(-8, 9, size=(qcap, 1))
+        elif kind == 4:  # a zero row (cosine defined as 0)
+            X[b, 3] = 0
+        elif kind == 5:  # tight clusters: many near-ties
+            c = rng.standard_normal((3, d))
+            X[b] = c[rng.integers(0, 3, qcap)] * 10 + 0.01 * rng.standard_normal((qcap, d))
+    return X
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("fill", [31, 30, 0, 17])
+def test_fps_update_matches_oracle(d, fill):
+    rng = np.random.default_rng(100 + d + fill)
+    cfg = TINY.scaled(d=d, n_layers=3, batch=5, hq=8, hkv=2)
+    nbuf, qcap = cfg.qbufs, cfg.qcap
+    X = _adversarial_buffers(nbuf, d, qcap, rng)
+    qb = torch.from_numpy(X).to(torch.bfloat16)
+    qn = torch.from_numpy(rng.standard_normal((nbuf, d)).astype(np.float32)).to(torch.bfloat16)
+    qc = np.full(nbuf, fill, np.int32)
+    qc[::7] = rng.integers(0, 31, size=len(qc[::7]))
+    qbuf_h = synth.to_u16(qb).copy()
+    qc_h = qc.copy()
+    sel_o = O.fps_update(qbuf_h, qc_h, synth.to_u16(qn), cfg.n_beacon, cfg.n_recent_q)
+    qbuf_d = qb.cuda()
+    qc_d = torch.from_numpy(qc).cuda()
+    sel_d = torch.full((nbuf, cfg.n_beacon), -7, dtype=torch.int32, device="cuda")
+    L.fps_update(L.shape_of(cfg), qbuf_d, qc_d, qn.cuda(), sel_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc_d.cpu().numpy(), qc_h)
+    assert np.array_equal(sel_d.cpu().numpy(), sel_o)
+    g = synth.to_u16(qbuf_d)
+    for b in range(nbuf):
+        n = qc_h[b]
+        assert np.array_equal(g[b, :n], qbuf_h[b, :n]), b
+
+
+@pytest.mark.parametrize("cfg", [TINY, QWEN3_4B.scaled(n_layers=2, batch=3), R1_QWEN_7B.scaled(n_layers=1, batch=2)],
+                         ids=lambda c: c.name)
+def test_fps_update_many_random_buffers(cfg):
+    """Full buffers of the workload's query mixture: one sampling round each."""
+    cfgx = cfg.scaled(batch=max(cfg.batch, 64)) if cfg.name == "tiny" else cfg
+    q = synth.make_query_buffers(cfgx, device="cuda")
+    nbuf = cfgx.qbufs
+    qbuf_h = synth.to_u16(q["qbuf"]).reshape(nbuf, cfgx.qcap, cfgx.d).copy()
+    qc_h = q["qcount"].cpu().numpy().reshape(nbuf).copy()
+    sel_o = O.fps_update(qbuf_h, qc_h, synth.to_u16(q["q_new"]).reshape(nbuf, cfgx.d),
+                         cfgx.n_beacon, cfgx.n_recent_q)
+    sel_d = torch.full((nbuf, cfgx.n_beacon), -7, dtype=torch.int32, device="cuda")
+    L.fps_update(L.shape_of(cfgx), q["qbuf"], q["qcount"], q["q_new"], sel_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel_d.cpu().numpy(), sel_o)
+    assert np.array_equal(q["qcount"].cpu().numpy().reshape(-1), qc_h)
+    g = synth.to_u16(q["qbuf"]).reshape(nbuf, cfgx.qcap, cfgx.d)
+    assert np.array_equal(g[:, :cfgx.n_beacon], qbuf_h[:, :cfgx.n_beacon])
+
+
+@pytest.mark.parametrize("qcount", [16, 9, 0, 20])
+def test_fps_merge_matches_oracle(qcount):
+    cfg = QWEN3_4B.scaled(n_layers=2, batch=3)
+    inp = synth.make_evict_inputs(cfg, device="cuda", qcount=qcount)
+    qc = inp["qcount"].clone()
+    qc.view(-1)[::5] = 3
+    v = synth.oracle_views(cfg, {**inp, "qcount": qc})
+    sel_o = O.merge(H.ocfg(cfg), v["qbuf"], v["qcount"], v["q_recent"])
+    qbuf = inp["qbuf"].clone()
+    sel_d = torch.full((cfg.qbufs, cfg.n_beacon), -7, dtype=torch.int32, device="cuda")
+    L.fps_merge(L.shape_of(cfg), qbuf, qc, inp["q_recent"], sel_d)
+    torch.cuda.synchronize()
+    G = cfg.G
+    assert np.array_equal(sel_d.cpu().numpy().reshape(cfg.units, G, -1), sel_o)
+    assert np.array_equal(qc.cpu().numpy().reshape(cfg.units, G), v["qcount"])
+    g = synth.to_u16(qbuf).reshape(cfg.units, G, cfg.qcap, cfg.d)
+    for u in range(cfg.units):
+        for h in range(G):
+            n = v["qcount"][u, h]
+            assert np.array_equal(g[u, h, :n], v["qbuf"][u, h, :n])
+
+
+# ---------------------------------------------------------------------------
+# Scores.
+
+SCORE_CASES = [
+    (TINY, None, 1),
+    (TINY, 97, 1),
+    (TINY, 160, 0),
+    (QWEN3_4B.scaled(n_layers=2, batch=2), None, 1),
+    (QWEN3_4B.scaled(n_layers=1, batch=2), 1000, 1),
+    (R1_QWEN_7B.scaled(n_layers=1, batch=2), None, 1),
+    (QWEN3_14B_1K.scaled(n_layers=1, batch=2), None, 1),
+    (QWEN3_14B_4K.scaled(n_layers=1, batch=1), None, 1),
+    (TINY.scaled(hq=8, hkv=1, name="g8"), 150, 1),
+    (TINY.scaled(hq=3, hkv=3, name="g1"), 33, 1),
+    (TINY.scaled(hq=6, hkv=2, name="g3"), 159, 1),
+    (TINY.scaled(hq=6, hkv=1, name="g6"), 140, 1),
+    (TINY.scaled(d=128, hq=5, hkv=1, name="g5d128"), 160, 1),
+]
+
+
+@pytest.mark.parametrize("cfg,n_len,causal", SCORE_CASES,
+                         ids=[f"{c.name}-{n}-{z}" for c, n, z in SCORE_CASES])
+def test_score_matches_oracle(cfg, n_len, causal):
+    N = cfg.n_len if n_len is None else n_len
+    _flush(f"score {cfg.name} N={N} causal={causal}")
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    qc = inp["qcount"]
+    qc.view(-1)[::3] = 5     # some buffers hold fewer beacons
+    qc.view(-1)[1::7] = 0
+    shape = L.shape_of(cfg, cap=cfg.n_len, flags=causal)
+    scores = torch.empty((cfg.units, N), dtype=torch.float32, device="cuda")
+    L.score(shape, inp["K"], N, inp["qbuf"], qc, inp["q_recent"], inp["pos_recent"], inp["t"],
+            H.rope_dev(cfg), scores)
+    torch.cuda.synchronize()
+    v = synth.oracle_views(cfg, inp)
+    o = O.score(H.ocfg(cfg, n_len=cfg.n_len, causal=causal), v["K"], v["qbuf"], v["qcount"], v["q_recent"],
+                v["pos_recent"], v["t"], n_len=N)
+    H.check_scores(scores.cpu().numpy(), o, f"{cfg.name} N={N}")
+
+
+# ---------------------------------------------------------------------------
+# Keep set.
+
+@pytest.mark.parametrize("n_len,budget,npf,nr", [(2176, 2048, 4, 16), (160, 128, 8, 16), (1000, 1000, 4, 16),
+                                                  (4224, 4096, 4, 16), (33, 20, 0, 0), (8192, 100, 50, 50),
+                                                  (300, 20, 4, 16)])
+def test_select_matches_oracle(n_len, budget, npf, nr):
+    rng = np.random.default_rng(n_len + budget)
+    U = 24
+    s = (rng.random((U, n_len)) ** 4).astype(np.float32)
+    s[1] = np.round(s[1] * 20) / 20          # many exact ties
+    s[2] = 0.5                               # all equal
+    s[3, :] = 0.0                            # zeros
+    s[4] = rng.integers(0, 3, n_len) * np.float32(1e-30)
+    cfg = QWEN3_4B.scaled(n_layers=1, batch=U, hkv=1, hq=1, budget=budget, n_new=n_len - budget,
+                          n_prefix=npf, n_recent_kv=nr)
+    shape = L.shape_of(cfg, cap=n_len)
+    idx = torch.full((U, budget), -7, dtype=torch.int32, device="cuda")
+    L.select(shape, torch.from_numpy(s).cuda(), n_len, idx)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    for u in range(U):
+        ref, _ = O.select(s[u].astype(np.float64), budget, npf, nr)
+        assert np.array_equal(g[u], ref), u
+
+
+# ---------------------------------------------------------------------------
+# Compaction.
+
+def _index_lists(U, n_len, budget, rng):
+    lists = []
+    for u in range(U):
+        kind = u % 6
+        if kind == 0:
+            sel = np.arange(budget)                                       # identity
+        elif kind == 1:
+            sel = np.arange(1, budget + 1)                                # single hole at 0
+        elif kind == 2:
+            sel = np.arange(n_len - budget, n_len)                        # keep only the tail
+        elif kind == 3:
+            sel = np.sort(rng.choice(n_len, budget, replace=False))
+        elif kind == 4:
+            sel = np.concatenate([np.arange(budget - 1), [n_len - 1]])    # last row only moves
+        else:
+            sel = np.sort(np.concatenate([np.arange(0, n_len, 2)[: budget // 2],
+                                          np.arange(1, n_len, 2)[-(budget - budget // 2):]]))
+        lists.append(sel[:budget])
+    return np.stack(lists).astype(np.int32)
+
+
+@pytest.mark.parametrize("d,n_len,budget", [(128, 2176, 2048), (64, 160, 128), (128, 300, 37), (128, 4224, 4096)])
+def test_compact_matches_oracle(d, n_len, budget):
+    rng = np.random.default_rng(d + n_len)
+    U = 30
+    cfg = TINY.scaled(d=d, n_layers=1, batch=U, hq=1, hkv=1, budget=budget, n_new=n_len - budget)
+    idx = _index_lists(U, n_len, budget, rng)
+    K = torch.from_numpy(rng.standard_normal((U, n_len, d)).astype(np.float32)).to(torch.bfloat16)
+    V = torch.from_numpy(rng.standard_normal((U, n_len, d)).astype(np.float32)).to(torch.bfloat16)
+    Kh, Vh = synth.to_u16(K).copy(), synth.to_u16(V).copy()
+    O.compact(H.ocfg(cfg), Kh, Vh, idx, n_len=n_len)
+    Kd, Vd = K.cuda(), V.cuda()
+    L.compact(L.shape_of(cfg, cap=n_len), Kd, Vd, n_len, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.to_u16(Kd), Kh)
+    assert np.array_equal(synth.to_u16(Vd), Vh)
+
+
+# ---------------------------------------------------------------------------
+# The whole eviction.
+
+EVICT_CASES = [
+    (TINY, None, 1),
+    (TINY, 159, 1),
+    (TINY, 128, 1),                 # nothing to evict
+    (TINY, 150, 0),
+    (QWEN3_4B.scaled(n_layers=2, batch=2), None, 1),
+    (R1_QWEN_7B.scaled(n_layers=1, batch=2), None, 1),
+    (QWEN3_14B_1K.scaled(n_layers=1, batch=2), None, 1),
+    (QWEN3_14B_4K.scaled(n_layers=1, batch=1), None, 1),
+    (TINY.scaled(hq=8, hkv=1, name="g8"), 150, 1),
+]
+
+
+@pytest.mark.parametrize("cfg,n_len,causal", EVICT_CASES, ids=[f"{c.name}-{n}-{z}" for c, n, z in EVICT_CASES])
+def test_evict_matches_oracle(cfg, n_len, causal):
+    N = cfg.n_len if n_len is None else n_len
+    _flush(f"evict {cfg.name} N={N} causal={causal}")
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    inp["qcount"].view(-1)[::5] = 7
+    out = H.run_evict_gpu(cfg, inp, N, flags=causal)
+    r = H.compare_evict(cfg, inp, out, N, causal=causal, where=f"{cfg.name} N={N}")
+    _flush(f"  tie-band differences: {r['n_tie_diff']}")
+
+
+FULL = [QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, QWEN3_14B_4K]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
+def test_evict_full_size_sampled_units(cfg):
+    """Full workload size, same launch as the benchmark; the oracle checks a
+    sample of units (first, last and spread across layers/batch/heads)."""
+    _flush(f"full-size evict {cfg.name}: {cfg.units} units, N={cfg.n_len}")
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    out = H.run_evict_gpu(cfg, inp, cfg.n_len)
+    rng = np.random.default_rng(7)
+    units = sorted(set([0, cfg.units - 1] + rng.choice(cfg.units, 22, replace=False).tolist()))
+    r = H.compare_evict(cfg, inp, out, cfg.n_len, units=units, where=cfg.name)
+    # every unit's kept list is a valid keep set
+    idx = out["idx"].cpu().numpy()
+    assert (np.diff(idx, axis=1) > 0).all()
+    assert (idx[:, : cfg.n_prefix] == np.arange(cfg.n_prefix)).all()
+    assert (idx[:, -cfg.n_recent_kv:] == np.arange(cfg.n_len - cfg.n_recent_kv, cfg.n_len)).all()
+    _flush(f"  tie-band differences in sample: {r['n_tie_diff']}")
+    del inp, out
+    torch.cuda.empty_cache()
+
+
+def test_evict_rejects_bad_shapes_without_launching():
+    cfg = TINY
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    shape = L.shape_of(cfg)
+    with pytest.raises(L.BkvError) as e:
+        L.evict(shape, inp["K"], inp["V"], cfg.n_len + 1, inp["qbuf"], inp["qcount"], inp["q_recent"],
+                inp["pos_recent"], inp["t"], H.rope_dev(cfg), idx_out=torch.empty((2, 128), dtype=torch.int32,
+                                                                                   device="cuda"),
+                scores_out=torch.empty((2, 161), device="cuda"))
+    assert e.value.code == -3
