@@ -80,6 +80,9 @@ def main() -> int:
     ap.add_argument("--config", default=QWEN3_4B.name, choices=sorted(EVICT_CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device-to-device once (a plain copy kernel of "
+                         "known size, for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: runs on one GPU only; every (layer, batch, KV head) unit is independent, so "
@@ -137,7 +140,8 @@ def main() -> int:
     for s in range(args.steps):
         e = evs[s]
         e[0].record(stream)
-        L.score(shape, K, N, qbuf, qcount, inp["q_recent"], inp["pos_recent"], inp["t"], rope, scores, stream)
+        L.score(shape, K, N, qbuf, qcount, inp["q_recent"], inp["pos_recent"], inp["t"], rope, scores,
+                stream=stream)
         e[1].record(stream)
         L.select(shape, scores, N, idx_b, stream)
         e[2].record(stream)
@@ -177,6 +181,14 @@ def main() -> int:
         "kernels_ms": kern_ms,
         "wall_s": wall,
     }
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel()
+        del src, dst
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

@@ -156,6 +156,8 @@ def compact(shape: Shape, K, V, n_len: int, idx, stream=None) -> None:
 
 def evict(shape: Shape, K, V, n_len: int, qbuf, qcount, q_recent, pos_recent, t, rope_cs,
           idx_out=None, scores_out=None, fps_sel_out=None, ws=None, stream=None) -> None:
+    if ws is None and (idx_out is None or scores_out is None):
+        ws = torch.empty(workspace_bytes(shape, n_len), dtype=torch.uint8, device=K.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().bkv_evict(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(n_len),
                             _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(q_recent, bf16, "q_recent"),
