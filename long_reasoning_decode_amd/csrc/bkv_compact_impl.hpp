@@ -1,0 +1,95 @@
+// bkv_compact_impl.hpp -- in-place gather of one tensor's kept rows by one
+// wavefront (Notes §2.3, Eq. 8: K^ = K[:, I_final, :], V^ likewise).
+//
+// The kept slots of the unit are staged in LDS (uint16: n_len <= 8192) and
+// strictly ascending, so src[r] >= r: every row's source sits at or after its
+// destination.  The wave skips the leading run with src[r] == r, then walks
+// destination chunks of kChunkRows rows in ascending order, software-
+// pipelined: the loads of chunk c+1 are issued before the stores of chunk c.
+// This is safe because
+//   * chunk c+1 reads rows >= its first destination, which lies beyond every
+//     row that chunk c (or any earlier chunk) stores;
+//   * a store of chunk c needs its own loads' data, and a wave's vector
+//     memory operations complete in issue order, so every load issued before
+//     it -- all loads of chunks <= c, including any that read the row it
+//     overwrites -- has returned by then.
+// K and V are independent, so one wave may move K while another moves V.
+// Loads and stores are non-temporal: the moved rows are not reused soon.
+#pragma once
+
+#include "bkv_device.hpp"
+
+namespace bkv {
+namespace compact {
+
+constexpr int kChunkRows = 32;
+
+template <int D>
+struct Chunk {
+    static constexpr int kPieces = D / 8;                     // 16-byte pieces per row
+    static constexpr int kPer = kChunkRows * kPieces / 64;    // pieces per lane
+    u32x4_t v[kPer];
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk(Chunk<D>& c, const bkv_bf16* X, const uint16_t* src, int r0, int B,
+                                           int lane) {
+#pragma unroll
+    for (int j = 0; j < Chunk<D>::kPer; ++j) {
+        const int p = lane + 64 * j;
+        const int row = r0 + p / Chunk<D>::kPieces;
+        const int col = p % Chunk<D>::kPieces;
+        if (row < B)
+            c.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(X + (size_t)src[row] * D + col * 8));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_chunk(const Chunk<D>& c, bkv_bf16* X, int r0, int B, int lane) {
+#pragma unroll
+    for (int j = 0; j < Chunk<D>::kPer; ++j) {
+        const int p = lane + 64 * j;
+        const int row = r0 + p / Chunk<D>::kPieces;
+        const int col = p % Chunk<D>::kPieces;
+        if (row < B) __builtin_nontemporal_store(c.v[j], reinterpret_cast<u32x4_t*>(X + (size_t)row * D + col * 8));
+    }
+}
+
+// The wave's LDS writes are complete and visible to its other lanes; the
+// compiler does not move LDS accesses across this point.
+__device__ __forceinline__ void wave_barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// First destination row whose source differs from itself (B if none).
+__device__ __forceinline__ int first_moved(const uint16_t* src, int B, int lane) {
+    for (int base = 0; base < B; base += 64) {
+        const int r = base + lane;
+        const uint64_t m = __ballot(r < B && src[r] != r);
+        if (m) return base + __ffsll((unsigned long long)m) - 1;
+    }
+    return B;
+}
+
+// Move rows [first, B) of X: X[r] <- X[src[r]].  One wavefront.
+template <int D>
+__device__ void move_rows(bkv_bf16* X, const uint16_t* src, int first, int B, int lane) {
+    if (first >= B) return;
+    Chunk<D> c0, c1;
+    int r0 = first;
+    load_chunk<D>(c0, X, src, r0, B, lane);
+    while (true) {
+        const int r1 = r0 + kChunkRows;
+        if (r1 < B) load_chunk<D>(c1, X, src, r1, B, lane);
+        store_chunk<D>(c0, X, r0, B, lane);
+        if (r1 >= B) break;
+        const int r2 = r1 + kChunkRows;
+        if (r2 < B) load_chunk<D>(c0, X, src, r2, B, lane);
+        store_chunk<D>(c1, X, r1, B, lane);
+        if (r2 >= B) break;
+        r0 = r2;
+    }
+}
+
+}  // namespace compact
+}  // namespace bkv

@@ -9,7 +9,7 @@
 // positions (Notes §2.3, realignment); other row slots are inactive.
 //
 // One workgroup owns one unit (layer, batch element, KV head).  Each wave owns
-// up to two query heads (row tiles) and keeps their rotated rows in MFMA
+// one query head (two when G > 4 or G = 2) and keeps its rotated rows in MFMA
 // operand registers for the whole unit.  The unit's keys stream twice:
 //   pass 1: D[key][row] = K Q^T on bf16 MFMA 32x32x16 (fp32 accumulate); each
 //           lane keeps an online (max, sum) of one row -> c_r;
@@ -357,7 +357,7 @@ hipError_t launch_d(const ScoreArgs& a, hipStream_t st) {
         case 1: return launch_one<D, 1, 1>(a, st);
         case 2: return launch_one<D, 1, 2>(a, st);
         case 3:
-        case 4: return launch_one<D, 2, 2>(a, st);
+        case 4: return launch_one<D, 4, 1>(a, st);
         default: return launch_one<D, 4, 2>(a, st);
     }
 }
