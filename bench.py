@@ -29,8 +29,93 @@ from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
 from long_reasoning_decode_amd.configs import EVICT_CONFIGS, QWEN3_4B
 
+HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 METRIC = "eviction steps/s (all layers x KV heads) at Qwen3-4B shape; % of HBM peak"
+# kernel -> the .hip file it is compiled from; its stored counters hold only while that file, everything it
+# includes and the build flags are unchanged
+KERNEL_SOURCE = {"compact_kernel": "bkv_compact.hip", "score_kernel": "bkv_score.hip",
+                 "select_kernel": "bkv_select.hip", "fps_kernel": "bkv_fps.hip"}
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_qwen3-4b.txt")
+
+
+def kernel_sources_sha256(kernel: str) -> str:
+    """sha256 over the kernel's .hip file, the local headers it includes (transitively) and build.py."""
+    import hashlib
+    import re
+    dirs = [os.path.join(HERE, "long_reasoning_decode_amd", "csrc"), os.path.join(HERE, "include")]
+    seen, todo, h = [], [KERNEL_SOURCE[kernel]], hashlib.sha256()
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.append(f)
+        path = next(os.path.join(d, f) for d in dirs if os.path.exists(os.path.join(d, f)))
+        text = open(path, "rb").read()
+        h.update(f.encode() + b"\0" + text)
+        todo += re.findall(r'#include "([^"]+)"', text.decode())
+    h.update(open(os.path.join(HERE, "long_reasoning_decode_amd", "build.py"), "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when there is
+    none or the kernel's sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("#"):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+        if f.get("kernel") == kernel:
+            if f.get("sources_sha256") != kernel_sources_sha256(kernel):
+                return None
+            return float(f["bytes_per_dispatch"])
+    return None
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, calib_bytes: int) -> str:
+    """Per-kernel HBM bytes from two rocprofv3 counter passes (CSV output): FETCH_SIZE in one,
+    WRITE_SIZE in the other, KiB per dispatch.  Each counter is scaled by what it reads for the run's
+    calibration copy (the longest copy dispatch, of calib_bytes read and calib_bytes written)."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        per = {}   # dispatch id -> [kernel name, duration ns, value]
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] != counter:
+                    continue
+                e = per.setdefault(r["Dispatch_Id"], [r["Kernel_Name"],
+                                                      int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), 0.0])
+                e[2] += float(r["Counter_Value"])
+        if not per:
+            raise SystemExit(f"no {counter} rows under {d}")
+        return per
+
+    lines = []
+    stats = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = load(d, counter)
+        copies = [e for e in per.values() if "copyBuffer" in e[0]]
+        cal = max(copies, key=lambda e: e[1])
+        factor = calib_bytes / (cal[2] * 1024.0)
+        lines.append(f"# calibration {counter}: copy of {calib_bytes} bytes ({cal[1] / 1e3:.0f} us) reads "
+                     f"{cal[2]:.0f} KiB -> factor {factor:.4f}")
+        for k in KERNEL_SOURCE:
+            vals = [e[2] for e in per.values() if k in e[0] and "bkv" in e[0]]
+            if vals:
+                stats.setdefault(k, {})[counter] = (float(np.mean(vals)), len(vals), factor)
+    for k, st in stats.items():
+        if len(st) != 2:
+            continue
+        (fk, nf, ff), (wk, nw, fw) = st["FETCH_SIZE"], st["WRITE_SIZE"]
+        b = fk * 1024 * ff + wk * 1024 * fw
+        lines.append(f"kernel={k} dispatches={nf},{nw} fetch_kib={fk:.0f} write_kib={wk:.0f} "
+                     f"fetch_bytes={fk * 1024 * ff:.4g} write_bytes={wk * 1024 * fw:.4g} bytes_per_dispatch={b:.6g} "
+                     f"sources_sha256={kernel_sources_sha256(k)}")
+    return "\n".join(lines) + "\n"
 
 
 def alg_bytes(cfg, qcount: np.ndarray, idx: np.ndarray, n_len: int) -> dict:
@@ -83,7 +168,15 @@ def main() -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device once (a plain copy kernel of "
                          "known size, for scaling hardware byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no benchmark: print per-kernel HBM bytes from two rocprofv3 --pmc runs of this script "
+                         "(FETCH_SIZE, then WRITE_SIZE, --output-format csv) made with --copy-calibration-mib")
     args = ap.parse_args()
+    if args.summarize_counters:
+        if args.copy_calibration_mib <= 0:
+            ap.error("--summarize-counters needs the --copy-calibration-mib the runs used")
+        print(summarize_counters(*args.summarize_counters, args.copy_calibration_mib << 20), end="")
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: runs on one GPU only; every (layer, batch, KV head) unit is independent, so "
               "a multi-GPU step would shard units by batch or KV head with no exchange; --gpus must be 1",
@@ -174,7 +267,8 @@ def main() -> int:
                                f"{cfg.n_recent_kv}, {cfg.n_beacon} beacons + {cfg.n_recent_q} recent queries",
                    "units": cfg.units, "n_len": N, "budget": cfg.budget},
         "roofline": {"bound": "hbm", "kernel": "compact", "achieved": compact_ach, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": compact_ach / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": compact_ach / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("compact_kernel")},
         "step_hbm": {"alg_bytes": step_bytes, "achieved_GBs": step_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "compact_alg_bytes": compact_bytes},
@@ -182,6 +276,8 @@ def main() -> int:
         "wall_s": wall,
     }
     if args.copy_calibration_mib > 0:
+        # one device-to-device copy of known size, larger than any other copy in the run, so that a
+        # counter pass can find it as the longest copy dispatch
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
