@@ -27,7 +27,7 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import EVICT_CONFIGS, QWEN3_4B
+from long_reasoning_decode_amd.configs import EVICT_CONFIGS, QWEN3_4B, STREAM, STREAM_CONFIGS
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
@@ -157,6 +157,37 @@ def cpu_baseline(cfg, inp, target_s: float = 10.0) -> dict:
                       f"on {threads} threads; scaled to whole steps"}
 
 
+def stream_bench(args) -> int:
+    """Streaming decode: tokens/s of the eviction manager (library calls only; each block's inputs are
+    drawn before its timed region) and its HBM footprint."""
+    from long_reasoning_decode_amd.stream import StreamRun
+    scfg = STREAM_CONFIGS[args.stream_config]
+    b = scfg.base
+    steps = args.stream_steps or scfg.steps
+    torch.cuda.set_device(0)
+    L.load()
+    print(f"# stream {scfg.name}: batch {b.batch}, {steps} steps, {b.units} units", file=sys.stderr, flush=True)
+    run = StreamRun(scfg)
+    torch.cuda.reset_peak_memory_stats()
+    prog = lambda r: (r.steps_done % 4096 == 0) and print(f"# step {r.steps_done}, evictions {r.n_ev}",
+                                                            file=sys.stderr, flush=True)
+    r = run.run(steps, timed=True, progress=prog)
+    tokens = b.batch * steps
+    out = {
+        "metric": "streaming decode: tokens/s through the eviction manager (decode-step bookkeeping + evictions)",
+        "value": tokens / (r["gpu_ms"] * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{scfg.name}: {b.n_layers} layers x batch {b.batch} x {b.hkv} KV heads "
+                               f"({b.units} units), {b.hq} query heads, head_dim {b.d}, cache {b.cap} -> "
+                               f"budget {b.budget}, evict every {b.n_new} steps",
+                   "evictions": r["evictions"]},
+        "gpu_s": r["gpu_ms"] * 1e-3, "wall_s_with_generation": r["wall_s"],
+        "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +199,11 @@ def main() -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy this many MiB device-to-device once (a plain copy kernel of "
                          "known size, for scaling hardware byte counters)")
+    ap.add_argument("--stream", action="store_true",
+                    help="instead of the eviction-step benchmark, run the streaming decode simulation "
+                         "(bkv_decode_step every step, bkv_evict when the cache is full) and print its own line")
+    ap.add_argument("--stream-config", default=STREAM.name, choices=sorted(STREAM_CONFIGS))
+    ap.add_argument("--stream-steps", type=int, default=0, help="decode steps (default: the config's)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: print per-kernel HBM bytes from two rocprofv3 --pmc runs of this script "
                          "(FETCH_SIZE, then WRITE_SIZE, --output-format csv) made with --copy-calibration-mib")
@@ -185,6 +221,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    if args.stream:
+        return stream_bench(args)
     cfg = EVICT_CONFIGS[args.config]
     torch.cuda.set_device(0)
     L.load()

@@ -167,6 +167,33 @@ int bkv_evict(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t n_len,
               int32_t *idx_out, float *scores_out, int32_t *fps_sel_out,
               void *ws, size_t ws_bytes, void *stream);
 
+/* One decode step of the eviction cycle (Notes §2.2 App. Alg. 2; Summary,
+ * pseudocode) at cache length L: rows [0, L) of every unit are valid and
+ * 0 <= L < cap.
+ *   - Unit u appends k_new[u], rotated to position pos[b] exactly as
+ *     bkv_score rotates its observation rows, at row L of K, and v_new[u]
+ *     at row L of V.
+ *   - Query buffer uq takes q_new[uq].  While L < cap - n_recent_q (the
+ *     cycle's collection phase) it is appended by bkv_fps_update's rule.  In
+ *     the last n_recent_q steps before the cache is full the buffer is left
+ *     as it is (its first rows are this cycle's beacons) and the query goes
+ *     to the recent ring: q_recent[uq][i] = q_new[uq], pos_recent[b][i] =
+ *     pos[b], i = L - (cap - n_recent_q).
+ * After the step with L = cap - 1 the cache is full; the caller then runs
+ * bkv_evict with n_len = cap and t = the last step's pos, which leaves
+ * L = budget.
+ * k_new, v_new: bf16 [units][head_dim] (k_new pre-RoPE); q_new: bf16
+ * [qbufs][head_dim]; pos: int32 [batch].  Positions are clamped to
+ * [0, rope_rows).  In/out: K, V (row L), qbuf, qcount, q_recent,
+ * pos_recent.  fps_sel (nullable) as in bkv_fps_update; not written in the
+ * ring phase.  Errors: BKV_ERANGE if L < 0, L >= cap or rope_rows <= 0;
+ * BKV_EINVAL for null or misaligned pointers. */
+int bkv_decode_step(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t L,
+                    const bkv_bf16 *k_new, const bkv_bf16 *v_new, const int32_t *pos,
+                    bkv_bf16 *qbuf, int32_t *qcount, const bkv_bf16 *q_new,
+                    bkv_bf16 *q_recent, int32_t *pos_recent,
+                    const float *rope_cs, int32_t rope_rows, int32_t *fps_sel, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,11 +92,28 @@ EVICT_CONFIGS = {c.name: c for c in (TINY, QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, Q
 
 @dataclass(frozen=True)
 class StreamConfig:
-    """Streaming decode: per-step buffer update, eviction every n_new steps."""
+    """Streaming decode from an empty cache: every step appends one token per
+    sequence and routes its queries (buffer update or recent ring); the cache
+    is evicted from cap = budget + n_new rows to budget, i.e. every n_new
+    steps once it is full.  Token s of sequence b sits at position p0_b + s,
+    p0_b ~ U[0, p0_max); query cluster centres drift every drift_every steps."""
     name: str = "stream-qwen3-4b"
     base: EvictConfig = replace(QWEN3_4B, batch=192, seed=20261202 + 500)
     steps: int = 32768
     drift_every: int = 2048
+    p0_max: int = 4096
+
+    @property
+    def rope_rows(self) -> int:
+        return self.p0_max + self.steps
+
+    def evictions(self, steps: int | None = None) -> int:
+        s = self.steps if steps is None else steps
+        c, n = self.base.cap, self.base.n_new
+        return 0 if s < c else 1 + (s - c) // n
 
 
 STREAM = StreamConfig()
+TINY_STREAM = StreamConfig(name="stream-tiny", base=replace(TINY, batch=2, seed=20261202 + 510),
+                           steps=600, drift_every=256, p0_max=1000)
+STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM)}

@@ -278,4 +278,61 @@ int bkv_evict(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, bkv_b
     return hip_status(bkv::launch_fps(fa, s->head_dim, true, st));
 }
 
+int bkv_decode_step(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t L, const bkv_bf16* k_new,
+                    const bkv_bf16* v_new, const int32_t* pos, bkv_bf16* qbuf, int32_t* qcount,
+                    const bkv_bf16* q_new, bkv_bf16* q_recent, int32_t* pos_recent, const float* rope_cs,
+                    int32_t rope_rows, int32_t* fps_sel, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (L < 0 || L >= s->cap || rope_rows <= 0) return BKV_ERANGE;
+    if (!K || !V || !k_new || !v_new || !pos || !qbuf || !qcount || !q_new || !rope_cs) return BKV_EINVAL;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(qbuf) ||
+        !aligned16(q_new) || !aligned16(rope_cs) || !aligned4(pos) || !aligned4(qcount))
+        return BKV_EINVAL;
+    const int32_t ring0 = s->cap - s->n_recent_q;   // first step of the recent phase
+    const bool ring = L >= ring0;
+    if (ring && (!q_recent || !pos_recent || !aligned16(q_recent) || !aligned4(pos_recent))) return BKV_EINVAL;
+    if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+
+    bkv::AppendArgs aa;
+    aa.K = K;
+    aa.V = V;
+    aa.k_new = k_new;
+    aa.v_new = v_new;
+    aa.pos = pos;
+    aa.rope_cs = rope_cs;
+    aa.units = units_of(s);
+    aa.cap = s->cap;
+    aa.L = L;
+    aa.batch = s->batch;
+    aa.hkv = s->n_kv_heads;
+    aa.rope_rows = rope_rows;
+    if ((e = hip_status(bkv::launch_append(aa, s->head_dim, st)))) return e;
+
+    if (ring) {
+        bkv::RingArgs ra;
+        ra.q_recent = q_recent;
+        ra.pos_recent = pos_recent;
+        ra.q_new = q_new;
+        ra.pos = pos;
+        ra.qbufs = qbufs_of(s);
+        ra.batch = s->batch;
+        ra.n_recent_q = s->n_recent_q;
+        ra.slot = L - ring0;
+        return hip_status(bkv::launch_ring(ra, s->head_dim, st));
+    }
+    bkv::FpsArgs fa;
+    fa.qbuf = qbuf;
+    fa.qcount = qcount;
+    fa.q_new = q_new;
+    fa.q_recent = nullptr;
+    fa.fps_sel = fps_sel;
+    fa.nbuf = qbufs_of(s);
+    fa.qcap = s->qcap;
+    fa.n_beacon = s->n_beacon;
+    fa.n_recent_q = s->n_recent_q;
+    return hip_status(bkv::launch_fps(fa, s->head_dim, false, st));
+}
+
 }  // extern "C"

@@ -1,6 +1,6 @@
 // bkv_fps_impl.hpp -- continual farthest point sampling of pre-RoPE queries,
-// one wavefront per query buffer (device functions shared by the FPS kernels
-// and the fused eviction tail).
+// one wavefront per query buffer (device functions of the buffer-update and
+// merge kernels).
 //
 // The Gram matrix of the (at most 32) candidates is register-blocked 4 x 4
 // per lane (64 lanes cover the 32 x 32 entries); the rows stream through LDS

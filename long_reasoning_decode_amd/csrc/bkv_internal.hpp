@@ -42,9 +42,29 @@ struct CompactArgs {
     int units, n_len, cap, budget;
 };
 
+struct AppendArgs {
+    bkv_bf16* K;               // [units][cap][d]
+    bkv_bf16* V;
+    const bkv_bf16* k_new;     // [units][d] pre-RoPE
+    const bkv_bf16* v_new;     // [units][d]
+    const int32_t* pos;        // [batch]
+    const float* rope_cs;      // [rope_rows][d/2][2]
+    int units, cap, L, batch, hkv, rope_rows;
+};
+
+struct RingArgs {
+    bkv_bf16* q_recent;        // [qbufs][n_recent_q][d]
+    int32_t* pos_recent;       // [batch][n_recent_q]
+    const bkv_bf16* q_new;     // [qbufs][d]
+    const int32_t* pos;        // [batch]
+    int qbufs, batch, n_recent_q, slot;
+};
+
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, int d, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 hipError_t launch_compact(const CompactArgs& a, int d, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, int d, hipStream_t st);
+hipError_t launch_ring(const RingArgs& a, int d, hipStream_t st);
 
 }  // namespace bkv

@@ -24,7 +24,7 @@ BKV_CAUSAL_RECENT = 1
 ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE", -4: "BKV_EHIP"}
 
 EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_workspace_bytes", "bkv_fps_update",
-           "bkv_fps_merge", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict")
+           "bkv_fps_merge", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict", "bkv_decode_step")
 
 
 class Shape(C.Structure):
@@ -64,6 +64,7 @@ def load():
         L.bkv_select.argtypes = [SP, P, i32, P, st]
         L.bkv_compact.argtypes = [SP, P, P, i32, P, st]
         L.bkv_evict.argtypes = [SP, P, P, i32, P, P, P, P, P, P, i32, P, P, P, P, C.c_size_t, st]
+        L.bkv_decode_step.argtypes = [SP, P, P, i32, P, P, P, P, P, P, P, P, P, i32, P, st]
         for f in EXPORTS[4:]:
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -166,3 +167,13 @@ def evict(shape: Shape, K, V, n_len: int, qbuf, qcount, q_recent, pos_recent, t,
                             _ptr(fps_sel_out, i32, "fps_sel_out"),
                             None if ws is None else C.c_void_p(ws.data_ptr()), C.c_size_t(ws_bytes),
                             _stream(stream)), "bkv_evict")
+
+
+def decode_step(shape: Shape, K, V, L: int, k_new, v_new, pos, qbuf, qcount, q_new, q_recent, pos_recent,
+                rope_cs, fps_sel=None, stream=None) -> None:
+    _check(load().bkv_decode_step(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(L),
+                                  _ptr(k_new, bf16, "k_new"), _ptr(v_new, bf16, "v_new"), _ptr(pos, i32, "pos"),
+                                  _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(q_new, bf16, "q_new"),
+                                  _ptr(q_recent, bf16, "q_recent"), _ptr(pos_recent, i32, "pos_recent"),
+                                  _ptr(rope_cs, f32, "rope_cs"), int(rope_cs.shape[0]),
+                                  _ptr(fps_sel, i32, "fps_sel"), _stream(stream)), "bkv_decode_step")

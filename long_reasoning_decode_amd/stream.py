@@ -1,0 +1,127 @@
+"""Simulated decode loop around the eviction manager.
+
+This is the caller's side of ``bkv_decode_step`` and ``bkv_evict``: a stand-in
+for the model's decode loop (Notes §2.2, App. Alg. 2; Summary, pseudocode).
+It draws every step's pre-RoPE q/k/v with ``synth.StreamGen``, hands them to
+the library one decode step at a time, and evicts whenever the cache is full.
+The library does all of the method's work; this loop only keeps the cache
+length and passes pointers.
+
+Inputs are drawn a block of steps at a time, before the block's library calls,
+so that timing a block (``timed=True``) measures the eviction manager alone.
+"""
+from __future__ import annotations
+
+import time
+
+import torch
+
+from . import lib, synth
+from .configs import StreamConfig
+
+
+class StreamRun:
+    """State of one simulated decode stream on the GPU.
+
+    record_units: optional unit indices u = (l * batch + b) * Hkv + g whose
+    step inputs and eviction results are kept (for checking against the
+    oracle): ``hist`` holds q_new [S, Us, G, d], k_new / v_new [S, Us, d],
+    pos [S, Us], and per eviction idx [E, Us, budget], scores [E, Us, cap]."""
+
+    def __init__(self, scfg: StreamConfig, device="cuda", seed=None, record_units=None, block: int = 128):
+        b = scfg.base
+        self.scfg, self.base = scfg, b
+        self.device = torch.device(device)
+        self.shape = lib.shape_of(b)
+        dev = self.device
+        L, B, Hq, Hkv, d = b.n_layers, b.batch, b.hq, b.hkv, b.d
+        self.K = torch.zeros(L, B, Hkv, b.cap, d, dtype=torch.bfloat16, device=dev)
+        self.V = torch.zeros_like(self.K)
+        self.qbuf = torch.zeros(L, B, Hq, b.qcap, d, dtype=torch.bfloat16, device=dev)
+        self.qcount = torch.zeros(L, B, Hq, dtype=torch.int32, device=dev)
+        self.q_recent = torch.zeros(L, B, Hq, b.n_recent_q, d, dtype=torch.bfloat16, device=dev)
+        self.pos_recent = torch.zeros(B, b.n_recent_q, dtype=torch.int32, device=dev)
+        self.rope = torch.from_numpy(lib.rope_table(b.theta, d, 0, scfg.rope_rows)).to(dev)
+        self.idx = torch.empty(b.units, b.budget, dtype=torch.int32, device=dev)
+        self.scores = torch.empty(b.units, b.cap, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(lib.workspace_bytes(self.shape, b.cap), 256), dtype=torch.uint8, device=dev)
+        self.gen = synth.StreamGen(scfg, dev, seed)
+        self.block_steps = block
+        self.pool = self.gen.alloc(block)
+        self.L = 0
+        self.n_ev = 0
+        self.steps_done = 0
+        self.rec = None
+        if record_units is not None:
+            self.rec_units = torch.tensor(list(record_units), dtype=torch.long, device=dev)
+            self.rec_b = (self.rec_units // Hkv) % B
+            self.rec = {k: [] for k in ("q_new", "k_new", "v_new", "pos", "idx", "scores")}
+
+    def state_bytes(self) -> int:
+        """HBM held by the eviction manager's own state (cache, buffers, ring, table, workspace)."""
+        ts = (self.K, self.V, self.qbuf, self.qcount, self.q_recent, self.pos_recent, self.rope, self.idx,
+              self.scores, self.ws)
+        return sum(t.numel() * t.element_size() for t in ts)
+
+    def _record_inputs(self, blk: dict, n: int) -> None:
+        b = self.base
+        U, G, d = b.units, b.G, b.d
+        r, u = self.rec, self.rec_units
+        r["q_new"].append(blk["q_new"][:n].reshape(n, U, G, d).index_select(1, u))
+        r["k_new"].append(blk["k_new"][:n].reshape(n, U, d).index_select(1, u))
+        r["v_new"].append(blk["v_new"][:n].reshape(n, U, d).index_select(1, u))
+        r["pos"].append(blk["pos"][:n].index_select(1, self.rec_b))
+
+    def run(self, steps: int | None = None, timed: bool = False, stream=None, progress=None) -> dict:
+        """Run `steps` decode steps (default: the config's).  Returns the step count, evictions and,
+        when timed, the summed GPU time of the library calls (generation excluded)."""
+        b = self.base
+        steps = self.scfg.steps if steps is None else steps
+        stream = torch.cuda.current_stream() if stream is None else stream
+        gpu_ms = 0.0
+        t0 = time.perf_counter()
+        done = 0
+        while done < steps:
+            n = min(self.block_steps, steps - done)
+            blk = self.gen.block(n, self.pool)
+            if self.rec is not None:
+                self._record_inputs(blk, n)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            for i in range(n):
+                lib.decode_step(self.shape, self.K, self.V, self.L, blk["k_new"][i], blk["v_new"][i], blk["pos"][i],
+                                self.qbuf, self.qcount, blk["q_new"][i], self.q_recent, self.pos_recent, self.rope,
+                                stream=stream)
+                self.L += 1
+                if self.L == b.cap:
+                    lib.evict(self.shape, self.K, self.V, b.cap, self.qbuf, self.qcount, self.q_recent,
+                              self.pos_recent, blk["pos"][i], self.rope, idx_out=self.idx, scores_out=self.scores,
+                              ws=self.ws, stream=stream)
+                    if self.rec is not None:
+                        self.rec["idx"].append(self.idx.index_select(0, self.rec_units))
+                        self.rec["scores"].append(self.scores.index_select(0, self.rec_units))
+                    self.n_ev += 1
+                    self.L = b.budget
+            if timed:
+                e1.record(stream)
+                e1.synchronize()
+                gpu_ms += e0.elapsed_time(e1)
+            done += n
+            self.steps_done += n
+            if progress is not None:
+                progress(self)
+        torch.cuda.synchronize()
+        return {"steps": steps, "evictions": self.n_ev, "L": self.L, "gpu_ms": gpu_ms if timed else None,
+                "wall_s": time.perf_counter() - t0}
+
+    def history(self) -> dict:
+        """Recorded inputs and eviction results as host tensors (see the class docstring)."""
+        out = {}
+        for k, v in self.rec.items():
+            out[k] = torch.cat(v, 0).cpu() if v else None
+        if out["idx"] is not None:
+            E = len(self.rec["idx"])
+            out["idx"] = out["idx"].reshape(E, -1, self.base.budget)
+            out["scores"] = out["scores"].reshape(E, -1, self.base.cap)
+        return out

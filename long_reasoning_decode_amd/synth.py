@@ -143,6 +143,75 @@ def make_query_buffers(cfg: EvictConfig, device="cpu", seed: int | None = None,
 
 
 # ---------------------------------------------------------------------------
+# Streaming decode inputs.
+
+class StreamGen:
+    """Per-step inputs of the streaming decode simulation, drawn block by
+    block on the generator's device:
+      q_new [n, L, B, Hq, d]   bf16, pre-RoPE, the query mixture of the base
+                               config around per-(layer, batch, q-head) centres
+      k_new [n, L, B, Hkv, d]  bf16, pre-RoPE keys (N(0, I), 1% rows x 8)
+      v_new [n, L, B, Hkv, d]  bf16, N(0, I)
+      pos   [n, B]             int32, p0_b + s for global step s
+    Every drift_every steps (before step s = k * drift_every, k >= 1) each
+    centre becomes normalize(u_c + 0.5 g), g ~ N(0, I_d / d)."""
+
+    def __init__(self, scfg, device="cpu", seed: int | None = None):
+        base = scfg.base
+        self.scfg, self.base = scfg, base
+        self.device = torch.device(device)
+        self.g = _gen(self.device, base.seed if seed is None else seed)
+        L, B, Hq, d = base.n_layers, base.batch, base.hq, base.d
+        self.centres = _unit_rows(self.g, (L, B, Hq, n_centres(base.mix)), d, self.device)
+        self.p0 = torch.randint(0, scfg.p0_max, (B,), generator=self.g, device=self.device, dtype=torch.int64)
+        self.step = 0
+        self._last_drift = 0
+
+    def _drift(self) -> None:
+        d = self.base.d
+        g = torch.randn(self.centres.shape, generator=self.g, device=self.device) / math.sqrt(d)
+        c = self.centres + 0.5 * g
+        self.centres = c / c.norm(dim=-1, keepdim=True)
+
+    def _draw(self, n: int, out: dict, at: int) -> None:
+        b = self.base
+        L, B, Hq, Hkv, d = b.n_layers, b.batch, b.hq, b.hkv, b.d
+        q = query_rows(self.g, self.centres, n, b.mix)                  # [L, B, Hq, n, d]
+        out["q_new"][at:at + n] = q.permute(3, 0, 1, 2, 4).to(torch.bfloat16)
+        del q
+        out["k_new"][at:at + n] = key_rows(self.g, (n, L, B, Hkv), 1, d, self.device)[..., 0, :].to(torch.bfloat16)
+        out["v_new"][at:at + n] = torch.randn(n, L, B, Hkv, d, generator=self.g,
+                                              device=self.device).to(torch.bfloat16)
+        s = torch.arange(self.step, self.step + n, device=self.device, dtype=torch.int64)
+        out["pos"][at:at + n] = (self.p0.unsqueeze(0) + s.unsqueeze(1)).to(torch.int32)
+
+    def alloc(self, n: int) -> dict:
+        b = self.base
+        L, B, Hq, Hkv, d = b.n_layers, b.batch, b.hq, b.hkv, b.d
+        dev = self.device
+        return {"q_new": torch.empty(n, L, B, Hq, d, dtype=torch.bfloat16, device=dev),
+                "k_new": torch.empty(n, L, B, Hkv, d, dtype=torch.bfloat16, device=dev),
+                "v_new": torch.empty(n, L, B, Hkv, d, dtype=torch.bfloat16, device=dev),
+                "pos": torch.empty(n, B, dtype=torch.int32, device=dev)}
+
+    def block(self, n: int, out: dict | None = None, chunk: int = 16) -> dict:
+        """The next n steps' inputs (into `out` when given, a dict from alloc(>= n)).
+        Draws at most `chunk` steps at a time to bound the fp32 temporaries."""
+        out = self.alloc(n) if out is None else out
+        at = 0
+        while at < n:
+            if self.step % self.scfg.drift_every == 0 and self.step != self._last_drift:
+                self._drift()
+                self._last_drift = self.step
+            to_drift = self.scfg.drift_every - self.step % self.scfg.drift_every
+            k = min(chunk, n - at, to_drift)
+            self._draw(k, out, at)
+            self.step += k
+            at += k
+        return out
+
+
+# ---------------------------------------------------------------------------
 # Views for the oracle (numpy, unit-major).
 
 def to_u16(x: torch.Tensor):

@@ -87,6 +87,8 @@ def lib():
         L.bkvo_evict.argtypes = [P, i32, i32, P, P, P, P, P, P, P, P, P, P, P, i32]
         L.bkvo_merge.argtypes = [P, i32, P, P, P, P]
         L.bkvo_compact.argtypes = [P, i32, i32, P, P, P]
+        L.bkvo_stream.argtypes = [P, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, i32, i32]
+        L.bkvo_stream.restype = i32
         L.bkvo_cfg_size.restype = i32
         assert L.bkvo_cfg_size() == C.sizeof(_Cfg), "oracle cfg struct mismatch"
         _lib = L
@@ -234,3 +236,27 @@ def compact(cfg: OracleCfg, K, V, idx, n_len: int | None = None) -> None:
     N = cfg.cap if n_len is None else n_len
     cc = cfg.c()
     lib().bkvo_compact(C.byref(cc), U, N, _p(K), _p(V), _p(_i32(idx)))
+
+
+def stream(cfg: OracleCfg, k_new, v_new, q_new, pos, K, V, L: int, qbuf, qcount, q_recent, pos_recent,
+           max_ev: int = 0, nthreads: int | None = None) -> dict:
+    """Decode steps of the eviction cycle for U units in lockstep, in place on the state (K, V, qbuf,
+    qcount, q_recent, pos_recent: unit-major numpy arrays).  Step inputs are step-major:
+    k_new, v_new [S, U, d] (k_new pre-RoPE), q_new [S, U, G, d], pos [S, U].
+    Returns the final cache length, the number of evictions and the first max_ev evictions'
+    keep sets [max_ev, U, budget] and scores [max_ev, U, cap]."""
+    for a, dt in ((K, np.uint16), (V, np.uint16), (qbuf, np.uint16), (qcount, np.int32),
+                  (q_recent, np.uint16), (pos_recent, np.int32)):
+        assert a.dtype == dt and a.flags["C_CONTIGUOUS"]
+    k_new, v_new, q_new, pos = _u16(k_new), _u16(v_new), _u16(q_new), _i32(pos)
+    S, U = pos.shape
+    assert k_new.shape == (S, U, cfg.d) and v_new.shape == (S, U, cfg.d)
+    assert q_new.shape == (S, U, cfg.G, cfg.d)
+    idx = np.full((max_ev, U, cfg.budget), -1, dtype=np.int32) if max_ev > 0 else None
+    sc = np.zeros((max_ev, U, cfg.cap), dtype=np.float64) if max_ev > 0 else None
+    Lb = C.c_int32(int(L))
+    cc = cfg.c()
+    n_ev = lib().bkvo_stream(C.byref(cc), U, S, _p(k_new), _p(v_new), _p(q_new), _p(pos), _p(K), _p(V),
+                             C.byref(Lb), _p(qbuf), _p(qcount), _p(q_recent), _p(pos_recent), _p(idx), _p(sc),
+                             max_ev, nthreads or default_threads())
+    return {"L": Lb.value, "n_ev": n_ev, "idx": idx, "scores": sc}

@@ -613,4 +613,127 @@ void bkvo_compact(const bkvo_cfg *cfg, int U, int N, uint16_t *K, uint16_t *V, c
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Streaming decode cycle (Notes §2.2, App. Alg. 2; Summary, pseudocode) for
+ * U units whose caches have the same length L.  Each decode step s < S, per
+ * unit u (inputs step-major: k_new, v_new [S][U][d], q_new [S][U][G][d],
+ * pos [S][U], the position of step s's token in u's sequence):
+ *   1. the new key, rotated to its position, and the new value become row L
+ *      of the unit's K and V;
+ *   2. while L < cap - n_recent_q (the cycle's collection phase) each of the
+ *      unit's G query buffers takes its new pre-RoPE query by the continual
+ *      FPS update; in the last n_recent_q steps before the cache is full the
+ *      buffers stay frozen (their first rows are the cycle's beacons) and the
+ *      query goes to recent slot i = L - (cap - n_recent_q) with its position;
+ *   3. L grows by one; when it reaches cap the unit is evicted with N = cap
+ *      and t = this step's position -- scores, keep set, compaction, merge
+ *      FPS of beacons and recents -- and L becomes budget.
+ * State, in/out, unit-major as for bkvo_evict: K, V [U][cap][d], qbuf
+ * [U][G][qcap][d], qcount [U][G], q_recent [U][G][n_recent_q][d],
+ * pos_recent [U][n_recent_q]; *L_io is the shared cache length.  idx_hist
+ * [max_ev][U][budget] and score_hist [max_ev][U][cap] (nullable) receive the
+ * first max_ev evictions' keep sets and scores.  Returns the number of
+ * evictions.                                                               */
+typedef struct {
+    const bkvo_cfg *cfg;
+    int U, S, L0;
+    const uint16_t *k_new, *v_new, *q_new;
+    const int32_t *pos;
+    uint16_t *K, *V, *qbuf, *q_recent;
+    int32_t *qcount, *pos_recent, *t;
+    int32_t *idx_hist;
+    double *score_hist;
+    int max_ev;
+    int u0, u1;
+    int n_ev, L_end;
+} stream_job;
+
+static void *run_stream_units(void *arg)
+{
+    stream_job *J = (stream_job *)arg;
+    const bkvo_cfg *c = J->cfg;
+    int d = c->d, G = c->hq / c->hkv, U = J->U, nrq = c->n_recent_q;
+    int ring0 = c->cap - nrq;
+    double *sc = (double *)malloc(sizeof(double) * (size_t)c->cap);
+    int32_t *ix = (int32_t *)malloc(sizeof(int32_t) * (size_t)(c->budget > 0 ? c->budget : 1));
+    for (int u = J->u0; u < J->u1; ++u) {
+        int L = J->L0, ne = 0;
+        uint16_t *Ku = J->K + (size_t)u * c->cap * d;
+        uint16_t *Vu = J->V + (size_t)u * c->cap * d;
+        for (int s = 0; s < J->S; ++s) {
+            size_t su = (size_t)s * U + u;
+            int p = J->pos[su];
+            bkvo_rope_row(J->k_new + su * d, d, c->theta, p, Ku + (size_t)L * d);
+            memcpy(Vu + (size_t)L * d, J->v_new + su * d, sizeof(uint16_t) * (size_t)d);
+            const uint16_t *qn = J->q_new + su * G * d;
+            if (L < ring0) {
+                bkvo_fps_update(G, c->qcap, d, c->n_beacon, nrq, J->qbuf + (size_t)u * G * c->qcap * d,
+                                J->qcount + (size_t)u * G, qn, NULL);
+            } else {
+                int i = L - ring0;
+                for (int h = 0; h < G; ++h)
+                    memcpy(J->q_recent + (((size_t)u * G + h) * nrq + i) * d, qn + (size_t)h * d,
+                           sizeof(uint16_t) * (size_t)d);
+                J->pos_recent[(size_t)u * nrq + i] = p;
+            }
+            L += 1;
+            if (L == c->cap) {
+                J->t[u] = p;
+                score_unit(c, c->cap, u, J->K, J->qbuf, J->qcount, J->q_recent, J->pos_recent, J->t, sc);
+                bkvo_select(sc, c->cap, c->budget, c->n_prefix, c->n_recent_kv, ix);
+                compact_rows(Ku, d, c->cap, ix, c->budget);
+                compact_rows(Vu, d, c->cap, ix, c->budget);
+                merge_unit(c, u, J->qbuf, J->qcount, J->q_recent, NULL);
+                if (ne < J->max_ev) {
+                    if (J->idx_hist)
+                        memcpy(J->idx_hist + ((size_t)ne * U + u) * c->budget, ix,
+                               sizeof(int32_t) * (size_t)c->budget);
+                    if (J->score_hist)
+                        memcpy(J->score_hist + ((size_t)ne * U + u) * c->cap, sc, sizeof(double) * (size_t)c->cap);
+                }
+                ++ne;
+                L = c->budget < c->cap ? c->budget : c->cap;
+            }
+        }
+        J->n_ev = ne;
+        J->L_end = L;
+    }
+    free(sc);
+    free(ix);
+    return NULL;
+}
+
+int bkvo_stream(const bkvo_cfg *cfg, int U, int S, const uint16_t *k_new, const uint16_t *v_new,
+                const uint16_t *q_new, const int32_t *pos, uint16_t *K, uint16_t *V, int32_t *L_io,
+                uint16_t *qbuf, int32_t *qcount, uint16_t *q_recent, int32_t *pos_recent,
+                int32_t *idx_hist, double *score_hist, int max_ev, int nthreads)
+{
+    if (U <= 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > U) nthreads = U;
+    int32_t *t = (int32_t *)calloc((size_t)U, sizeof(int32_t));
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    stream_job *jobs = (stream_job *)malloc(sizeof(stream_job) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) {
+        stream_job *J = &jobs[i];
+        memset(J, 0, sizeof *J);
+        J->cfg = cfg; J->U = U; J->S = S; J->L0 = *L_io;
+        J->k_new = k_new; J->v_new = v_new; J->q_new = q_new; J->pos = pos;
+        J->K = K; J->V = V; J->qbuf = qbuf; J->q_recent = q_recent;
+        J->qcount = qcount; J->pos_recent = pos_recent; J->t = t;
+        J->idx_hist = idx_hist; J->score_hist = score_hist; J->max_ev = max_ev;
+        J->u0 = (int)((long)U * i / nthreads);
+        J->u1 = (int)((long)U * (i + 1) / nthreads);
+        J->L_end = J->L0;
+        pthread_create(&th[i], NULL, run_stream_units, J);
+    }
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    int n_ev = jobs[0].n_ev;
+    *L_io = jobs[0].L_end;
+    free(th);
+    free(jobs);
+    free(t);
+    return n_ev;
+}
+
 int bkvo_cfg_size(void) { return (int)sizeof(bkvo_cfg); }

@@ -1,0 +1,71 @@
+"""Helpers of the streaming-decode tests: oracle replay of recorded units and
+comparison with the GPU stream."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+from long_reasoning_decode_amd.configs import StreamConfig
+
+from _helpers import check_keep, check_scores
+
+
+def stream_ocfg(scfg: StreamConfig) -> O.OracleCfg:
+    b = scfg.base
+    return O.OracleCfg(hq=b.hq, hkv=b.hkv, d=b.d, cap=b.cap, budget=b.budget, n_prefix=b.n_prefix,
+                       n_recent_kv=b.n_recent_kv, n_beacon=b.n_beacon, n_recent_q=b.n_recent_q, theta=b.theta,
+                       qcap=b.qcap, n_layers=b.n_layers, batch=b.batch)
+
+
+def empty_state(scfg: StreamConfig, U: int) -> dict:
+    b = scfg.base
+    G, d = b.G, b.d
+    return {"K": np.zeros((U, b.cap, d), np.uint16), "V": np.zeros((U, b.cap, d), np.uint16),
+            "qbuf": np.zeros((U, G, b.qcap, d), np.uint16), "qcount": np.zeros((U, G), np.int32),
+            "q_recent": np.zeros((U, G, b.n_recent_q, d), np.uint16),
+            "pos_recent": np.zeros((U, b.n_recent_q), np.int32)}
+
+
+def replay(scfg: StreamConfig, k_new, v_new, q_new, pos, max_ev: int, nthreads=None) -> dict:
+    """Oracle stream from an empty state over step-major inputs of U units."""
+    st = empty_state(scfg, pos.shape[1])
+    o = O.stream(stream_ocfg(scfg), k_new, v_new, q_new, pos, st["K"], st["V"], 0, st["qbuf"], st["qcount"],
+                 st["q_recent"], st["pos_recent"], max_ev=max_ev, nthreads=nthreads)
+    o.update(st)
+    return o
+
+
+def compare_stream(scfg: StreamConfig, o: dict, g_idx, g_scores, g_state: dict, where: str = "") -> dict:
+    """Per unit: every eviction's kept set and scores, then the final state.
+
+    Keep sets must equal the oracle's or differ only within the tie band; after
+    such a (correct) difference the unit's cache legitimately differs from the
+    oracle's, so later evictions and its final K/V are not compared.  The
+    query-buffer state does not depend on the cache and is always compared."""
+    b = scfg.base
+    E, U = o["idx"].shape[:2]
+    assert g_idx.shape[:2] == (E, U), (g_idx.shape, E, U)
+    diverged = {}
+    for k in range(U):
+        for e in range(E):
+            w = f"{where} unit {k} eviction {e}"
+            check_scores(g_scores[e, k], o["scores"][e, k], w)
+            if np.array_equal(g_idx[e, k], o["idx"][e, k]):
+                continue
+            check_keep(g_idx[e, k], o["idx"][e, k], o["scores"][e, k], b.cap, b.budget, b.n_prefix,
+                       b.n_recent_kv, w)
+            diverged[k] = e
+            break
+    L = o["L"]
+    for k in range(U):
+        w = f"{where} unit {k}"
+        if k not in diverged:
+            assert np.array_equal(g_state["K"][k, :L], o["K"][k, :L]), f"{w}: K rows"
+            assert np.array_equal(g_state["V"][k, :L], o["V"][k, :L]), f"{w}: V rows"
+        assert np.array_equal(g_state["qcount"][k], o["qcount"][k]), f"{w}: qcount"
+        for h in range(b.G):
+            n = int(o["qcount"][k, h])
+            assert np.array_equal(g_state["qbuf"][k, h, :n], o["qbuf"][k, h, :n]), f"{w} head {h}: buffer"
+        assert np.array_equal(g_state["q_recent"][k], o["q_recent"][k]), f"{w}: recent ring"
+        assert np.array_equal(g_state["pos_recent"][k], o["pos_recent"][k]), f"{w}: ring positions"
+    return {"diverged": diverged}

@@ -1,0 +1,89 @@
+"""Streaming decode on the GPU (bkv_decode_step every step, bkv_evict when the
+cache is full) against the oracle's replay of the same per-step inputs."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from long_reasoning_decode_amd import lib as L
+from long_reasoning_decode_amd import synth
+from long_reasoning_decode_amd.configs import STREAM, TINY_STREAM
+from long_reasoning_decode_amd.stream import StreamRun
+
+from _stream_helpers import compare_stream, replay
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_state(run: StreamRun, units) -> dict:
+    b = run.base
+    U, G, d = b.units, b.G, b.d
+    ut = torch.tensor(list(units), dtype=torch.long, device="cuda")
+    bt = (ut // b.hkv) % b.batch
+    return {"K": synth.to_u16(run.K.reshape(U, b.cap, d).index_select(0, ut)),
+            "V": synth.to_u16(run.V.reshape(U, b.cap, d).index_select(0, ut)),
+            "qbuf": synth.to_u16(run.qbuf.reshape(U, G, b.qcap, d).index_select(0, ut)),
+            "qcount": run.qcount.reshape(U, G).index_select(0, ut).cpu().numpy(),
+            "q_recent": synth.to_u16(run.q_recent.reshape(U, G, b.n_recent_q, d).index_select(0, ut)),
+            "pos_recent": run.pos_recent.index_select(0, bt).cpu().numpy()}
+
+
+def _check(scfg, run: StreamRun, units, where, nthreads=None):
+    h = run.history()
+    u16 = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    o = replay(scfg, u16(h["k_new"]), u16(h["v_new"]), u16(h["q_new"]), h["pos"].numpy().astype(np.int32),
+               max_ev=run.n_ev, nthreads=nthreads)
+    assert o["n_ev"] == run.n_ev and o["L"] == run.L
+    res = compare_stream(scfg, o, h["idx"].numpy(), h["scores"].numpy(), _gpu_state(run, units), where)
+    print(f"{where}: {run.n_ev} evictions, L={run.L}, tie-band divergences {res['diverged']}", flush=True)
+    return res
+
+
+def test_stream_tiny_all_units():
+    scfg = TINY_STREAM
+    units = range(scfg.base.units)
+    run = StreamRun(scfg, record_units=units, block=48)
+    r = run.run()
+    assert r["evictions"] == scfg.evictions() == 14
+    res = _check(scfg, run, units, "stream-tiny")
+    assert len(res["diverged"]) <= 1
+
+
+def test_stream_tiny_resumes_across_calls():
+    """Running the steps in several calls (blocks ending mid-cycle) gives the
+    same stream as one call."""
+    scfg = TINY_STREAM
+    units = range(scfg.base.units)
+    run = StreamRun(scfg, record_units=units, block=37)
+    for n in (100, 61, 200, 239):
+        run.run(n)
+    assert run.steps_done == scfg.steps
+    _check(scfg, run, units, "stream-tiny resumed")
+
+
+def test_decode_step_rejects_bad_length():
+    scfg = TINY_STREAM
+    run = StreamRun(scfg, block=4)
+    blk = run.gen.block(1, run.pool)
+    for bad in (-1, scfg.base.cap):
+        with pytest.raises(L.BkvError) as e:
+            L.decode_step(run.shape, run.K, run.V, bad, blk["k_new"][0], blk["v_new"][0], blk["pos"][0], run.qbuf,
+                          run.qcount, blk["q_new"][0], run.q_recent, run.pos_recent, run.rope)
+        assert e.value.code == -3
+
+
+def test_stream_full_size_sampled_units():
+    """The streaming workload at full size: Qwen3-4B shape, batch 192, 32768
+    decode steps (240 evictions), checked on units spread over layers, batch
+    elements and KV heads."""
+    scfg = STREAM
+    b = scfg.base
+    units = [0, b.units - 1, 7 * b.batch * b.hkv + 93 * b.hkv + 3, 20 * b.batch * b.hkv + 150 * b.hkv + 6,
+             35 * b.batch * b.hkv + 11 * b.hkv + 1, 13 * b.batch * b.hkv + 64 * b.hkv + 4]
+    run = StreamRun(scfg, record_units=units)
+    prog = lambda r: (r.steps_done % 4096 == 0) and print(f"  step {r.steps_done}, evictions {r.n_ev}", flush=True)
+    r = run.run(progress=prog)
+    assert r["evictions"] == scfg.evictions() == 240
+    res = _check(scfg, run, units, "stream-qwen3-4b b192", nthreads=len(units))
+    assert len(res["diverged"]) <= 2

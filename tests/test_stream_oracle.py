@@ -1,0 +1,106 @@
+"""The oracle's streaming decode cycle (Notes §2.2, App. Alg. 2; Summary,
+pseudocode), pinned on the CPU: it equals the step-by-step composition of the
+separately pinned calls, and the cache it leaves obeys the cycle's
+invariants."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as O
+from long_reasoning_decode_amd import synth
+from long_reasoning_decode_amd.configs import TINY_STREAM
+
+from _stream_helpers import empty_state, replay, stream_ocfg
+
+
+def _inputs(scfg, S, seed=None):
+    b = scfg.base
+    U, G, d = b.units, b.G, b.d
+    gen = synth.StreamGen(scfg, "cpu", seed)
+    blk = gen.block(S)
+    b_of = [(u // b.hkv) % b.batch for u in range(U)]
+    return {"k_new": synth.to_u16(blk["k_new"].reshape(S, U, d)),
+            "v_new": synth.to_u16(blk["v_new"].reshape(S, U, d)),
+            "q_new": synth.to_u16(blk["q_new"].reshape(S, U, G, d)),
+            "pos": np.ascontiguousarray(blk["pos"].numpy()[:, b_of]).astype(np.int32)}
+
+
+def test_stream_equals_composition_of_calls():
+    scfg = TINY_STREAM
+    b = scfg.base
+    S = 260    # first eviction after 160 steps, then every 32
+    x = _inputs(scfg, S)
+    U = b.units
+    o = replay(scfg, x["k_new"], x["v_new"], x["q_new"], x["pos"], max_ev=8, nthreads=2)
+
+    st = empty_state(scfg, U)
+    oc = stream_ocfg(scfg)
+    ring0 = b.cap - b.n_recent_q
+    L, idx_hist, sc_hist = 0, [], []
+    for s in range(S):
+        for u in range(U):
+            st["K"][u, L] = O.rope_row(x["k_new"][s, u], b.theta, int(x["pos"][s, u]))
+            st["V"][u, L] = x["v_new"][s, u]
+            if L < ring0:
+                O.fps_update(st["qbuf"][u], st["qcount"][u], x["q_new"][s, u], b.n_beacon, b.n_recent_q)
+            else:
+                st["q_recent"][u, :, L - ring0] = x["q_new"][s, u]
+                st["pos_recent"][u, L - ring0] = x["pos"][s, u]
+        L += 1
+        if L == b.cap:
+            r = O.evict(oc, st["K"], st["V"], st["qbuf"], st["qcount"], st["q_recent"], st["pos_recent"],
+                        x["pos"][s].copy(), nthreads=2)
+            idx_hist.append(r["idx"])
+            sc_hist.append(r["scores"])
+            L = b.budget
+    E = len(idx_hist)
+    assert E == scfg.evictions(S) == o["n_ev"] == 4
+    assert L == o["L"]
+    assert np.array_equal(np.stack(idx_hist), o["idx"][:E])
+    assert np.array_equal(np.stack(sc_hist), o["scores"][:E])
+    for k in ("K", "V"):
+        assert np.array_equal(st[k][:, :L], o[k][:, :L]), k
+    for k in ("qbuf", "qcount", "q_recent", "pos_recent"):
+        assert np.array_equal(st[k], o[k]), k
+
+
+def test_stream_cache_invariants():
+    """Rows are identified by their (unique, random) value rows: the cache keeps
+    tokens in stream order, always holds the first n_prefix tokens, and holds
+    every token since the last eviction's recent window; keys are the rotated
+    inputs of those same tokens."""
+    scfg = TINY_STREAM
+    b = scfg.base
+    S = scfg.steps
+    x = _inputs(scfg, S)
+    o = replay(scfg, x["k_new"], x["v_new"], x["q_new"], x["pos"], max_ev=0, nthreads=4)
+    E = scfg.evictions(S)
+    assert o["n_ev"] == E == 14
+    L = o["L"]
+    last_ev = b.cap - 1 + (E - 1) * b.n_new          # step at which the last eviction ran
+    assert L == b.budget + (S - 1 - last_ev)
+    for u in range(b.units):
+        lookup = {x["v_new"][s, u].tobytes(): s for s in range(S)}
+        steps = np.array([lookup[o["V"][u, r].tobytes()] for r in range(L)])
+        assert np.all(np.diff(steps) > 0), "tokens out of order"
+        assert np.array_equal(steps[:b.n_prefix], np.arange(b.n_prefix)), "prefix evicted"
+        tail = np.arange(last_ev - b.n_recent_kv + 1, S)
+        assert np.array_equal(steps[-len(tail):], tail), "recent window or new tokens missing"
+        for r in (0, L // 2, L - 1):
+            s = steps[r]
+            assert np.array_equal(o["K"][u, r], O.rope_row(x["k_new"][s, u], b.theta, int(x["pos"][s, u])))
+        # every buffer holds a valid count; FPS leaves n_beacon after each compression
+        assert np.all((o["qcount"][u] >= 0) & (o["qcount"][u] < b.n_beacon + b.n_recent_q))
+
+
+@pytest.mark.parametrize("S", [159, 160, 161, 191, 192])
+def test_stream_eviction_boundaries(S):
+    """The eviction runs exactly when the cache reaches cap rows."""
+    scfg = TINY_STREAM
+    b = scfg.base
+    x = _inputs(scfg, S)
+    o = replay(scfg, x["k_new"], x["v_new"], x["q_new"], x["pos"], max_ev=0, nthreads=2)
+    assert o["n_ev"] == scfg.evictions(S)
+    expect_L = S if S < b.cap else b.budget + (S - b.cap) % b.n_new
+    assert o["L"] == expect_L
