@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 1
+#define BKV_ABI_VERSION 2
 
 typedef uint16_t bkv_bf16; /* raw bf16 bits */
 
@@ -98,10 +98,6 @@ const char *bkv_strerror(int code);
  * p1 when p0 = 0.  Errors: BKV_EINVAL (null, odd or non-positive head_dim,
  * p0 < 0 or p1 <= p0). */
 int bkv_rope_table(double theta, int32_t head_dim, int32_t p0, int32_t p1, float *host_out);
-
-/* Workspace bytes that bkv_evict needs for n_len when both idx_out and
- * scores_out are NULL (an upper bound otherwise).  0 on invalid input. */
-size_t bkv_workspace_bytes(const bkv_shape *shape, int32_t n_len);
 
 /* Continual FPS buffer update, one decode step (Notes §2.2 Eq. 9 and App.
  * Alg. 1; Summary, pseudocode).  For every buffer uq: append q_new[uq] at
@@ -155,17 +151,19 @@ int bkv_fps_merge(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
                   const bkv_bf16 *q_recent, int32_t *fps_sel, void *stream);
 
 /* One whole eviction (Notes §2.2 App. Alg. 2 and §2.3; Summary,
- * pseudocode): bkv_score, bkv_select, bkv_compact, then bkv_fps_merge, over
- * all units.  idx_out, scores_out and fps_sel_out are optional outputs
- * (NULL: kept in the workspace or not written).  ws must hold
- * bkv_workspace_bytes(shape, n_len) bytes (it may be NULL when both idx_out
- * and scores_out are given).  In/out: K, V, qbuf, qcount. */
+ * pseudocode) over all units: the scores of bkv_score, the keep set of
+ * bkv_select and the compaction of bkv_compact, computed per unit by one
+ * workgroup without leaving the chip in between (so the unit's keys are
+ * re-read from the on-die cache rather than from HBM), then bkv_fps_merge.
+ * idx_out ([units][budget]), scores_out ([units][n_len]) and fps_sel_out
+ * ([qbufs][n_beacon]) are optional copies of the intermediate results
+ * (NULL: not written); the results equal those of the separate calls.
+ * In/out: K, V, qbuf, qcount. */
 int bkv_evict(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t n_len,
               bkv_bf16 *qbuf, int32_t *qcount, const bkv_bf16 *q_recent,
               const int32_t *pos_recent, const int32_t *t,
               const float *rope_cs, int32_t rope_rows,
-              int32_t *idx_out, float *scores_out, int32_t *fps_sel_out,
-              void *ws, size_t ws_bytes, void *stream);
+              int32_t *idx_out, float *scores_out, int32_t *fps_sel_out, void *stream);
 
 /* One decode step of the eviction cycle (Notes §2.2 App. Alg. 2; Summary,
  * pseudocode) at cache length L: rows [0, L) of every unit are valid and

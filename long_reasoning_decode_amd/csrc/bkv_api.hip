@@ -17,8 +17,6 @@ constexpr int32_t kMaxGroup = 8;     // query heads per KV head
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
-size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
-
 int check_shape(const bkv_shape* s) {
     if (!s) return BKV_EINVAL;
     if (s->n_layers <= 0 || s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0) return BKV_EINVAL;
@@ -123,12 +121,6 @@ int bkv_rope_table(double theta, int32_t head_dim, int32_t p0, int32_t p1, float
     return BKV_OK;
 }
 
-size_t bkv_workspace_bytes(const bkv_shape* s, int32_t n_len) {
-    if (check_shape(s) != BKV_OK || n_len <= 0) return 0;
-    const size_t units = (size_t)units_of(s);
-    return round256(units * (size_t)n_len * 4) + round256(units * (size_t)(s->budget > 0 ? s->budget : 1) * 4);
-}
-
 int bkv_fps_update(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const bkv_bf16* q_new,
                    int32_t* fps_sel, void* stream) {
     int e = check_shape(s);
@@ -216,8 +208,7 @@ int bkv_compact(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, con
 
 int bkv_evict(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, bkv_bf16* qbuf, int32_t* qcount,
               const bkv_bf16* q_recent, const int32_t* pos_recent, const int32_t* t, const float* rope_cs,
-              int32_t rope_rows, int32_t* idx_out, float* scores_out, int32_t* fps_sel_out, void* ws,
-              size_t ws_bytes, void* stream) {
+              int32_t rope_rows, int32_t* idx_out, float* scores_out, int32_t* fps_sel_out, void* stream) {
     int e = check_shape(s);
     if (e) return e;
     if ((e = check_len(s, n_len))) return e;
@@ -227,43 +218,17 @@ int bkv_evict(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, bkv_b
     if ((idx_out && !aligned4(idx_out)) || (scores_out && !aligned4(scores_out)) ||
         (fps_sel_out && !aligned4(fps_sel_out)))
         return BKV_EINVAL;
-    const size_t units = (size_t)units_of(s);
-    const size_t sc_bytes = round256(units * (size_t)n_len * 4);
-    size_t need = 0;
-    if (!scores_out) need += sc_bytes;
-    if (!idx_out) need += round256(units * (size_t)(s->budget > 0 ? s->budget : 1) * 4);
-    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return BKV_EINVAL;
-    unsigned char* w = (unsigned char*)ws;
-    float* scores = scores_out;
-    if (!scores) {
-        scores = (float*)w;
-        w += sc_bytes;
-    }
-    int32_t* idx = idx_out ? idx_out : (int32_t*)w;
     hipStream_t st = (hipStream_t)stream;
 
-    bkv::ScoreArgs sa = score_args(s, K, n_len, qbuf, qcount, q_recent, pos_recent, t, rope_cs, rope_rows, scores);
-    if ((e = hip_status(bkv::launch_score(sa, s->head_dim, st)))) return e;
-
-    bkv::SelectArgs la;
-    la.scores = scores;
-    la.idx = idx;
-    la.units = (int)units;
-    la.n_len = n_len;
-    la.budget = s->budget;
-    la.n_prefix = s->n_prefix;
-    la.n_recent_kv = s->n_recent_kv;
-    if ((e = hip_status(bkv::launch_select(la, st)))) return e;
-
-    bkv::CompactArgs ca;
-    ca.K = K;
-    ca.V = V;
-    ca.idx = idx;
-    ca.units = (int)units;
-    ca.n_len = n_len;
-    ca.cap = s->cap;
-    ca.budget = s->budget;
-    if ((e = hip_status(bkv::launch_compact(ca, s->head_dim, st)))) return e;
+    bkv::EvictArgs ea;
+    ea.sc = score_args(s, K, n_len, qbuf, qcount, q_recent, pos_recent, t, rope_cs, rope_rows, scores_out);
+    ea.K = K;
+    ea.V = V;
+    ea.idx = idx_out;
+    ea.budget = s->budget;
+    ea.n_prefix = s->n_prefix;
+    ea.n_recent_kv = s->n_recent_kv;
+    if ((e = hip_status(bkv::launch_evict(ea, s->head_dim, st)))) return e;
 
     bkv::FpsArgs fa;
     fa.qbuf = qbuf;

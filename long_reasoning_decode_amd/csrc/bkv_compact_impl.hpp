@@ -91,5 +91,54 @@ __device__ void move_rows(bkv_bf16* X, const uint16_t* src, int first, int B, in
     }
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Move rows [first, B) of X by NW waves of one workgroup (w = this wave's
+// index among them), in windows of NW chunks: wave w moves chunk w of each
+// window.  Every wave's loads of a window complete before any of the window's
+// stores (a wait and a barrier), so no source row is overwritten before it
+// is read.  A window's stores and the next window's loads touch disjoint
+// rows -- the next window's sources lie at or after its destinations, which
+// follow this window's -- so the next loads are issued before this window's
+// stores.  All NW waves, and any other waves of the workgroup, must call it
+// with the same first and B (they meet the same barriers).
+template <int D, int NW>
+__device__ void move_rows_wg(bkv_bf16* X, const uint16_t* src, int first, int B, int w, int lane) {
+    if (first >= B) return;
+    constexpr int kWin = NW * kChunkRows;
+    constexpr int kPer = Chunk<D>::kPer;
+    Chunk<D> c0, c1;
+    int a = first;
+    load_chunk<D>(c0, X, src, a + w * kChunkRows, B, lane);
+    wait_vm<0>();
+    wg_barrier();
+    while (true) {
+        const int n1 = a + kWin;
+        if (n1 < B) load_chunk<D>(c1, X, src, n1 + w * kChunkRows, B, lane);
+        store_chunk<D>(c0, X, a + w * kChunkRows, B, lane);
+        if (n1 >= B) break;
+        wait_vm<kPer>();   // the window's loads (issued before the kPer stores) are done
+        wg_barrier();
+        const int n2 = n1 + kWin;
+        if (n2 < B) load_chunk<D>(c0, X, src, n2 + w * kChunkRows, B, lane);
+        store_chunk<D>(c1, X, n1 + w * kChunkRows, B, lane);
+        if (n2 >= B) break;
+        wait_vm<kPer>();
+        wg_barrier();
+        a = n2;
+    }
+}
+
 }  // namespace compact
 }  // namespace bkv

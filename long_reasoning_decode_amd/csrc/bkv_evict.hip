@@ -1,0 +1,89 @@
+// bkv_evict.hip -- the eviction of one unit by one 16-wave workgroup (Notes
+// §2.3, Eq. 7-8): its scores (bkv_score_impl.hpp), its keep set by an LDS
+// radix select over them (bkv_select_impl.hpp), and the in-place compaction
+// of its K and V rows (bkv_compact_impl.hpp), with nothing but the optional
+// outputs leaving the chip in between.  Doing all three in one workgroup
+// keeps the unit's keys in the MALL from the first scoring pass to the
+// compaction, so only the first pass and the value rows are read from HBM.
+// The merge of the query buffers runs as its own launch afterwards.
+#include "bkv_compact_impl.hpp"
+#include "bkv_score_impl.hpp"
+#include "bkv_select_impl.hpp"
+
+namespace bkv {
+
+namespace {
+
+// Select scratch and kept slots, placed in the key ring once scoring is done.
+constexpr int kHistOff = 0;        // uint32 [256]
+constexpr int kWsumOff = 1024;     // int [16]
+constexpr int kBinOff = 1280;      // uint32 [2]
+constexpr int kFirstOff = 1296;    // int
+constexpr int kSrcOff = 2048;      // uint16 [budget]
+
+template <int D, int KS>
+__global__ __launch_bounds__(score::kThreads) void evict_kernel(EvictArgs a) {
+    using L = score::Layout<D>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint32_t* codes = reinterpret_cast<uint32_t*>(smem + L::kFixed);
+    const int u = blockIdx.x;
+    if (u >= a.sc.units) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int N = a.sc.n_len;
+
+    // scores, then the order codes of the fp32 scores, which the select ranks
+    score::unit_codes<D, KS>(a.sc, u, smem, codes);
+    float* sc_out = a.sc.scores ? a.sc.scores + (size_t)u * N : nullptr;
+    for (int j = tid; j < N; j += score::kThreads) {
+        const float s = __builtin_amdgcn_exp2f(f32_unorder(codes[j]));
+        if (sc_out) sc_out[j] = s;
+        codes[j] = f32_order(s);
+    }
+    __syncthreads();
+
+    // keep set (kept slots ascending in LDS, and optionally in global memory)
+    const int B = a.budget;
+    uint16_t* src = reinterpret_cast<uint16_t*>(smem + kSrcOff);
+    sel::Scratch w{codes, reinterpret_cast<uint32_t*>(smem + kHistOff), reinterpret_cast<int*>(smem + kWsumOff),
+                   reinterpret_cast<uint32_t*>(smem + kBinOff)};
+    sel::select_staged<score::kThreads>(N, B, a.n_prefix, a.n_recent_kv, a.idx ? a.idx + (size_t)u * B : nullptr,
+                                        src, w);
+
+    // in-place compaction: waves 0-7 move K rows, waves 8-15 V rows
+    const int Bv = N < B ? N : B;
+    int* first_sh = reinterpret_cast<int*>(smem + kFirstOff);
+    if (wave == 0) {
+        const int f = compact::first_moved(src, Bv, lane);
+        if (lane == 0) *first_sh = f;
+    }
+    __syncthreads();
+    const int first = *first_sh;
+    bkv_bf16* X = (wave < 8 ? a.K : a.V) + (size_t)u * a.sc.cap * D;
+    compact::move_rows_wg<D, 8>(X, src, first, Bv, wave & 7, lane);
+}
+
+template <int D, int KS>
+hipError_t launch_one(const EvictArgs& a, hipStream_t st) {
+    using L = score::Layout<D>;
+    static_assert(kSrcOff + 2 * 8192 <= L::kRingBytes, "select scratch fits in the key ring");
+    const size_t smem = L::kFixed + (size_t)a.sc.n_len * 4;
+    hipLaunchKernelGGL((evict_kernel<D, KS>), dim3(a.sc.units), dim3(score::kThreads), smem, st, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const EvictArgs& a, hipStream_t st) {
+    if (a.sc.G <= 1) return launch_one<D, 16>(a, st);
+    if (a.sc.G <= 2) return launch_one<D, 8>(a, st);
+    if (a.sc.G <= 4) return launch_one<D, 4>(a, st);
+    return launch_one<D, 2>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_evict(const EvictArgs& a, int d, hipStream_t st) {
+    if (a.sc.units <= 0 || a.sc.n_len <= 0) return hipSuccess;
+    return d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+}  // namespace bkv

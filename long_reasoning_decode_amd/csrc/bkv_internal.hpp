@@ -42,6 +42,14 @@ struct CompactArgs {
     int units, n_len, cap, budget;
 };
 
+struct EvictArgs {
+    ScoreArgs sc;              // scoring inputs (sc.scores: optional copy of the scores, may be null)
+    bkv_bf16* K;               // [units][cap][d], in place
+    bkv_bf16* V;
+    int32_t* idx;              // [units][budget], optional copy of the keep set (may be null)
+    int budget, n_prefix, n_recent_kv;
+};
+
 struct AppendArgs {
     bkv_bf16* K;               // [units][cap][d]
     bkv_bf16* V;
@@ -65,6 +73,7 @@ hipError_t launch_score(const ScoreArgs& a, int d, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 hipError_t launch_compact(const CompactArgs& a, int d, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int d, hipStream_t st);
+hipError_t launch_evict(const EvictArgs& a, int d, hipStream_t st);
 hipError_t launch_ring(const RingArgs& a, int d, hipStream_t st);
 
 }  // namespace bkv

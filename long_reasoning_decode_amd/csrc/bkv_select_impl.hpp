@@ -48,11 +48,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total
     return base + x - v;
 }
 
-// Kept slots of one unit: idx (global, [B], -1 padded; may be null) and
-// src (LDS, [min(N, B)] as uint16; may be null).  All BLOCK threads call it.
+// Kept slots of one unit from its score codes w.keys[0..N) (f32_order of the
+// scores, already in LDS and visible to the workgroup): idx (global, [B], -1
+// padded; may be null) and src (LDS, [min(N, B)] as uint16; may be null).
+// All BLOCK threads call it.
 template <int BLOCK>
-__device__ void select_unit(const float* sc, int N, int B, int n_prefix, int n_recent_kv, int32_t* idx,
-                            uint16_t* src, const Scratch& w) {
+__device__ void select_staged(int N, int B, int n_prefix, int n_recent_kv, int32_t* idx, uint16_t* src,
+                              const Scratch& w) {
     const int tid = threadIdx.x;
     if (N <= B) {
         for (int r = tid; r < B; r += BLOCK) {
@@ -65,8 +67,6 @@ __device__ void select_unit(const float* sc, int N, int B, int n_prefix, int n_r
     const int np = n_prefix < N ? n_prefix : N;
     const int rs = N - n_recent_kv > 0 ? N - n_recent_kv : 0;
     const int k_sel = B - np - (N - rs);   // >= 0: checked on the host
-    for (int j = tid; j < N; j += BLOCK) w.keys[j] = f32_order(sc[j]);
-    __syncthreads();
 
     // ---- radix select of the k_sel-th largest candidate code
     uint32_t prefix = 0, pmask = 0;
@@ -160,6 +160,17 @@ __device__ void select_unit(const float* sc, int N, int B, int n_prefix, int n_r
         }
     }
     __syncthreads();
+}
+
+// As select_staged, with the scores read from global memory first.
+template <int BLOCK>
+__device__ void select_unit(const float* sc, int N, int B, int n_prefix, int n_recent_kv, int32_t* idx,
+                            uint16_t* src, const Scratch& w) {
+    if (N > B) {
+        for (int j = threadIdx.x; j < N; j += BLOCK) w.keys[j] = f32_order(sc[j]);
+        __syncthreads();
+    }
+    select_staged<BLOCK>(N, B, n_prefix, n_recent_kv, idx, src, w);
 }
 
 }  // namespace sel

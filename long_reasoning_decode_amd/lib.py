@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libbkv.so")
 BKV_CAUSAL_RECENT = 1
 ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE", -4: "BKV_EHIP"}
 
-EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_workspace_bytes", "bkv_fps_update",
+EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_fps_update",
            "bkv_fps_merge", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict", "bkv_decode_step")
 
 
@@ -56,16 +56,14 @@ def load():
         L.bkv_strerror.argtypes = [C.c_int]
         L.bkv_strerror.restype = C.c_char_p
         L.bkv_rope_table.argtypes = [C.c_double, i32, i32, i32, P]
-        L.bkv_workspace_bytes.argtypes = [SP, i32]
-        L.bkv_workspace_bytes.restype = C.c_size_t
         L.bkv_fps_update.argtypes = [SP, P, P, P, P, st]
         L.bkv_fps_merge.argtypes = [SP, P, P, P, P, st]
         L.bkv_score.argtypes = [SP, P, i32, P, P, P, P, P, P, i32, P, st]
         L.bkv_select.argtypes = [SP, P, i32, P, st]
         L.bkv_compact.argtypes = [SP, P, P, i32, P, st]
-        L.bkv_evict.argtypes = [SP, P, P, i32, P, P, P, P, P, P, i32, P, P, P, P, C.c_size_t, st]
+        L.bkv_evict.argtypes = [SP, P, P, i32, P, P, P, P, P, P, i32, P, P, P, st]
         L.bkv_decode_step.argtypes = [SP, P, P, i32, P, P, P, P, P, P, P, P, P, i32, P, st]
-        for f in EXPORTS[4:]:
+        for f in EXPORTS[3:]:
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -120,10 +118,6 @@ def rope_table(theta: float, head_dim: int, p0: int, p1: int) -> np.ndarray:
     return out
 
 
-def workspace_bytes(shape: Shape, n_len: int) -> int:
-    return int(load().bkv_workspace_bytes(C.byref(shape), int(n_len)))
-
-
 def fps_update(shape: Shape, qbuf, qcount, q_new, fps_sel=None, stream=None) -> None:
     _check(load().bkv_fps_update(C.byref(shape), _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"),
                                  _ptr(q_new, bf16, "q_new"), _ptr(fps_sel, i32, "fps_sel"), _stream(stream)),
@@ -156,17 +150,12 @@ def compact(shape: Shape, K, V, n_len: int, idx, stream=None) -> None:
 
 
 def evict(shape: Shape, K, V, n_len: int, qbuf, qcount, q_recent, pos_recent, t, rope_cs,
-          idx_out=None, scores_out=None, fps_sel_out=None, ws=None, stream=None) -> None:
-    if ws is None and (idx_out is None or scores_out is None):
-        ws = torch.empty(workspace_bytes(shape, n_len), dtype=torch.uint8, device=K.device)
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+          idx_out=None, scores_out=None, fps_sel_out=None, stream=None) -> None:
     _check(load().bkv_evict(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(n_len),
                             _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(q_recent, bf16, "q_recent"),
                             _ptr(pos_recent, i32, "pos_recent"), _ptr(t, i32, "t"), _ptr(rope_cs, f32, "rope_cs"),
                             int(rope_cs.shape[0]), _ptr(idx_out, i32, "idx_out"), _ptr(scores_out, f32, "scores_out"),
-                            _ptr(fps_sel_out, i32, "fps_sel_out"),
-                            None if ws is None else C.c_void_p(ws.data_ptr()), C.c_size_t(ws_bytes),
-                            _stream(stream)), "bkv_evict")
+                            _ptr(fps_sel_out, i32, "fps_sel_out"), _stream(stream)), "bkv_evict")
 
 
 def decode_step(shape: Shape, K, V, L: int, k_new, v_new, pos, qbuf, qcount, q_new, q_recent, pos_recent,

@@ -44,7 +44,6 @@ class StreamRun:
         self.rope = torch.from_numpy(lib.rope_table(b.theta, d, 0, scfg.rope_rows)).to(dev)
         self.idx = torch.empty(b.units, b.budget, dtype=torch.int32, device=dev)
         self.scores = torch.empty(b.units, b.cap, dtype=torch.float32, device=dev)
-        self.ws = torch.empty(max(lib.workspace_bytes(self.shape, b.cap), 256), dtype=torch.uint8, device=dev)
         self.gen = synth.StreamGen(scfg, dev, seed)
         self.block_steps = block
         self.pool = self.gen.alloc(block)
@@ -58,9 +57,9 @@ class StreamRun:
             self.rec = {k: [] for k in ("q_new", "k_new", "v_new", "pos", "idx", "scores")}
 
     def state_bytes(self) -> int:
-        """HBM held by the eviction manager's own state (cache, buffers, ring, table, workspace)."""
+        """HBM held by the eviction manager's own state (cache, buffers, ring, table, keep-set and score copies)."""
         ts = (self.K, self.V, self.qbuf, self.qcount, self.q_recent, self.pos_recent, self.rope, self.idx,
-              self.scores, self.ws)
+              self.scores)
         return sum(t.numel() * t.element_size() for t in ts)
 
     def _record_inputs(self, blk: dict, n: int) -> None:
@@ -97,7 +96,7 @@ class StreamRun:
                 if self.L == b.cap:
                     lib.evict(self.shape, self.K, self.V, b.cap, self.qbuf, self.qcount, self.q_recent,
                               self.pos_recent, blk["pos"][i], self.rope, idx_out=self.idx, scores_out=self.scores,
-                              ws=self.ws, stream=stream)
+                              stream=stream)
                     if self.rec is not None:
                         self.rec["idx"].append(self.idx.index_select(0, self.rec_units))
                         self.rec["scores"].append(self.scores.index_select(0, self.rec_units))

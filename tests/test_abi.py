@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strerror(so):
-    assert L.version() == 1
+    assert L.version() == 2
     for code in (0, -1, -2, -3, -4):
         assert len(L.strerror(code)) > 0
     assert L.strerror(-99) == "unknown error"
@@ -90,7 +90,8 @@ MISALIGNED = C.c_void_p(0x10002)
 def test_shape_validation(so, field, value, code):
     s = _shape(**{field: value})
     assert so.bkv_fps_update(C.byref(s), FAKE, FAKE, FAKE, None, None) == code
-    assert so.bkv_workspace_bytes(C.byref(s), 100) == 0
+    assert so.bkv_evict(C.byref(s), FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
+                        None, None, None, None) == code
 
 
 def test_pointer_and_range_validation(so):
@@ -110,20 +111,13 @@ def test_pointer_and_range_validation(so):
     # score: table rows must be positive; recent queries need their arrays
     assert so.bkv_score(C.byref(s), FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == -3
     assert so.bkv_score(C.byref(s), FAKE, 100, FAKE, FAKE, None, FAKE, FAKE, FAKE, 10, FAKE, None) == -1
-    # evict without workspace or outputs
+    # evict: missing V, misaligned optional outputs, keep set larger than the budget allows
+    assert so.bkv_evict(C.byref(s), FAKE, None, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
+                        None, None, None, None) == -1
     assert so.bkv_evict(C.byref(s), FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
-                        None, None, None, None, 0, None) == -1
-    need = so.bkv_workspace_bytes(C.byref(s), 100)
-    assert so.bkv_evict(C.byref(s), FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
-                        None, None, None, FAKE, need - 1, None) == -1
-
-
-def test_workspace_bytes_monotone(so):
-    s = L.shape_of(QWEN3_4B)
-    a = so.bkv_workspace_bytes(C.byref(s), 1000)
-    b = so.bkv_workspace_bytes(C.byref(s), 2176)
-    assert 0 < a < b
-    assert b >= QWEN3_4B.units * (2176 + QWEN3_4B.budget) * 4
+                        MISALIGNED, None, None, None) == -1
+    assert so.bkv_evict(C.byref(tight), FAKE, FAKE, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10,
+                        None, None, None, None) == -3
 
 
 def test_all_configs_are_supported_shapes():
