@@ -1,4 +1,4 @@
-// bkv_evict.hip -- the eviction of one unit by one 16-wave workgroup (Notes
+// bkv_evict.hip -- the eviction of one unit by one 8-wave workgroup (Notes
 // §2.3, Eq. 7-8): its scores (bkv_score_impl.hpp), its keep set by an LDS
 // radix select over them (bkv_select_impl.hpp), and the in-place compaction
 // of its K and V rows (bkv_compact_impl.hpp), with nothing but the optional
@@ -16,7 +16,7 @@ namespace {
 
 // Select scratch and kept slots, placed in the key ring once scoring is done.
 constexpr int kHistOff = 0;        // uint32 [256]
-constexpr int kWsumOff = 1024;     // int [16]
+constexpr int kWsumOff = 1024;     // int [waves]
 constexpr int kBinOff = 1280;      // uint32 [2]
 constexpr int kFirstOff = 1296;    // int
 constexpr int kSrcOff = 2048;      // uint16 [budget]
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(score::kThreads) void evict_kernel(EvictArgs a) {
     sel::select_staged<score::kThreads>(N, B, a.n_prefix, a.n_recent_kv, a.idx ? a.idx + (size_t)u * B : nullptr,
                                         src, w);
 
-    // in-place compaction: waves 0-7 move K rows, waves 8-15 V rows
+    // in-place compaction: the first half of the waves move K rows, the second half V rows
     const int Bv = N < B ? N : B;
     int* first_sh = reinterpret_cast<int*>(smem + kFirstOff);
     if (wave == 0) {
@@ -58,8 +58,9 @@ __global__ __launch_bounds__(score::kThreads) void evict_kernel(EvictArgs a) {
     }
     __syncthreads();
     const int first = *first_sh;
-    bkv_bf16* X = (wave < 8 ? a.K : a.V) + (size_t)u * a.sc.cap * D;
-    compact::move_rows_wg<D, 8>(X, src, first, Bv, wave & 7, lane);
+    constexpr int kHalf = score::kWaves / 2;
+    bkv_bf16* X = (wave < kHalf ? a.K : a.V) + (size_t)u * a.sc.cap * D;
+    compact::move_rows_wg<D, kHalf>(X, src, first, Bv, wave % kHalf, lane);
 }
 
 template <int D, int KS>
@@ -73,10 +74,12 @@ hipError_t launch_one(const EvictArgs& a, hipStream_t st) {
 
 template <int D>
 hipError_t launch_d(const EvictArgs& a, hipStream_t st) {
-    if (a.sc.G <= 1) return launch_one<D, 16>(a, st);
-    if (a.sc.G <= 2) return launch_one<D, 8>(a, st);
-    if (a.sc.G <= 4) return launch_one<D, 4>(a, st);
-    return launch_one<D, 2>(a, st);
+    // query heads per workgroup: the smallest power of two >= G; key split KS = waves / heads
+    constexpr int W = score::kWaves;
+    if (a.sc.G <= 1) return launch_one<D, W>(a, st);
+    if (a.sc.G <= 2) return launch_one<D, W / 2>(a, st);
+    if (a.sc.G <= 4) return launch_one<D, W / 4>(a, st);
+    return launch_one<D, 1>(a, st);
 }
 
 }  // namespace

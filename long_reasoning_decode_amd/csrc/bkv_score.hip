@@ -1,4 +1,4 @@
-// bkv_score.hip -- scoring kernel: one 16-wave workgroup per unit (the work
+// bkv_score.hip -- scoring kernel: one 8-wave workgroup per unit (the work
 // is in bkv_score_impl.hpp), scores written as exp2 of the per-key codes.
 #include "bkv_score_impl.hpp"
 
@@ -27,10 +27,12 @@ hipError_t launch_one(const ScoreArgs& a, hipStream_t st) {
 
 template <int D>
 hipError_t launch_d(const ScoreArgs& a, hipStream_t st) {
-    if (a.G <= 1) return launch_one<D, 16>(a, st);
-    if (a.G <= 2) return launch_one<D, 8>(a, st);
-    if (a.G <= 4) return launch_one<D, 4>(a, st);
-    return launch_one<D, 2>(a, st);
+    // query heads per workgroup: the smallest power of two >= G; key split KS = waves / heads
+    constexpr int W = score::kWaves;
+    if (a.G <= 1) return launch_one<D, W>(a, st);
+    if (a.G <= 2) return launch_one<D, W / 2>(a, st);
+    if (a.G <= 4) return launch_one<D, W / 4>(a, st);
+    return launch_one<D, 1>(a, st);
 }
 
 }  // namespace

@@ -1,4 +1,4 @@
-// bkv_score_impl.hpp -- scores of one unit's keys by one 16-wave workgroup
+// bkv_score_impl.hpp -- scores of one unit's keys by one 8-wave workgroup
 // (device functions of the scoring kernel and of the fused eviction kernel).
 //
 // Scores (Notes §2.1 Eq. 4-5, §2.3 Eq. 7):
@@ -11,7 +11,7 @@
 //
 // Waves: head = wave / KS owns one query head's 32 rows (inactive when
 // head >= G), ks = wave % KS takes the key tiles j = ks (mod KS).  The unit's
-// keys stream twice through a 3-stage LDS ring of 4-tile (128-key) stages,
+// keys stream twice through a 3-stage LDS ring of 2-tile (64-key) stages,
 // filled by the gfx950 LDS-DMA load (global_load_lds_dwordx4) two stages ahead,
 // in an XOR-swizzled layout: each DMA instruction reads whole key rows
 // (coalesced) and the MFMA operand reads hit distinct banks.
@@ -20,9 +20,10 @@
 //           row are merged in LDS into c_r;
 //   pass 2: D[row][key] = Q K^T; max over the wave's rows of z - c per key,
 //           then over the heads with LDS atomics.
-// One unit per workgroup and one workgroup per CU keep about 256 units in
-// flight (about 143 MB at 2176 keys of d = 128), which the MALL holds: the
-// second pass reads mostly from it rather than from HBM.
+// One unit per 8-wave workgroup and two workgroups per CU keep about 512
+// units in flight (about 285 MB at 2176 keys of d = 128), so a unit's keys
+// are still in the MALL when the second pass (and the compaction of the
+// fused eviction kernel) reads them again.
 //
 // Because the DMA bypasses registers, the compiler does not track it: the
 // loops wait on vmcnt explicitly (this wave's DMA for the current stage) and
@@ -43,9 +44,9 @@ namespace bkv {
 namespace score {
 
 constexpr int kTileKeys = 32;
-constexpr int kStageTiles = 4;                  // tiles per ring stage
+constexpr int kStageTiles = 2;                  // tiles per ring stage
 constexpr int kStages = 3;                      // two stages in flight while one is consumed
-constexpr int kWaves = 16;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 template <int D>
@@ -57,7 +58,7 @@ struct Layout {
     static constexpr int kDmaPerWave = kStageTiles * kDmaPerTile / kWaves;
     static constexpr int kRingBytes = kStages * kStageBytes;
     static constexpr int kCrowOff = kRingBytes;                       // float [8 heads][32 rows]
-    static constexpr int kPartOff = kCrowOff + 8 * 32 * 4;            // float2 [16 waves][32 rows]
+    static constexpr int kPartOff = kCrowOff + 8 * 32 * 4;            // float2 [waves][32 rows]
     static constexpr int kFixed = kPartOff + kWaves * 32 * 8;         // then uint32 per-key codes [n_len]
     static_assert((kStageTiles * kDmaPerTile) % kWaves == 0, "stage DMA split");
 };
@@ -196,7 +197,7 @@ __device__ __forceinline__ void dma_stage(const bkv_bf16* Ku, int st, int n_len,
 }
 
 // Per-key codes f32_order(max over rows of z - c) of unit u (base 2) into
-// codes[0 .. n_len) in LDS.  All 16 waves call it; on return the codes are
+// codes[0 .. n_len) in LDS.  All waves call it; on return the codes are
 // complete and visible to the workgroup, and this wave has no memory
 // operation in flight.
 template <int D, int KS>
@@ -234,6 +235,8 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
         for (int s = 0; s < kS; ++s) qop[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
     }
     const int vis = ri.valid ? ri.vis : -1;
+    // every valid row sees keys [0, vis_floor]; rows that are not valid get c = +inf
+    const int vis_floor = (a.causal && a.n_recent_q > 0) ? n_len - a.n_recent_q : n_len - 1;
     for (int j = tid; j < n_len; j += kThreads) codes[j] = f32_order(-__builtin_inff());
 
     // ---- pass 1: per-row online (max, sum), base 2
@@ -255,10 +258,15 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
             for (int s = 0; s < kS; ++s)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<D>(tl, r, s, half), qop[s], acc, 0, 0, 0);
             float z[16];
+            if (key0 + kTileKeys - 1 > vis_floor) {   // tile reaches a causal limit or the cache end
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int key = key0 + 8 * (q >> 2) + 4 * half + (q & 3);
-                z[q] = (key > vis || key >= n_len) ? -__builtin_inff() : acc[q];
+                for (int q = 0; q < 16; ++q) {
+                    const int key = key0 + 8 * (q >> 2) + 4 * half + (q & 3);
+                    z[q] = (key > vis || key >= n_len) ? -__builtin_inff() : acc[q];
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) z[q] = acc[q];
             }
             // common case: every term relative to the running max stays below 2^32
             float sum = 0.0f;
@@ -305,7 +313,7 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
             M = Mn;
         }
         float c = __builtin_inff();
-        if (M != -__builtin_inff() && Ls > 0.0f) c = M + __builtin_log2f(Ls);
+        if (ri.valid && M != -__builtin_inff() && Ls > 0.0f) c = M + __builtin_log2f(Ls);
         crow[head * 32 + r] = c;
     }
     lds_barrier();   // c_r published
@@ -331,11 +339,16 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
             for (int s = 0; s < kS; ++s)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], k_operand<D>(tl, r, s, half), acc, 0, 0, 0);
             float cm = -__builtin_inff();
+            if (j * kTileKeys + kTileKeys - 1 > vis_floor) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                float tv = __builtin_fmaf(acc[q], sc2, -cq[q]);
-                if (key > row_vis(a, 8 * (q >> 2) + 4 * half + (q & 3))) tv = -__builtin_inff();
-                cm = __builtin_fmaxf(cm, tv);
+                for (int q = 0; q < 16; ++q) {
+                    float tv = __builtin_fmaf(acc[q], sc2, -cq[q]);
+                    if (key > row_vis(a, 8 * (q >> 2) + 4 * half + (q & 3))) tv = -__builtin_inff();
+                    cm = __builtin_fmaxf(cm, tv);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) cm = __builtin_fmaxf(cm, __builtin_fmaf(acc[q], sc2, -cq[q]));
             }
             cm = __builtin_fmaxf(cm, __shfl_xor(cm, 32, 64));
             if (half == 0 && key < n_len) atomicMax(&codes[key], f32_order(cm));
