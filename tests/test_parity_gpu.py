@@ -145,6 +145,9 @@ SCORE_CASES = [
     (TINY.scaled(hq=6, hkv=2, name="g3"), 159, 1),
     (TINY.scaled(hq=6, hkv=1, name="g6"), 140, 1),
     (TINY.scaled(d=128, hq=5, hkv=1, name="g5d128"), 160, 1),
+    (TINY.scaled(n_recent_q=0, name="nrq0"), 160, 1),
+    (TINY.scaled(n_beacon=0, name="nb0"), 160, 1),
+    (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 1),
 ]
 
 
@@ -248,6 +251,18 @@ EVICT_CASES = [
     (QWEN3_14B_1K.scaled(n_layers=1, batch=2), None, 1),
     (QWEN3_14B_4K.scaled(n_layers=1, batch=1), None, 1),
     (TINY.scaled(hq=8, hkv=1, name="g8"), 150, 1),
+    # every workgroup layout of the fused kernel (query heads per unit 1, 2, 3-4, 5-8) and both head sizes
+    (TINY.scaled(hq=3, hkv=3, name="g1"), 160, 1),
+    (TINY.scaled(hq=3, hkv=3, name="g1"), 33, 1),          # one partial stage, nothing to evict
+    (TINY.scaled(hq=6, hkv=2, name="g3"), 159, 1),
+    (TINY.scaled(hq=6, hkv=1, name="g6"), 140, 0),
+    (TINY.scaled(d=128, hq=5, hkv=1, name="g5d128"), 160, 1),
+    (TINY.scaled(d=128, hq=2, hkv=2, name="g1d128"), 97, 1),
+    # no recent queries; no beacons
+    (TINY.scaled(n_recent_q=0, name="nrq0"), 160, 1),
+    (TINY.scaled(n_beacon=0, name="nb0"), 160, 1),
+    # the longest cache the kernels take (8192 keys)
+    (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 1),
 ]
 
 
