@@ -171,8 +171,12 @@ def stream_bench(args) -> int:
     torch.cuda.reset_peak_memory_stats()
     prog = lambda r: (r.steps_done % 4096 == 0) and print(f"# step {r.steps_done}, evictions {r.n_ev}",
                                                             file=sys.stderr, flush=True)
-    r = run.run(steps, timed=True, progress=prog)
+    n_blocks = (steps + run.block_steps - 1) // run.block_steps
+    detail = sorted({n_blocks // 4, n_blocks // 2, (3 * n_blocks) // 4})
+    r = run.run(steps, timed=True, progress=prog, detail_blocks=detail)
     tokens = b.batch * steps
+    pct = lambda v, q: float(np.percentile(v, q)) if len(v) else None
+    rounds = run.fps_rounds_per_buffer(steps)
     out = {
         "metric": "streaming decode: tokens/s through the eviction manager (decode-step bookkeeping + evictions)",
         "value": tokens / (r["gpu_ms"] * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
@@ -182,6 +186,13 @@ def stream_bench(args) -> int:
                                f"budget {b.budget}, evict every {b.n_new} steps",
                    "evictions": r["evictions"]},
         "gpu_s": r["gpu_ms"] * 1e-3, "wall_s_with_generation": r["wall_s"],
+        "eviction_ms": {"mean": float(np.mean(r["evict_ms"])) if r["evict_ms"] else None,
+                        "p50": pct(r["evict_ms"], 50), "p99": pct(r["evict_ms"], 99),
+                        "max": max(r["evict_ms"]) if r["evict_ms"] else None},
+        "decode_step_us": {"sampled_steps": len(r["step_ms"]), "mean": float(np.mean(r["step_ms"])) * 1e3,
+                           "p50": pct(r["step_ms"], 50) * 1e3, "p99": pct(r["step_ms"], 99) * 1e3,
+                           "max": max(r["step_ms"]) * 1e3},
+        "fps_rounds": {"per_buffer": rounds, "total": rounds * b.qbufs},
         "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
     }
     print(json.dumps(out), flush=True)

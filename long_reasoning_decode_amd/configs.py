@@ -116,4 +116,11 @@ class StreamConfig:
 STREAM = StreamConfig()
 TINY_STREAM = StreamConfig(name="stream-tiny", base=replace(TINY, batch=2, seed=20261202 + 510),
                            steps=600, drift_every=256, p0_max=1000)
-STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM)}
+# the most beacon-heavy split of the recent/beacon ablation (1 recent + 31 beacons): the buffer is full after
+# every step, so every collection step runs a sampling round
+STREAM_1R31B = StreamConfig(name="stream-qwen3-4b-1r31b",
+                            base=replace(QWEN3_4B, batch=192, n_beacon=31, n_recent_q=1, seed=20261202 + 520))
+TINY_STREAM_1R31B = StreamConfig(name="stream-tiny-1r31b",
+                                 base=replace(TINY, batch=2, n_beacon=31, n_recent_q=1, seed=20261202 + 530),
+                                 steps=400, drift_every=256, p0_max=1000)
+STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM, STREAM_1R31B, TINY_STREAM_1R31B)}

@@ -190,33 +190,28 @@ __device__ void write_rows(uint32_t mask, const bkv_bf16* src0, int n0, const bk
     }
 }
 
-// Continual FPS buffer update of buffer b (Notes §2.2, Eq. 9).
+// Sampling round of the continual FPS buffer update for buffer b (Notes §2.2,
+// Eq. 9), after the step's query has been appended: a buffer whose count has
+// reached B_Q^max becomes FPS(buffer, n_beacon), survivors in ascending slot
+// order, count n_beacon; other buffers are left as they are.
 template <int D>
-__device__ void update_one(const FpsArgs& a, int b, Smem& s, int lane) {
+__device__ void compress_one(const FpsArgs& a, int b, Smem& s, int lane) {
     const int bqmax = a.n_beacon + a.n_recent_q;
-    bkv_bf16* buf = a.qbuf + (size_t)b * a.qcap * D;
-    const bkv_bf16* qn = a.q_new + (size_t)b * D;
-    const int c = clampi(a.qcount[b], 0, bqmax - 1);
-    const int n = c + 1;
     const int m = a.n_beacon;
-    if (n < bqmax) {  // append only
-        for (int kc = lane; kc < D / 8; kc += kWave)
-            *reinterpret_cast<u32x4_t*>(buf + (size_t)c * D + kc * 8) =
-                *reinterpret_cast<const u32x4_t*>(qn + kc * 8);
-        if (lane == 0) a.qcount[b] = n;
+    bkv_bf16* buf = a.qbuf + (size_t)b * a.qcap * D;
+    const int n = a.qcount[b];
+    if (n != bqmax) {
         if (a.fps_sel)
             for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)b * m + i] = -1;
         return;
     }
     if (n <= m) {  // no sampling: keep all rows (only when n_recent_q == 0)
-        write_rows<D>(n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u), buf, c, qn, buf, lane);
-        if (lane == 0) a.qcount[b] = n;
         if (a.fps_sel)
             for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)b * m + i] = i < n ? i : -1;
         return;
     }
-    const uint32_t mask = m > 0 ? select<D>(s, buf, c, qn, n, m, lane) : 0u;
-    write_rows<D>(mask, buf, c, qn, buf, lane);
+    const uint32_t mask = select<D>(s, buf, n, buf, n, m, lane);
+    write_rows<D>(mask, buf, n, buf, buf, lane);
     if (lane == 0) a.qcount[b] = m;
     if (a.fps_sel)
         for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)b * m + i] = s.sel[i];

@@ -56,6 +56,21 @@ class StreamRun:
             self.rec_b = (self.rec_units // Hkv) % B
             self.rec = {k: [] for k in ("q_new", "k_new", "v_new", "pos", "idx", "scores")}
 
+    _STATE = ("K", "V", "qbuf", "qcount", "q_recent", "pos_recent")
+
+    def state_dict(self) -> dict:
+        """Everything needed to resume the stream: the eviction manager's tensors, the cache length and
+        counters, and the input generator's state."""
+        st = {k: getattr(self, k).clone() for k in self._STATE}
+        st.update(L=self.L, n_ev=self.n_ev, steps_done=self.steps_done, gen=self.gen.state_dict())
+        return st
+
+    def load_state_dict(self, st: dict) -> None:
+        for k in self._STATE:
+            getattr(self, k).copy_(st[k])
+        self.L, self.n_ev, self.steps_done = int(st["L"]), int(st["n_ev"]), int(st["steps_done"])
+        self.gen.load_state_dict(st["gen"])
+
     def state_bytes(self) -> int:
         """HBM held by the eviction manager's own state (cache, buffers, ring, table, keep-set and score copies)."""
         ts = (self.K, self.V, self.qbuf, self.qcount, self.q_recent, self.pos_recent, self.rope, self.idx,
@@ -71,33 +86,53 @@ class StreamRun:
         r["v_new"].append(blk["v_new"][:n].reshape(n, U, d).index_select(1, u))
         r["pos"].append(blk["pos"][:n].index_select(1, self.rec_b))
 
-    def run(self, steps: int | None = None, timed: bool = False, stream=None, progress=None) -> dict:
+    def run(self, steps: int | None = None, timed: bool = False, stream=None, progress=None,
+            detail_blocks=()) -> dict:
         """Run `steps` decode steps (default: the config's).  Returns the step count, evictions and,
-        when timed, the summed GPU time of the library calls (generation excluded)."""
+        when timed, the summed GPU time of the library calls (generation excluded), each eviction's
+        latency, and the latency of every decode step in the blocks listed in `detail_blocks` (block
+        indices counted from this call's first block)."""
         b = self.base
         steps = self.scfg.steps if steps is None else steps
         stream = torch.cuda.current_stream() if stream is None else stream
         gpu_ms = 0.0
+        evict_ms, step_ms = [], []
         t0 = time.perf_counter()
         done = 0
+        blk_no = 0
+        ev = lambda: torch.cuda.Event(enable_timing=True)
         while done < steps:
             n = min(self.block_steps, steps - done)
             blk = self.gen.block(n, self.pool)
             if self.rec is not None:
                 self._record_inputs(blk, n)
+            detail = timed and blk_no in detail_blocks
+            evs, step_evs = [], []
             if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = ev(), ev()
                 e0.record(stream)
             for i in range(n):
+                if detail:
+                    step_evs.append(ev())
+                    step_evs[-1].record(stream)
                 lib.decode_step(self.shape, self.K, self.V, self.L, blk["k_new"][i], blk["v_new"][i], blk["pos"][i],
                                 self.qbuf, self.qcount, blk["q_new"][i], self.q_recent, self.pos_recent, self.rope,
                                 stream=stream)
                 self.L += 1
+                if detail:
+                    step_evs.append(ev())
+                    step_evs[-1].record(stream)
                 if self.L == b.cap:
+                    rec = self.rec is not None
+                    if timed:
+                        evs.append((ev(), ev()))
+                        evs[-1][0].record(stream)
                     lib.evict(self.shape, self.K, self.V, b.cap, self.qbuf, self.qcount, self.q_recent,
-                              self.pos_recent, blk["pos"][i], self.rope, idx_out=self.idx, scores_out=self.scores,
-                              stream=stream)
-                    if self.rec is not None:
+                              self.pos_recent, blk["pos"][i], self.rope, idx_out=self.idx if rec else None,
+                              scores_out=self.scores if rec else None, stream=stream)
+                    if timed:
+                        evs[-1][1].record(stream)
+                    if rec:
                         self.rec["idx"].append(self.idx.index_select(0, self.rec_units))
                         self.rec["scores"].append(self.scores.index_select(0, self.rec_units))
                     self.n_ev += 1
@@ -106,13 +141,35 @@ class StreamRun:
                 e1.record(stream)
                 e1.synchronize()
                 gpu_ms += e0.elapsed_time(e1)
+                evict_ms += [a.elapsed_time(z) for a, z in evs]
+                step_ms += [step_evs[k].elapsed_time(step_evs[k + 1]) for k in range(0, len(step_evs), 2)]
             done += n
+            blk_no += 1
             self.steps_done += n
             if progress is not None:
                 progress(self)
         torch.cuda.synchronize()
         return {"steps": steps, "evictions": self.n_ev, "L": self.L, "gpu_ms": gpu_ms if timed else None,
-                "wall_s": time.perf_counter() - t0}
+                "evict_ms": evict_ms, "step_ms": step_ms, "wall_s": time.perf_counter() - t0}
+
+    def fps_rounds_per_buffer(self, steps: int | None = None) -> int:
+        """Sampling rounds each query buffer goes through in `steps` decode steps from an empty state
+        (the count evolves the same way in every buffer)."""
+        b = self.base
+        steps = self.scfg.steps if steps is None else steps
+        bqmax, ring0 = b.n_beacon + b.n_recent_q, b.cap - b.n_recent_q
+        L = qc = rounds = 0
+        for _ in range(steps):
+            if L < ring0:
+                qc += 1
+                if qc >= bqmax:
+                    rounds += 1
+                    qc = b.n_beacon
+            L += 1
+            if L == b.cap:
+                qc = min(min(qc, b.n_beacon) + b.n_recent_q, b.n_beacon)
+                L = b.budget
+        return rounds
 
     def history(self) -> dict:
         """Recorded inputs and eviction results as host tensors (see the class docstring)."""

@@ -146,26 +146,49 @@ def make_query_buffers(cfg: EvictConfig, device="cpu", seed: int | None = None,
 # Streaming decode inputs.
 
 class StreamGen:
-    """Per-step inputs of the streaming decode simulation, drawn block by
-    block on the generator's device:
+    """Per-step inputs of the streaming decode simulation, drawn on the
+    generator's device:
       q_new [n, L, B, Hq, d]   bf16, pre-RoPE, the query mixture of the base
                                config around per-(layer, batch, q-head) centres
       k_new [n, L, B, Hkv, d]  bf16, pre-RoPE keys (N(0, I), 1% rows x 8)
       v_new [n, L, B, Hkv, d]  bf16, N(0, I)
       pos   [n, B]             int32, p0_b + s for global step s
     Every drift_every steps (before step s = k * drift_every, k >= 1) each
-    centre becomes normalize(u_c + 0.5 g), g ~ N(0, I_d / d)."""
+    centre becomes normalize(u_c + 0.5 g), g ~ N(0, I_d / d).  Draws happen in
+    whole chunks of `chunk` steps at fixed step boundaries, and steps a call
+    does not use wait for the next one, so the sequence does not depend on how
+    the caller splits the run into blocks (and resumes exactly from
+    state_dict())."""
 
-    def __init__(self, scfg, device="cpu", seed: int | None = None):
+    def __init__(self, scfg, device="cpu", seed: int | None = None, chunk: int = 16):
         base = scfg.base
-        self.scfg, self.base = scfg, base
+        if scfg.drift_every % chunk:
+            raise ValueError("drift_every must be a multiple of the chunk size")
+        self.scfg, self.base, self.chunk = scfg, base, chunk
         self.device = torch.device(device)
         self.g = _gen(self.device, base.seed if seed is None else seed)
         L, B, Hq, d = base.n_layers, base.batch, base.hq, base.d
         self.centres = _unit_rows(self.g, (L, B, Hq, n_centres(base.mix)), d, self.device)
         self.p0 = torch.randint(0, scfg.p0_max, (B,), generator=self.g, device=self.device, dtype=torch.int64)
-        self.step = 0
+        self.step = 0           # steps handed out
         self._last_drift = 0
+        self._buf = None        # the current chunk
+        self._cpos = 0          # steps of it handed out
+
+    def state_dict(self) -> dict:
+        st = {"rng": self.g.get_state(), "centres": self.centres.clone(), "p0": self.p0.clone(),
+              "step": self.step, "last_drift": self._last_drift, "cpos": self._cpos}
+        if self._buf is not None:
+            st.update({"buf_" + k: v.clone() for k, v in self._buf.items()})
+        return st
+
+    def load_state_dict(self, st: dict) -> None:
+        self.g.set_state(st["rng"])
+        self.centres = st["centres"].to(self.device).clone()
+        self.p0 = st["p0"].to(self.device).clone()
+        self.step, self._last_drift, self._cpos = int(st["step"]), int(st["last_drift"]), int(st["cpos"])
+        keys = [k[4:] for k in st if k.startswith("buf_")]
+        self._buf = {k: st["buf_" + k].to(self.device).clone() for k in keys} if keys else None
 
     def _drift(self) -> None:
         d = self.base.d
@@ -173,17 +196,23 @@ class StreamGen:
         c = self.centres + 0.5 * g
         self.centres = c / c.norm(dim=-1, keepdim=True)
 
-    def _draw(self, n: int, out: dict, at: int) -> None:
+    def _draw_chunk(self) -> None:
+        """Draw the chunk that starts at step self.step (a multiple of the chunk size)."""
         b = self.base
         L, B, Hq, Hkv, d = b.n_layers, b.batch, b.hq, b.hkv, b.d
+        s0, n = self.step, self.chunk
+        if s0 % self.scfg.drift_every == 0 and s0 != self._last_drift:
+            self._drift()
+            self._last_drift = s0
+        out = self.alloc(n) if self._buf is None else self._buf
         q = query_rows(self.g, self.centres, n, b.mix)                  # [L, B, Hq, n, d]
-        out["q_new"][at:at + n] = q.permute(3, 0, 1, 2, 4).to(torch.bfloat16)
+        out["q_new"].copy_(q.permute(3, 0, 1, 2, 4))
         del q
-        out["k_new"][at:at + n] = key_rows(self.g, (n, L, B, Hkv), 1, d, self.device)[..., 0, :].to(torch.bfloat16)
-        out["v_new"][at:at + n] = torch.randn(n, L, B, Hkv, d, generator=self.g,
-                                              device=self.device).to(torch.bfloat16)
-        s = torch.arange(self.step, self.step + n, device=self.device, dtype=torch.int64)
-        out["pos"][at:at + n] = (self.p0.unsqueeze(0) + s.unsqueeze(1)).to(torch.int32)
+        out["k_new"].copy_(key_rows(self.g, (n, L, B, Hkv), 1, d, self.device)[..., 0, :])
+        out["v_new"].copy_(torch.randn(n, L, B, Hkv, d, generator=self.g, device=self.device))
+        s = torch.arange(s0, s0 + n, device=self.device, dtype=torch.int64)
+        out["pos"].copy_(self.p0.unsqueeze(0) + s.unsqueeze(1))
+        self._buf, self._cpos = out, 0
 
     def alloc(self, n: int) -> dict:
         b = self.base
@@ -194,18 +223,17 @@ class StreamGen:
                 "v_new": torch.empty(n, L, B, Hkv, d, dtype=torch.bfloat16, device=dev),
                 "pos": torch.empty(n, B, dtype=torch.int32, device=dev)}
 
-    def block(self, n: int, out: dict | None = None, chunk: int = 16) -> dict:
-        """The next n steps' inputs (into `out` when given, a dict from alloc(>= n)).
-        Draws at most `chunk` steps at a time to bound the fp32 temporaries."""
+    def block(self, n: int, out: dict | None = None) -> dict:
+        """The next n steps' inputs (into `out` when given, a dict from alloc(>= n))."""
         out = self.alloc(n) if out is None else out
         at = 0
         while at < n:
-            if self.step % self.scfg.drift_every == 0 and self.step != self._last_drift:
-                self._drift()
-                self._last_drift = self.step
-            to_drift = self.scfg.drift_every - self.step % self.scfg.drift_every
-            k = min(chunk, n - at, to_drift)
-            self._draw(k, out, at)
+            if self._buf is None or self._cpos >= self.chunk:
+                self._draw_chunk()
+            k = min(self.chunk - self._cpos, n - at)
+            for key, t in out.items():
+                t[at:at + k] = self._buf[key][self._cpos:self._cpos + k]
+            self._cpos += k
             self.step += k
             at += k
         return out

@@ -69,3 +69,23 @@ def test_oracle_views_unit_major():
     assert (v["qbuf"][0] == synth.to_u16(a["qbuf"][0, 2, 2:4])).all()
     assert int(v["t"][0]) == int(a["t"][2])
     assert (v["K"][1] == synth.to_u16(a["K"][0, 0, 0])).all()
+
+
+def test_stream_inputs_do_not_depend_on_block_sizes_and_resume():
+    """The streaming generator gives the same step sequence however the run is split into blocks, and
+    continues exactly from a saved state."""
+    from long_reasoning_decode_amd.configs import TINY_STREAM
+    whole = synth.StreamGen(TINY_STREAM).block(300)
+    g = synth.StreamGen(TINY_STREAM)
+    parts = [g.block(n) for n in (7, 30, 13, 50, 200)]
+    for k in whole:
+        assert torch.equal(whole[k], torch.cat([p[k] for p in parts])), k
+    g3 = synth.StreamGen(TINY_STREAM)
+    g3.block(37)
+    g4 = synth.StreamGen(TINY_STREAM, seed=1)
+    g4.load_state_dict(g3.state_dict())
+    rest = g4.block(263)
+    for k in whole:
+        assert torch.equal(whole[k][37:], rest[k]), k
+    # cluster centres drift at the stated cadence: step 256 starts a new drift period
+    assert g4._last_drift == 256

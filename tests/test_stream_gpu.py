@@ -8,7 +8,7 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import STREAM, TINY_STREAM
+from long_reasoning_decode_amd.configs import STREAM, TINY_STREAM, TINY_STREAM_1R31B
 from long_reasoning_decode_amd.stream import StreamRun
 
 from _stream_helpers import compare_stream, replay
@@ -60,6 +60,33 @@ def test_stream_tiny_resumes_across_calls():
         run.run(n)
     assert run.steps_done == scfg.steps
     _check(scfg, run, units, "stream-tiny resumed")
+
+
+def test_stream_tiny_one_recent_31_beacons():
+    """The 1 recent + 31 beacon split: a sampling round after every collection step."""
+    scfg = TINY_STREAM_1R31B
+    units = range(scfg.base.units)
+    run = StreamRun(scfg, record_units=units, block=64)
+    run.run()
+    assert run.fps_rounds_per_buffer() > 0.8 * scfg.steps   # nearly every step samples
+    _check(scfg, run, units, "stream-tiny 1r31b")
+
+
+def test_stream_checkpoint_resume(tmp_path):
+    """Stopping at a step, saving the state to a file and resuming in a fresh stream object gives the
+    same stream, bit for bit, as running straight through."""
+    scfg = TINY_STREAM
+    a = StreamRun(scfg, block=50)
+    a.run(600)
+    b = StreamRun(scfg, block=50)
+    b.run(265)                      # mid-cycle, inside a collection phase
+    torch.save(b.state_dict(), tmp_path / "stream.pt")
+    c = StreamRun(scfg, block=50)
+    c.load_state_dict(torch.load(tmp_path / "stream.pt", weights_only=True))
+    c.run(335)
+    assert (c.L, c.n_ev, c.steps_done) == (a.L, a.n_ev, a.steps_done)
+    for k in StreamRun._STATE:
+        assert torch.equal(getattr(c, k), getattr(a, k)), k
 
 
 def test_decode_step_rejects_bad_length():
