@@ -310,3 +310,37 @@ def test_evict_rejects_bad_shapes_without_launching():
                                                                                    device="cuda"),
                 scores_out=torch.empty((2, 161), device="cuda"))
     assert e.value.code == -3
+
+
+@pytest.mark.parametrize("cfg", [TINY, QWEN3_4B.scaled(n_layers=2, batch=2), R1_QWEN_7B.scaled(n_layers=1, batch=2)],
+                         ids=lambda c: c.name)
+def test_evict_equals_the_separate_calls(cfg):
+    """bkv_evict (one fused kernel per unit, then the merge) gives bit for bit what bkv_score, bkv_select,
+    bkv_compact and bkv_fps_merge give one after the other, with or without its optional outputs."""
+    N = cfg.n_len
+    _flush(f"evict vs separate calls {cfg.name}")
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    inp["qcount"].view(-1)[::5] = 7
+    rope = H.rope_dev(cfg)
+    shape = L.shape_of(cfg, cap=N)
+    fused = H.run_evict_gpu(cfg, inp, N, rope=rope)
+
+    sep = {k: v.clone() for k, v in inp.items()}
+    scores = torch.empty((cfg.units, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.units, cfg.budget), dtype=torch.int32, device="cuda")
+    sel = torch.empty((cfg.qbufs, cfg.n_beacon), dtype=torch.int32, device="cuda")
+    L.score(shape, sep["K"], N, sep["qbuf"], sep["qcount"], sep["q_recent"], sep["pos_recent"], sep["t"], rope, scores)
+    L.select(shape, scores, N, idx)
+    L.compact(shape, sep["K"], sep["V"], N, idx)
+    L.fps_merge(shape, sep["qbuf"], sep["qcount"], sep["q_recent"], sel)
+
+    bare = {k: v.clone() for k, v in inp.items()}
+    L.evict(shape, bare["K"], bare["V"], N, bare["qbuf"], bare["qcount"], bare["q_recent"], bare["pos_recent"],
+            bare["t"], rope)
+    torch.cuda.synchronize()
+    assert torch.equal(fused["scores"], scores)
+    assert torch.equal(fused["idx"], idx)
+    assert torch.equal(fused["fps_sel"], sel)
+    for k in ("K", "V", "qbuf", "qcount"):
+        assert torch.equal(fused[k], sep[k]), k
+        assert torch.equal(bare[k], sep[k]), k
