@@ -30,7 +30,7 @@ _lib = None
 class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int) for n in (
         "n_layers", "batch", "hq", "hkv", "d", "cap", "budget", "n_prefix",
-        "n_recent_kv", "n_beacon", "n_recent_q", "causal", "qcap")] + [("theta", C.c_double)]
+        "n_recent_kv", "n_beacon", "n_recent_q", "causal", "qcap", "pool_mean")] + [("theta", C.c_double)]
 
 
 @dataclass
@@ -47,13 +47,14 @@ class OracleCfg:
     theta: float
     qcap: int = 32
     causal: int = 1
+    pool_mean: int = 0
     n_layers: int = 1
     batch: int = 1
 
     def c(self) -> _Cfg:
         return _Cfg(self.n_layers, self.batch, self.hq, self.hkv, self.d, self.cap,
                     self.budget, self.n_prefix, self.n_recent_kv, self.n_beacon,
-                    self.n_recent_q, self.causal, self.qcap, float(self.theta))
+                    self.n_recent_q, self.causal, self.qcap, self.pool_mean, float(self.theta))
 
     @property
     def G(self) -> int:

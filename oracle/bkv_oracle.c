@@ -10,7 +10,7 @@
  * notes "BeaconKV：用历史查询代表保护长推理的远程回看" on liuzhao09.github.io,
  * "Summary" means the rcap.io post "BeaconKV: Key-Value Cache Compression
  * Guided by Beacon Queries"):
- *   Notes §2.1, Eq. 4-6     attention weights w_{tau,j}, max pooling s_j^max
+ *   Notes §2.1, Eq. 4-6     attention weights w_{tau,j}, max and mean pooling
  *   Notes §2.2, App. Alg. 1 farthest point sampling (FPS)
  *   Notes §2.2, Eq. 9       continual FPS buffer bounds B_Q^min / B_Q^max
  *   Notes §2.2, App. Alg. 2 cycle: freeze beacons, collect recents, evict,
@@ -47,6 +47,7 @@ typedef struct {
     int n_recent_q;   /* recent queries; B_Q^max = n_beacon + n_recent_q */
     int causal;       /* recent query i sees only slots <= N - n_recent_q + i */
     int qcap;         /* rows allocated per query buffer (>= B_Q^max) */
+    int pool_mean;    /* 0: max pooling (Eq. 7); 1: mean pooling (Eq. 6) */
     double theta;     /* RoPE base */
 } bkvo_cfg;
 
@@ -389,8 +390,22 @@ static int n_beacons_of(const bkvo_cfg *c, int qcount)
     return nb < 0 ? 0 : nb;
 }
 
+/* Fold one observation row's weights into the unit's score. */
+static void pool_row(const bkvo_cfg *c, const double *w, int N, double *score)
+{
+    for (int j = 0; j < N; ++j) {
+        if (c->pool_mean) score[j] += w[j];
+        else if (w[j] > score[j]) score[j] = w[j];
+    }
+}
+
 /* Score of one unit (Notes §2.3, Eq. 7): max over the group's heads and all
- * their observation rows of the row's attention weight. */
+ * their observation rows of the row's attention weight.
+ * With pool_mean the max becomes the mean of Notes §2.1 Eq. 6, taken over the
+ * same rows of all the group's heads (the Max/Mean ablation of Notes §3.3
+ * Table 2 pools both over the queries and over the heads).  A row's weight on
+ * a key it does not see is 0, and the divisor counts every observation row:
+ * sum over the heads h of min(qcount_h, n_beacon) + n_recent_q. */
 static void score_unit(const bkvo_cfg *c, int N, int u, const uint16_t *K,
                        const uint16_t *qbuf, const int32_t *qcount,
                        const uint16_t *q_recent, const int32_t *pos_recent,
@@ -401,24 +416,29 @@ static void score_unit(const bkvo_cfg *c, int N, int u, const uint16_t *K,
     uint16_t *qh = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
     for (int j = 0; j < N; ++j) score[j] = 0.0;
     const uint16_t *Ku = K + (size_t)u * c->cap * d;
+    int rows = 0;
     for (int h = 0; h < G; ++h) {
         const uint16_t *buf = qbuf + ((size_t)u * G + h) * c->qcap * d;
         int nb = n_beacons_of(c, qcount[(size_t)u * G + h]);
         for (int s = 0; s < nb; ++s) {
             bkvo_rope_row(buf + (size_t)s * d, d, c->theta, t[u], qh);
             bkvo_row_weights(qh, Ku, N, d, N - 1, w);
-            for (int j = 0; j < N; ++j) if (w[j] > score[j]) score[j] = w[j];
+            pool_row(c, w, N, score);
+            ++rows;
         }
         const uint16_t *rec = q_recent + ((size_t)u * G + h) * c->n_recent_q * d;
         for (int i = 0; i < c->n_recent_q; ++i) {
+            ++rows;
             int vis = c->causal ? N - c->n_recent_q + i : N - 1;
             if (vis < 0) continue;
             bkvo_rope_row(rec + (size_t)i * d, d, c->theta,
                           pos_recent[(size_t)u * c->n_recent_q + i], qh);
             bkvo_row_weights(qh, Ku, N, d, vis, w);
-            for (int j = 0; j < N; ++j) if (w[j] > score[j]) score[j] = w[j];
+            pool_row(c, w, N, score);
         }
     }
+    if (c->pool_mean && rows > 0)
+        for (int j = 0; j < N; ++j) score[j] /= rows;
     free(w);
     free(qh);
 }

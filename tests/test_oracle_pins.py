@@ -311,12 +311,13 @@ def _random_unit_inputs(cfg, U, rng, qcount=None):
     return dict(K=K, V=V, qbuf=qbuf, qcount=qc, q_recent=qr, pos_recent=pos, t=t)
 
 
-def _brute_scores(cfg, inp, N):
-    """Max over the group's heads and rows of scipy softmax rows (brute force)."""
+def _brute_scores(cfg, inp, N, mean=False):
+    """Max (or mean) over the group's heads and rows of scipy softmax rows (brute force)."""
     U = inp["K"].shape[0]
     out = np.zeros((U, N))
     for u in range(U):
         Kf = f32(inp["K"][u, :N]).astype(np.float64)
+        stack = []
         for h in range(cfg.G):
             nb = min(int(inp["qcount"][u, h]), cfg.n_beacon)
             obs = [(O.rope_row(inp["qbuf"][u, h, s], cfg.theta, int(inp["t"][u])), N - 1) for s in range(nb)]
@@ -324,11 +325,13 @@ def _brute_scores(cfg, inp, N):
                 vis = N - cfg.n_recent_q + i if cfg.causal else N - 1
                 obs.append((O.rope_row(inp["q_recent"][u, h, i], cfg.theta, int(inp["pos_recent"][u, i])), vis))
             for q, vis in obs:
-                if vis < 0:
-                    continue
-                z = Kf[:vis + 1] @ f32(q).astype(np.float64) / math.sqrt(cfg.d)
-                w = scipy.special.softmax(z)
-                out[u, :vis + 1] = np.maximum(out[u, :vis + 1], w)
+                w = np.zeros(N)
+                if vis >= 0:
+                    z = Kf[:vis + 1] @ f32(q).astype(np.float64) / math.sqrt(cfg.d)
+                    w[:vis + 1] = scipy.special.softmax(z)
+                stack.append(w)
+        if stack:
+            out[u] = np.mean(stack, axis=0) if mean else np.max(stack, axis=0)
     return out
 
 
@@ -342,6 +345,47 @@ def test_score_is_max_over_heads_and_rows(causal, qcount):
     s = O.score(cfg, inp["K"], inp["qbuf"], inp["qcount"], inp["q_recent"], inp["pos_recent"], inp["t"], n_len=N)
     ref = _brute_scores(cfg, inp, N)
     assert np.allclose(s, ref, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+@pytest.mark.parametrize("qcount", [3, 1, 0, 6, (5, 1)])
+@pytest.mark.parametrize("N", [37, 2])
+def test_mean_score_is_mean_over_heads_and_rows(causal, qcount, N):
+    """Mean pooling (Notes §2.1 Eq. 6, over queries and heads as in §3.3 Table 2)."""
+    rng = np.random.default_rng(20 + N + 10 * causal + (qcount if isinstance(qcount, int) else 7))
+    cfg = _cfg(causal=causal, pool_mean=1)
+    inp = _random_unit_inputs(cfg, 3, rng, qcount=0)
+    inp["qcount"][:] = qcount
+    s = O.score(cfg, inp["K"], inp["qbuf"], inp["qcount"], inp["q_recent"], inp["pos_recent"], inp["t"], n_len=N)
+    assert np.allclose(s, _brute_scores(cfg, inp, N, mean=True), rtol=1e-12, atol=1e-300)
+    # every row that sees a key has weights summing to 1, so the scores sum to
+    # (rows that see a key) / (all rows); at N = 2 causal recent rows 0 and 1 see nothing
+    nb = np.minimum(inp["qcount"][0], cfg.n_beacon).sum()
+    rows = nb + cfg.G * cfg.n_recent_q
+    seen = nb + cfg.G * sum(1 for i in range(cfg.n_recent_q)
+                            if (N - cfg.n_recent_q + i if causal else N - 1) >= 0)
+    assert np.allclose(s.sum(axis=1), seen / rows, rtol=1e-12)
+    # the mean lies between max / rows and the max
+    smax = O.score(_cfg(causal=causal), inp["K"], inp["qbuf"], inp["qcount"], inp["q_recent"],
+                   inp["pos_recent"], inp["t"], n_len=N)
+    assert np.all(s <= smax * (1 + 1e-12)) and np.all(s >= smax / rows * (1 - 1e-12))
+
+
+def test_mean_of_identical_rows_is_one_softmax():
+    """Every observation row the same query at the same position, no causal mask: the mean equals the
+    max equals that row's softmax."""
+    rng = np.random.default_rng(21)
+    cfg = _cfg(causal=0, pool_mean=1)
+    inp = _random_unit_inputs(cfg, 2, rng, qcount=3)
+    q = inp["qbuf"][:, :1, :1]
+    inp["qbuf"][:] = q
+    inp["q_recent"][:] = q
+    inp["pos_recent"][:] = inp["t"][:, None]
+    s = O.score(cfg, inp["K"], inp["qbuf"], inp["qcount"], inp["q_recent"], inp["pos_recent"], inp["t"])
+    for u in range(2):
+        qr = O.rope_row(q[u, 0, 0], cfg.theta, int(inp["t"][u]))
+        z = f32(inp["K"][u]).astype(np.float64) @ f32(qr).astype(np.float64) / math.sqrt(cfg.d)
+        assert np.allclose(s[u], scipy.special.softmax(z), rtol=1e-12)
 
 
 def test_score_single_row_equals_softmax():
