@@ -140,7 +140,7 @@ def cpu_baseline(cfg, inp, target_s: float = 10.0) -> dict:
     threads = O.default_threads()
     oc = O.OracleCfg(hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, cap=cfg.n_len, budget=cfg.budget, n_prefix=cfg.n_prefix,
                      n_recent_kv=cfg.n_recent_kv, n_beacon=cfg.n_beacon, n_recent_q=cfg.n_recent_q,
-                     theta=cfg.theta, qcap=cfg.qcap)
+                     theta=cfg.theta, qcap=cfg.qcap, pool_mean=int(cfg.pool == "mean"))
     n = max(threads, 8)
     while True:
         v = synth.oracle_views(cfg, inp, list(range(n)))

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 2
+#define BKV_ABI_VERSION 3
 
 typedef uint16_t bkv_bf16; /* raw bf16 bits */
 
@@ -71,6 +71,7 @@ enum {
 
 /* flags */
 #define BKV_CAUSAL_RECENT 1u /* recent query i sees only slots <= n_len - n_recent_q + i */
+#define BKV_POOL_MEAN 2u     /* scores pool the weights by their mean, not their max (see bkv_score) */
 
 typedef struct bkv_shape {
     int32_t n_layers, batch, n_q_heads, n_kv_heads, head_dim; /* head_dim in {64, 128}; G <= 8 */
@@ -81,7 +82,7 @@ typedef struct bkv_shape {
     int32_t n_beacon;     /* B_Q^min: beacons kept by FPS */
     int32_t n_recent_q;   /* recent queries; B_Q^max = n_beacon + n_recent_q <= 32 */
     int32_t qcap;         /* rows allocated per query buffer, >= B_Q^max */
-    uint32_t flags;       /* BKV_CAUSAL_RECENT */
+    uint32_t flags;       /* BKV_CAUSAL_RECENT | BKV_POOL_MEAN */
 } bkv_shape;
 
 /* ABI version (BKV_ABI_VERSION). */
@@ -120,6 +121,10 @@ int bkv_fps_update(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
  * over the keys a row sees (all n_len keys for beacons; for recent row i,
  * under BKV_CAUSAL_RECENT, keys <= n_len - n_recent_q + i):
  *   scores[u][j] = max over rows r of exp(z_rj - logsumexp_j' z_rj').
+ * Under BKV_POOL_MEAN (Notes §2.1 Eq. 6, pooled over queries and heads as in
+ * the Max/Mean ablation of Notes §3.3 Table 2) the max becomes the sum over
+ * the rows divided by their number, sum_h min(qcount, n_beacon) + n_recent_q
+ * over the group; a row's weight on a key it does not see counts as 0.
  * bf16 MFMA products with fp32 accumulation.  Positions are clamped to
  * [0, rope_rows).  Out: scores [units][n_len]. */
 int bkv_score(const bkv_shape *shape, const bkv_bf16 *K, int32_t n_len,

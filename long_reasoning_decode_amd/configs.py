@@ -33,6 +33,7 @@ class EvictConfig:
     mix: str = "clusters8"  # query distribution, see synth.py
     seed: int = 20261202
     qcap: int = 32         # rows allocated per query buffer
+    pool: str = "max"      # pooling of the weights: "max" (§2.3 Eq. 7) or "mean" (§2.1 Eq. 6, §3.3 Table 2)
 
     @property
     def n_len(self) -> int:
@@ -87,7 +88,10 @@ QWEN3_14B_4K = EvictConfig(
     budget=4096, n_new=128, n_prefix=4, n_recent_kv=16,
     t_lo=4223, t_hi=32768, seed=20261202 + 410)
 
-EVICT_CONFIGS = {c.name: c for c in (TINY, QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, QWEN3_14B_4K)}
+# the Max/Mean ablation (§3.3 Table 2): the same eviction with mean pooling over queries and heads
+QWEN3_4B_MEAN = replace(QWEN3_4B, name="qwen3-4b-mean", pool="mean")
+
+EVICT_CONFIGS = {c.name: c for c in (TINY, QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, QWEN3_14B_4K, QWEN3_4B_MEAN)}
 
 
 @dataclass(frozen=True)
@@ -123,4 +127,6 @@ STREAM_1R31B = StreamConfig(name="stream-qwen3-4b-1r31b",
 TINY_STREAM_1R31B = StreamConfig(name="stream-tiny-1r31b",
                                  base=replace(TINY, batch=2, n_beacon=31, n_recent_q=1, seed=20261202 + 530),
                                  steps=400, drift_every=256, p0_max=1000)
-STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM, STREAM_1R31B, TINY_STREAM_1R31B)}
+TINY_STREAM_MEAN = StreamConfig(name="stream-tiny-mean", base=replace(TINY, batch=2, pool="mean", seed=20261202 + 540),
+                                steps=600, drift_every=256, p0_max=1000)
+STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM, STREAM_1R31B, TINY_STREAM_1R31B, TINY_STREAM_MEAN)}

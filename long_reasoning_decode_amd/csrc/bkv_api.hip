@@ -27,7 +27,7 @@ int check_shape(const bkv_shape* s) {
     if (s->n_beacon + s->n_recent_q > kMaxBq) return BKV_EUNSUPPORTED;
     if (s->qcap < s->n_beacon + s->n_recent_q) return BKV_EINVAL;
     if (s->cap <= 0 || s->budget < 0 || s->n_prefix < 0 || s->n_recent_kv < 0) return BKV_EINVAL;
-    if (s->flags & ~BKV_CAUSAL_RECENT) return BKV_EINVAL;
+    if (s->flags & ~(BKV_CAUSAL_RECENT | BKV_POOL_MEAN)) return BKV_EINVAL;
     const int64_t units = (int64_t)s->n_layers * s->batch * s->n_kv_heads;
     const int64_t qbufs = (int64_t)s->n_layers * s->batch * s->n_q_heads;
     if (units > INT32_MAX || qbufs > INT32_MAX) return BKV_ERANGE;
@@ -73,6 +73,7 @@ bkv::ScoreArgs score_args(const bkv_shape* s, const bkv_bf16* K, int32_t n_len, 
     a.n_beacon = s->n_beacon;
     a.n_recent_q = s->n_recent_q;
     a.causal = (s->flags & BKV_CAUSAL_RECENT) ? 1 : 0;
+    a.pool_mean = (s->flags & BKV_POOL_MEAN) ? 1 : 0;
     a.rope_rows = rope_rows;
     return a;
 }

@@ -21,21 +21,21 @@ constexpr int kBinOff = 1280;      // uint32 [2]
 constexpr int kFirstOff = 1296;    // int
 constexpr int kSrcOff = 2048;      // uint16 [budget]
 
-template <int D, int KS>
+template <int D, int KS, bool MEAN>
 __global__ __launch_bounds__(score::kThreads) void evict_kernel(EvictArgs a) {
     using L = score::Layout<D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    uint32_t* codes = reinterpret_cast<uint32_t*>(smem + L::kFixed);
+    uint32_t* codes = reinterpret_cast<uint32_t*>(smem + L::fixed_bytes(MEAN));
     const int u = blockIdx.x;
     if (u >= a.sc.units) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = a.sc.n_len;
 
     // scores, then the order codes of the fp32 scores, which the select ranks
-    score::unit_codes<D, KS>(a.sc, u, smem, codes);
+    score::unit_codes<D, KS, MEAN>(a.sc, u, smem, codes);
     float* sc_out = a.sc.scores ? a.sc.scores + (size_t)u * N : nullptr;
     for (int j = tid; j < N; j += score::kThreads) {
-        const float s = __builtin_amdgcn_exp2f(f32_unorder(codes[j]));
+        const float s = score::score_of<MEAN>(codes[j]);
         if (sc_out) sc_out[j] = s;
         codes[j] = f32_order(s);
     }
@@ -63,23 +63,28 @@ __global__ __launch_bounds__(score::kThreads) void evict_kernel(EvictArgs a) {
     compact::move_rows_wg<D, kHalf>(X, src, first, Bv, wave % kHalf, lane);
 }
 
-template <int D, int KS>
+template <int D, int KS, bool MEAN>
 hipError_t launch_one(const EvictArgs& a, hipStream_t st) {
     using L = score::Layout<D>;
     static_assert(kSrcOff + 2 * 8192 <= L::kRingBytes, "select scratch fits in the key ring");
-    const size_t smem = L::kFixed + (size_t)a.sc.n_len * 4;
-    hipLaunchKernelGGL((evict_kernel<D, KS>), dim3(a.sc.units), dim3(score::kThreads), smem, st, a);
+    const size_t smem = L::fixed_bytes(MEAN) + (size_t)a.sc.n_len * 4;
+    hipLaunchKernelGGL((evict_kernel<D, KS, MEAN>), dim3(a.sc.units), dim3(score::kThreads), smem, st, a);
     return hipGetLastError();
+}
+
+template <int D, bool MEAN>
+hipError_t launch_dm(const EvictArgs& a, hipStream_t st) {
+    // query heads per workgroup: the smallest power of two >= G; key split KS = waves / heads
+    constexpr int W = score::kWaves;
+    if (a.sc.G <= 1) return launch_one<D, W, MEAN>(a, st);
+    if (a.sc.G <= 2) return launch_one<D, W / 2, MEAN>(a, st);
+    if (a.sc.G <= 4) return launch_one<D, W / 4, MEAN>(a, st);
+    return launch_one<D, 1, MEAN>(a, st);
 }
 
 template <int D>
 hipError_t launch_d(const EvictArgs& a, hipStream_t st) {
-    // query heads per workgroup: the smallest power of two >= G; key split KS = waves / heads
-    constexpr int W = score::kWaves;
-    if (a.sc.G <= 1) return launch_one<D, W>(a, st);
-    if (a.sc.G <= 2) return launch_one<D, W / 2>(a, st);
-    if (a.sc.G <= 4) return launch_one<D, W / 4>(a, st);
-    return launch_one<D, 1>(a, st);
+    return a.sc.pool_mean ? launch_dm<D, true>(a, st) : launch_dm<D, false>(a, st);
 }
 
 }  // namespace

@@ -26,7 +26,7 @@ struct ScoreArgs {
     const int32_t* t;          // [batch]
     const float* rope_cs;      // [rope_rows][d/2][2]
     float* scores;             // [units][n_len]
-    int units, n_len, cap, batch, hkv, G, qcap, n_beacon, n_recent_q, causal, rope_rows;
+    int units, n_len, cap, batch, hkv, G, qcap, n_beacon, n_recent_q, causal, pool_mean, rope_rows;
 };
 
 struct SelectArgs {

@@ -20,6 +20,12 @@
 //           row are merged in LDS into c_r;
 //   pass 2: D[row][key] = Q K^T; max over the wave's rows of z - c per key,
 //           then over the heads with LDS atomics.
+// Mean pooling (Notes §2.1 Eq. 6, pooled over queries and heads as in the
+// Max/Mean ablation of Notes §3.3 Table 2) replaces pass 2's max by the sum of
+// exp2(z - c) over the wave's rows; the heads' partial sums of a stage go to
+// LDS and are added in head order by one wave during the next stage, so the
+// result does not depend on wave timing.  The divisor counts every
+// observation row of the group, sum_h min(qcount_h, n_beacon) + n_recent_q.
 // One unit per 8-wave workgroup and two workgroups per CU keep about 512
 // units in flight (about 285 MB at 2176 keys of d = 128), so a unit's keys
 // are still in the MALL when the second pass (and the compaction of the
@@ -59,9 +65,20 @@ struct Layout {
     static constexpr int kRingBytes = kStages * kStageBytes;
     static constexpr int kCrowOff = kRingBytes;                       // float [8 heads][32 rows]
     static constexpr int kPartOff = kCrowOff + 8 * 32 * 4;            // float2 [waves][32 rows]
-    static constexpr int kFixed = kPartOff + kWaves * 32 * 8;         // then uint32 per-key codes [n_len]
+    static constexpr int kPsumOff = kPartOff + kWaves * 32 * 8;       // mean: float [2][8 heads][64 keys]
+    static constexpr int kPsumBytes = 2 * 8 * kStageTiles * kTileKeys * 4;
+    // then uint32 per-key codes [n_len]
+    static constexpr int fixed_bytes(bool mean) { return mean ? kPsumOff + kPsumBytes : kPsumOff; }
     static_assert((kStageTiles * kDmaPerTile) % kWaves == 0, "stage DMA split");
 };
+
+// Score of a key from its code: max pooling keeps f32_order(max log2 weight),
+// mean pooling the fp32 bits of the mean weight.
+template <bool MEAN>
+__device__ __forceinline__ float score_of(uint32_t code) {
+    if constexpr (MEAN) return __uint_as_float(code);
+    else return __builtin_amdgcn_exp2f(f32_unorder(code));
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -196,11 +213,10 @@ __device__ __forceinline__ void dma_stage(const bkv_bf16* Ku, int st, int n_len,
     }
 }
 
-// Per-key codes f32_order(max over rows of z - c) of unit u (base 2) into
-// codes[0 .. n_len) in LDS.  All waves call it; on return the codes are
-// complete and visible to the workgroup, and this wave has no memory
-// operation in flight.
-template <int D, int KS>
+// Per-key codes of unit u into codes[0 .. n_len) in LDS (see score_of).  All
+// waves call it; on return the codes are complete and visible to the
+// workgroup, and this wave has no memory operation in flight.
+template <int D, int KS, bool MEAN>
 __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint32_t* codes) {
     using L = Layout<D>;
     constexpr int kS = D / 16;
@@ -318,15 +334,35 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
     }
     lds_barrier();   // c_r published
 
-    // ---- pass 2: max over rows of z - c, per key
+    // ---- pass 2: max (or sum) over rows of z - c, per key
     float cq[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) cq[q] = active ? crow[head * 32 + 8 * (q >> 2) + 4 * half + (q & 3)] : 0.0f;
+    constexpr int kStageKeys = kStageTiles * kTileKeys;
+    float* psum = reinterpret_cast<float*>(smem + L::kPsumOff);
+    float inv_rows = 0.0f;
+    if constexpr (MEAN) {
+        int rows = 0;
+        for (int h = 0; h < a.G; ++h) rows += clampi(a.qcount[u * a.G + h], 0, a.n_beacon) + a.n_recent_q;
+        inv_rows = rows > 0 ? 1.0f / (float)rows : 0.0f;
+    }
+    // mean: one wave adds the heads' partial sums of stage rs, in head order
+    auto reduce_stage = [&](int rs) {
+        if (wave != rs % kWaves) return;
+        const float* ps = psum + (rs & 1) * (8 * kStageKeys);
+        const int key = rs * kStageKeys + lane;
+        float sum = 0.0f;
+        for (int h = 0; h < a.G; ++h) sum += ps[h * kStageKeys + lane];
+        if (key < n_len) codes[key] = __float_as_uint(sum * inv_rows);
+    };
     for (int st = 0; st < n_st; ++st) {
         if (st + 1 < n_st) wait_vm<L::kDmaPerWave>();
         else wait_vm<0>();
         lds_barrier();
         if (st + 2 < n_st) dma_stage<D>(Ku, st + 2, n_len, stage(st + 2), wave, lane);
+        if constexpr (MEAN) {
+            if (st > 0) reduce_stage(st - 1);
+        }
         if (!active) continue;
 #pragma unroll
         for (int i = 0; i < kStageTiles; ++i) {
@@ -338,21 +374,38 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
 #pragma unroll
             for (int s = 0; s < kS; ++s)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], k_operand<D>(tl, r, s, half), acc, 0, 0, 0);
-            float cm = -__builtin_inff();
-            if (j * kTileKeys + kTileKeys - 1 > vis_floor) {
+            const bool edge = j * kTileKeys + kTileKeys - 1 > vis_floor;
+            if constexpr (MEAN) {
+                float sm = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
-                    float tv = __builtin_fmaf(acc[q], sc2, -cq[q]);
-                    if (key > row_vis(a, 8 * (q >> 2) + 4 * half + (q & 3))) tv = -__builtin_inff();
-                    cm = __builtin_fmaxf(cm, tv);
+                    float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[q], sc2, -cq[q]));
+                    if (edge && key > row_vis(a, 8 * (q >> 2) + 4 * half + (q & 3))) e = 0.0f;
+                    sm += e;
                 }
+                sm += __shfl_xor(sm, 32, 64);
+                if (half == 0) psum[(st & 1) * (8 * kStageKeys) + head * kStageKeys + i * kTileKeys + r] = sm;
             } else {
+                float cm = -__builtin_inff();
+                if (edge) {
 #pragma unroll
-                for (int q = 0; q < 16; ++q) cm = __builtin_fmaxf(cm, __builtin_fmaf(acc[q], sc2, -cq[q]));
+                    for (int q = 0; q < 16; ++q) {
+                        float tv = __builtin_fmaf(acc[q], sc2, -cq[q]);
+                        if (key > row_vis(a, 8 * (q >> 2) + 4 * half + (q & 3))) tv = -__builtin_inff();
+                        cm = __builtin_fmaxf(cm, tv);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) cm = __builtin_fmaxf(cm, __builtin_fmaf(acc[q], sc2, -cq[q]));
+                }
+                cm = __builtin_fmaxf(cm, __shfl_xor(cm, 32, 64));
+                if (half == 0 && key < n_len) atomicMax(&codes[key], f32_order(cm));
             }
-            cm = __builtin_fmaxf(cm, __shfl_xor(cm, 32, 64));
-            if (half == 0 && key < n_len) atomicMax(&codes[key], f32_order(cm));
         }
+    }
+    if constexpr (MEAN) {
+        lds_barrier();   // the last stage's partial sums are in LDS
+        reduce_stage(n_st - 1);
     }
     __syncthreads();
 }

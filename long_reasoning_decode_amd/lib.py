@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbkv.so")
 
 BKV_CAUSAL_RECENT = 1
+BKV_POOL_MEAN = 2
 ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE", -4: "BKV_EHIP"}
 
 EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_fps_update",
@@ -77,7 +78,13 @@ def version() -> int:
     return load().bkv_version()
 
 
-def shape_of(cfg: EvictConfig, cap: Optional[int] = None, flags: int = BKV_CAUSAL_RECENT) -> Shape:
+def flags_of(cfg: EvictConfig) -> int:
+    """Default flags of a workload: causal recent rows, and the pooling it names."""
+    return BKV_CAUSAL_RECENT | (BKV_POOL_MEAN if cfg.pool == "mean" else 0)
+
+
+def shape_of(cfg: EvictConfig, cap: Optional[int] = None, flags: Optional[int] = None) -> Shape:
+    flags = flags_of(cfg) if flags is None else flags
     return Shape(cfg.n_layers, cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.cap if cap is None else cap,
                  cfg.budget, cfg.n_prefix, cfg.n_recent_kv, cfg.n_beacon, cfg.n_recent_q, cfg.qcap, flags)
 

@@ -16,11 +16,14 @@ TIE_BAND_ABS = 1e-6      # keys within this of the k-th score may swap
 TIE_BAND_REL = 2e-4      # ... and only if within twice the score tolerance
 
 
-def ocfg(cfg: EvictConfig, n_len: int | None = None, causal: int = 1) -> O.OracleCfg:
+def ocfg(cfg: EvictConfig, n_len: int | None = None, flags: int | None = None) -> O.OracleCfg:
+    """Oracle configuration of a workload; flags as in bkv.h (default: the workload's own)."""
     N = cfg.n_len if n_len is None else n_len
+    flags = L.flags_of(cfg) if flags is None else flags
     return O.OracleCfg(hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, cap=N, budget=cfg.budget,
                        n_prefix=cfg.n_prefix, n_recent_kv=cfg.n_recent_kv, n_beacon=cfg.n_beacon,
-                       n_recent_q=cfg.n_recent_q, theta=cfg.theta, qcap=cfg.qcap, causal=causal,
+                       n_recent_q=cfg.n_recent_q, theta=cfg.theta, qcap=cfg.qcap,
+                       causal=int(bool(flags & L.BKV_CAUSAL_RECENT)), pool_mean=int(bool(flags & L.BKV_POOL_MEAN)),
                        n_layers=cfg.n_layers, batch=cfg.batch)
 
 
@@ -67,7 +70,7 @@ def check_keep(idx_gpu: np.ndarray, idx_orc: np.ndarray, s_orc: np.ndarray, n_le
     return len(diff) // 2
 
 
-def run_evict_gpu(cfg: EvictConfig, inp: dict, n_len: int, flags: int = L.BKV_CAUSAL_RECENT,
+def run_evict_gpu(cfg: EvictConfig, inp: dict, n_len: int, flags: int | None = None,
                   rope: torch.Tensor | None = None) -> dict:
     """bkv_evict on device copies of inp; returns the outputs (device tensors)."""
     d = {k: v.clone() for k, v in inp.items()}
@@ -84,13 +87,13 @@ def run_evict_gpu(cfg: EvictConfig, inp: dict, n_len: int, flags: int = L.BKV_CA
     return d
 
 
-def compare_evict(cfg: EvictConfig, inp: dict, out: dict, n_len: int, units=None, causal: int = 1,
+def compare_evict(cfg: EvictConfig, inp: dict, out: dict, n_len: int, units=None, flags: int | None = None,
                   where: str = "") -> dict:
     """Oracle on the listed units (default all) vs the GPU outputs."""
     U = cfg.units
     units = list(range(U)) if units is None else list(units)
     v = synth.oracle_views(cfg, inp, units)
-    oc = ocfg(cfg, n_len=inp["K"].shape[-2], causal=causal)
+    oc = ocfg(cfg, n_len=inp["K"].shape[-2], flags=flags)
     K0, V0 = v["K"].copy(), v["V"].copy()
     o = O.evict(oc, v["K"], v["V"], v["qbuf"], v["qcount"], v["q_recent"], v["pos_recent"], v["t"],
                 n_len=n_len)

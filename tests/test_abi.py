@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strerror(so):
-    assert L.version() == 2
+    assert L.version() == 3
     for code in (0, -1, -2, -3, -4):
         assert len(L.strerror(code)) > 0
     assert L.strerror(-99) == "unknown error"

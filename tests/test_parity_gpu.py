@@ -15,8 +15,8 @@ import torch
 import oracle as O
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import (QWEN3_4B, QWEN3_14B_1K, QWEN3_14B_4K, R1_QWEN_7B, TINY,
-                                               EvictConfig)
+from long_reasoning_decode_amd.configs import (QWEN3_4B, QWEN3_4B_MEAN, QWEN3_14B_1K, QWEN3_14B_4K, R1_QWEN_7B,
+                                               TINY, EvictConfig)
 
 import _helpers as H
 
@@ -148,25 +148,39 @@ SCORE_CASES = [
     (TINY.scaled(n_recent_q=0, name="nrq0"), 160, 1),
     (TINY.scaled(n_beacon=0, name="nb0"), 160, 1),
     (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 1),
+    (TINY, 10, 1),                  # fewer keys than recent queries: recent rows 0-5 see nothing
+    # mean pooling (flags 3: causal + mean, 2: mean alone) on every workgroup layout
+    (TINY, None, 3),
+    (TINY, 10, 3),
+    (TINY, 160, 2),
+    (QWEN3_4B.scaled(n_layers=2, batch=2), None, 3),
+    (R1_QWEN_7B.scaled(n_layers=1, batch=2), None, 3),
+    (TINY.scaled(hq=3, hkv=3, name="g1"), 33, 3),
+    (TINY.scaled(hq=6, hkv=2, name="g3"), 159, 3),
+    (TINY.scaled(hq=8, hkv=1, name="g8"), 150, 2),
+    (TINY.scaled(d=128, hq=5, hkv=1, name="g5d128"), 160, 3),
+    (TINY.scaled(n_recent_q=0, name="nrq0"), 160, 3),
+    (TINY.scaled(n_beacon=0, name="nb0"), 160, 3),
+    (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 3),
 ]
 
 
-@pytest.mark.parametrize("cfg,n_len,causal", SCORE_CASES,
+@pytest.mark.parametrize("cfg,n_len,flags", SCORE_CASES,
                          ids=[f"{c.name}-{n}-{z}" for c, n, z in SCORE_CASES])
-def test_score_matches_oracle(cfg, n_len, causal):
+def test_score_matches_oracle(cfg, n_len, flags):
     N = cfg.n_len if n_len is None else n_len
-    _flush(f"score {cfg.name} N={N} causal={causal}")
+    _flush(f"score {cfg.name} N={N} flags={flags}")
     inp = synth.make_evict_inputs(cfg, device="cuda")
     qc = inp["qcount"]
     qc.view(-1)[::3] = 5     # some buffers hold fewer beacons
     qc.view(-1)[1::7] = 0
-    shape = L.shape_of(cfg, cap=cfg.n_len, flags=causal)
+    shape = L.shape_of(cfg, cap=cfg.n_len, flags=flags)
     scores = torch.empty((cfg.units, N), dtype=torch.float32, device="cuda")
     L.score(shape, inp["K"], N, inp["qbuf"], qc, inp["q_recent"], inp["pos_recent"], inp["t"],
             H.rope_dev(cfg), scores)
     torch.cuda.synchronize()
     v = synth.oracle_views(cfg, inp)
-    o = O.score(H.ocfg(cfg, n_len=cfg.n_len, causal=causal), v["K"], v["qbuf"], v["qcount"], v["q_recent"],
+    o = O.score(H.ocfg(cfg, n_len=cfg.n_len, flags=flags), v["K"], v["qbuf"], v["qcount"], v["q_recent"],
                 v["pos_recent"], v["t"], n_len=N)
     H.check_scores(scores.cpu().numpy(), o, f"{cfg.name} N={N}")
 
@@ -263,21 +277,33 @@ EVICT_CASES = [
     (TINY.scaled(n_beacon=0, name="nb0"), 160, 1),
     # the longest cache the kernels take (8192 keys)
     (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 1),
+    # mean pooling (flags 3: causal + mean, 2: mean alone)
+    (TINY, None, 3),
+    (TINY, 150, 2),
+    (QWEN3_4B.scaled(n_layers=2, batch=2), None, 3),
+    (R1_QWEN_7B.scaled(n_layers=1, batch=2), None, 3),
+    (QWEN3_14B_1K.scaled(n_layers=1, batch=2), None, 3),
+    (TINY.scaled(hq=3, hkv=3, name="g1"), 160, 3),
+    (TINY.scaled(hq=6, hkv=2, name="g3"), 159, 3),
+    (TINY.scaled(hq=6, hkv=1, name="g6"), 140, 2),
+    (TINY.scaled(d=128, hq=5, hkv=1, name="g5d128"), 160, 3),
+    (TINY.scaled(n_beacon=0, name="nb0"), 160, 3),
+    (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 3),
 ]
 
 
-@pytest.mark.parametrize("cfg,n_len,causal", EVICT_CASES, ids=[f"{c.name}-{n}-{z}" for c, n, z in EVICT_CASES])
-def test_evict_matches_oracle(cfg, n_len, causal):
+@pytest.mark.parametrize("cfg,n_len,flags", EVICT_CASES, ids=[f"{c.name}-{n}-{z}" for c, n, z in EVICT_CASES])
+def test_evict_matches_oracle(cfg, n_len, flags):
     N = cfg.n_len if n_len is None else n_len
-    _flush(f"evict {cfg.name} N={N} causal={causal}")
+    _flush(f"evict {cfg.name} N={N} flags={flags}")
     inp = synth.make_evict_inputs(cfg, device="cuda")
     inp["qcount"].view(-1)[::5] = 7
-    out = H.run_evict_gpu(cfg, inp, N, flags=causal)
-    r = H.compare_evict(cfg, inp, out, N, causal=causal, where=f"{cfg.name} N={N}")
+    out = H.run_evict_gpu(cfg, inp, N, flags=flags)
+    r = H.compare_evict(cfg, inp, out, N, flags=flags, where=f"{cfg.name} N={N}")
     _flush(f"  tie-band differences: {r['n_tie_diff']}")
 
 
-FULL = [QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, QWEN3_14B_4K]
+FULL = [QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, QWEN3_14B_4K, QWEN3_4B_MEAN]
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
@@ -312,7 +338,8 @@ def test_evict_rejects_bad_shapes_without_launching():
     assert e.value.code == -3
 
 
-@pytest.mark.parametrize("cfg", [TINY, QWEN3_4B.scaled(n_layers=2, batch=2), R1_QWEN_7B.scaled(n_layers=1, batch=2)],
+@pytest.mark.parametrize("cfg", [TINY, QWEN3_4B.scaled(n_layers=2, batch=2), R1_QWEN_7B.scaled(n_layers=1, batch=2),
+                                 QWEN3_4B_MEAN.scaled(n_layers=2, batch=2), TINY.scaled(name="tiny-mean", pool="mean")],
                          ids=lambda c: c.name)
 def test_evict_equals_the_separate_calls(cfg):
     """bkv_evict (one fused kernel per unit, then the merge) gives bit for bit what bkv_score, bkv_select,

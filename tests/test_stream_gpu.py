@@ -8,7 +8,7 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import STREAM, TINY_STREAM, TINY_STREAM_1R31B
+from long_reasoning_decode_amd.configs import STREAM, TINY_STREAM, TINY_STREAM_1R31B, TINY_STREAM_MEAN
 from long_reasoning_decode_amd.stream import StreamRun
 
 from _stream_helpers import compare_stream, replay
@@ -70,6 +70,15 @@ def test_stream_tiny_one_recent_31_beacons():
     run.run()
     assert run.fps_rounds_per_buffer() > 0.8 * scfg.steps   # nearly every step samples
     _check(scfg, run, units, "stream-tiny 1r31b")
+
+
+def test_stream_tiny_mean_pooling():
+    """The whole cycle with mean pooling of the weights."""
+    scfg = TINY_STREAM_MEAN
+    units = range(scfg.base.units)
+    run = StreamRun(scfg, record_units=units, block=64)
+    run.run()
+    _check(scfg, run, units, "stream-tiny mean")
 
 
 def test_stream_checkpoint_resume(tmp_path):

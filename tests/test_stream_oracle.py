@@ -9,7 +9,7 @@ import pytest
 
 import oracle as O
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import TINY_STREAM, TINY_STREAM_1R31B
+from long_reasoning_decode_amd.configs import TINY_STREAM, TINY_STREAM_1R31B, TINY_STREAM_MEAN
 
 from _stream_helpers import empty_state, replay, stream_ocfg
 
@@ -26,7 +26,7 @@ def _inputs(scfg, S, seed=None):
             "pos": np.ascontiguousarray(blk["pos"].numpy()[:, b_of]).astype(np.int32)}
 
 
-@pytest.mark.parametrize("scfg", [TINY_STREAM, TINY_STREAM_1R31B], ids=lambda c: c.name)
+@pytest.mark.parametrize("scfg", [TINY_STREAM, TINY_STREAM_1R31B, TINY_STREAM_MEAN], ids=lambda c: c.name)
 def test_stream_equals_composition_of_calls(scfg):
     b = scfg.base
     S = 260    # first eviction after 160 steps, then every 32
