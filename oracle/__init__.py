@@ -80,6 +80,11 @@ def lib():
         L.bkvo_fps_f64.argtypes = [P, i32, i32, i32, P, P]
         L.bkvo_fps_f64.restype = i32
         L.bkvo_fps_update.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
+        L.bkvo_fps_long.argtypes = [P, i32, i32, i32, P]
+        L.bkvo_fps_long.restype = i32
+        L.bkvo_pairwise_sum.argtypes = [P, i32]
+        L.bkvo_pairwise_sum.restype = C.c_float
+        L.bkvo_prefill.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
         L.bkvo_row_weights.argtypes = [P, P, i32, i32, i32, P]
         L.bkvo_row_weights.restype = C.c_double
         L.bkvo_select.argtypes = [P, i32, i32, i32, i32, P]
@@ -162,6 +167,33 @@ def fps_f64(X, m: int):
     mar = np.empty(max(n, 1), dtype=np.float64)
     got = lib().bkvo_fps_f64(_p(X), n, d, m, _p(sel), _p(mar))
     return sel[:got].tolist(), mar[:got].copy()
+
+
+def fps_long(X, m: int) -> list[int]:
+    """FPS of many rows with the O(n d) seed (the prefill variant)."""
+    X = _u16(X)
+    n, d = X.shape
+    sel = np.empty(max(n, 1), dtype=np.int32)
+    got = lib().bkvo_fps_long(_p(X), n, d, m, _p(sel))
+    return sel[:got].tolist()
+
+
+def pairwise_sum(x) -> float:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return float(np.float32(lib().bkvo_pairwise_sum(_p(x), x.size)))
+
+
+def prefill(q_prompt, qbuf, qcount, n_beacon: int) -> np.ndarray:
+    """Prefill initialisation, in place on qbuf [nbuf, qcap, d] and qcount [nbuf] from q_prompt [nbuf, P, d];
+    returns the selection order [nbuf, n_beacon] (-1 past the last pick)."""
+    assert qbuf.dtype == np.uint16 and qbuf.flags["C_CONTIGUOUS"]
+    assert qcount.dtype == np.int32 and qcount.flags["C_CONTIGUOUS"]
+    q_prompt = _u16(q_prompt)
+    nbuf, P, d = q_prompt.shape
+    assert qbuf.shape[0] == nbuf and qbuf.shape[2] == d and qcount.shape == (nbuf,)
+    sel = np.empty((nbuf, n_beacon), dtype=np.int32)
+    lib().bkvo_prefill(nbuf, P, d, n_beacon, qbuf.shape[1], _p(q_prompt), _p(qbuf), _p(qcount), _p(sel))
+    return sel
 
 
 def fps_update(qbuf, qcount, q_new, n_beacon: int, n_recent_q: int) -> np.ndarray:

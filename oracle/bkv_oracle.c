@@ -11,7 +11,7 @@
  * "Summary" means the rcap.io post "BeaconKV: Key-Value Cache Compression
  * Guided by Beacon Queries"):
  *   Notes §2.1, Eq. 4-6     attention weights w_{tau,j}, max and mean pooling
- *   Notes §2.2, App. Alg. 1 farthest point sampling (FPS)
+ *   Notes §2.2, App. Alg. 1 farthest point sampling (FPS), and its prefill use
  *   Notes §2.2, Eq. 9       continual FPS buffer bounds B_Q^min / B_Q^max
  *   Notes §2.2, App. Alg. 2 cycle: freeze beacons, collect recents, evict,
  *                           merge beacons + recents by FPS
@@ -276,6 +276,129 @@ int bkvo_fps_f64(const uint16_t *X, int n, int d, int m, int *sel, double *margi
     }
     free(x); free(cs); free(nrm); free(S); free(taken); free(a);
     return cnt;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FPS over a long query set: the prefill initialisation (Notes §2.2: at
+ * prefill the first representatives are sampled from the prompt's queries,
+ * with the steps of App. Alg. 1).  The steps and fp32 operations are those of
+ * bkvo_fps except the seed.  With n in the thousands the n x n mean cosines
+ * cost O(n^2 d); they are taken instead from the identity
+ *   a_i = (1/n) sum_j cos(q_i, q_j) = (1/n) u_i . sum_j u_j,  u_j = q_j / |q_j|,
+ * which holds exactly in real arithmetic (cos is the dot product of the unit
+ * rows; a zero row has u = 0, matching cos = 0).  fp32, fixed order:
+ *   nrm_j  = sqrtf(fmaf chain of q_j . q_j over k ascending, from +0);
+ *   inv_j  = 1 / nrm_j, or 0 when nrm_j is 0;   u_j[k] = q_j[k] * inv_j;
+ *   s[k]   = pairwise sum of u_j[k] over j (pairwise_sum below);
+ *   a_i    = (fmaf chain of u_i[k] * s[k] over k ascending, from +0) / n;
+ * then p = argmin a_i and the S updates of bkvo_fps, with cos_ij =
+ * dot_ij / (nrm_i * nrm_j) computed from the bf16 rows as there.          */
+
+/* Pairwise (cascade) summation of x[lo .. lo + len), len a power of two:
+ * the sum of the left half plus the sum of the right half; terms at or
+ * beyond n are zero.  The result does not depend on how far the range is
+ * padded, since a zero subtree adds +0. */
+static float pairwise_sum(const float *x, size_t stride, int n, int lo, int len)
+{
+    if (lo >= n) return 0.0f;
+    if (len == 1) return x[(size_t)lo * stride];
+    int h = len / 2;
+    return pairwise_sum(x, stride, n, lo, h) + pairwise_sum(x, stride, n, lo + h, h);
+}
+
+/* Pairwise sum of x[0 .. n) (exported for its own pins). */
+float bkvo_pairwise_sum(const float *x, int n)
+{
+    int len = 1;
+    while (len < n) len *= 2;
+    return n > 0 ? pairwise_sum(x, 1, n, 0, len) : 0.0f;
+}
+
+int bkvo_fps_long(const uint16_t *X, int n, int d, int m, int *sel)
+{
+    if (n <= 0 || m <= 0) return 0;
+    if (n <= m) {
+        for (int i = 0; i < n; ++i) sel[i] = i;
+        return n;
+    }
+    float *x = (float *)malloc(sizeof(float) * (size_t)n * d);
+    float *u = (float *)malloc(sizeof(float) * (size_t)n * d);
+    float *nrm = (float *)malloc(sizeof(float) * (size_t)n);
+    float *ssum = (float *)malloc(sizeof(float) * (size_t)d);
+    float *S = (float *)malloc(sizeof(float) * (size_t)n);
+    char *taken = (char *)calloc((size_t)n, 1);
+    for (size_t i = 0; i < (size_t)n * d; ++i) x[i] = bf2f(X[i]);
+    for (int j = 0; j < n; ++j) {
+        float acc = 0.0f;
+        for (int k = 0; k < d; ++k) acc = fmaf(x[(size_t)j * d + k], x[(size_t)j * d + k], acc);
+        nrm[j] = sqrtf(acc);
+        float inv = nrm[j] == 0.0f ? 0.0f : 1.0f / nrm[j];
+        for (int k = 0; k < d; ++k) u[(size_t)j * d + k] = x[(size_t)j * d + k] * inv;
+    }
+    int len = 1;
+    while (len < n) len *= 2;
+    for (int k = 0; k < d; ++k) ssum[k] = pairwise_sum(u + k, (size_t)d, n, 0, len);
+    /* seed: lowest mean cosine */
+    int p = 0;
+    float best = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (int k = 0; k < d; ++k) acc = fmaf(u[(size_t)i * d + k], ssum[k], acc);
+        float a = acc / (float)n;
+        if (i == 0 || a < best) { best = a; p = i; }
+    }
+    int cnt = 0;
+    sel[cnt++] = p;
+    taken[p] = 1;
+    int r = p;
+    for (int j = 0; j < n; ++j) S[j] = -INFINITY;
+    while (cnt < m) {
+        /* fold in the cosines to the last pick, then take the farthest row */
+        for (int j = 0; j < n; ++j) {
+            float acc = 0.0f;
+            for (int k = 0; k < d; ++k) acc = fmaf(x[(size_t)j * d + k], x[(size_t)r * d + k], acc);
+            float c = (nrm[j] == 0.0f || nrm[r] == 0.0f) ? 0.0f : acc / (nrm[j] * nrm[r]);
+            if (c > S[j]) S[j] = c;
+        }
+        int nx = -1;
+        float bv = 0.0f;
+        for (int j = 0; j < n; ++j) {
+            if (taken[j]) continue;
+            if (nx < 0 || S[j] < bv) { nx = j; bv = S[j]; }
+        }
+        r = nx;
+        sel[cnt++] = r;
+        taken[r] = 1;
+    }
+    free(x); free(u); free(nrm); free(ssum); free(S); free(taken);
+    return cnt;
+}
+
+/* Prefill initialisation of nbuf query buffers: buffer b becomes
+ * FPS_long(q_prompt[b][0 .. P), n_beacon) with the survivors in ascending
+ * prompt order, qcount[b] their number (min(P, n_beacon)), and
+ * sel_out[b][i] (nullable) the i-th pick or -1 past the last.
+ * q_prompt: [nbuf][P][d]; qbuf: [nbuf][qcap][d]; qcount: [nbuf].           */
+void bkvo_prefill(int nbuf, int P, int d, int n_beacon, int qcap, const uint16_t *q_prompt,
+                  uint16_t *qbuf, int32_t *qcount, int32_t *sel_out)
+{
+    int *sel = (int *)malloc(sizeof(int) * (size_t)(n_beacon + 1));
+    char *keep = (char *)malloc((size_t)(P > 0 ? P : 1));
+    for (int b = 0; b < nbuf; ++b) {
+        const uint16_t *src = q_prompt + (size_t)b * P * d;
+        uint16_t *buf = qbuf + (size_t)b * qcap * d;
+        int got = bkvo_fps_long(src, P, d, n_beacon, sel);
+        if (sel_out)
+            for (int i = 0; i < n_beacon; ++i) sel_out[(size_t)b * n_beacon + i] = i < got ? sel[i] : -1;
+        memset(keep, 0, (size_t)(P > 0 ? P : 1));
+        for (int i = 0; i < got; ++i) keep[sel[i]] = 1;
+        int w = 0;
+        for (int i = 0; i < P; ++i)
+            if (keep[i]) { memcpy(buf + (size_t)w * d, src + (size_t)i * d, sizeof(uint16_t) * (size_t)d); ++w; }
+        qcount[b] = w;
+    }
+    free(sel);
+    free(keep);
 }
 
 /* ------------------------------------------------------------------------ */

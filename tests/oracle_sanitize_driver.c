@@ -79,6 +79,25 @@ static void run_case(int hq, int hkv, int d, int N, int budget, int npf, int nrk
     free(moved); free(sel); free(qn);
 }
 
+/* mean pooling, with and without the causal mask */
+static void c_mean_case(void)
+{
+    bkvo_cfg c;
+    memset(&c, 0, sizeof c);
+    c.n_layers = 1; c.batch = 1; c.hq = 4; c.hkv = 2; c.d = 64; c.cap = 20; c.budget = 12;
+    c.n_prefix = 2; c.n_recent_kv = 4; c.n_beacon = 3; c.n_recent_q = 4; c.qcap = 8; c.theta = 10000.0;
+    c.pool_mean = 1;
+    uint16_t K[2 * 20 * 64], qb[4 * 8 * 64], qr[4 * 4 * 64];
+    int32_t qc[4] = {3, 1, 0, 5}, pos[2 * 4] = {1, 2, 3, 4, 5, 6, 7, 8}, t[2] = {9, 10};
+    double sc[2 * 20];
+    fill_bf16(K, sizeof K / 2, 2.0f); fill_bf16(qb, sizeof qb / 2, 2.0f); fill_bf16(qr, sizeof qr / 2, 2.0f);
+    for (int causal = 0; causal < 2; ++causal) {
+        c.causal = causal;
+        bkvo_score(&c, 2, 20, K, qb, qc, qr, pos, t, sc, 2);
+        bkvo_score(&c, 2, 2, K, qb, qc, qr, pos, t, sc, 1);
+    }
+}
+
 int main(void)
 {
     float cs[64 * 2];
@@ -100,6 +119,19 @@ int main(void)
     run_case(2, 1, 64, 70, 40, 4, 8, 16, 0, 90);
     run_case(2, 1, 64, 70, 40, 4, 8, 0, 16, 0);
     run_case(2, 2, 64, 48, 40, 2, 4, 31, 1, 120);
+    c_mean_case();
+    /* prefill sampling: empty, shorter than the buffer, long */
+    for (int P = 0; P <= 300; P += 150) {
+        int P1 = P == 150 ? 9 : P;
+        uint16_t *qp = malloc((size_t)3 * (P1 > 0 ? P1 : 1) * 64 * 2), *qb = malloc((size_t)3 * 32 * 64 * 2);
+        int32_t qcnt[3], sl[3 * 16];
+        fill_bf16(qp, (size_t)3 * (P1 > 0 ? P1 : 1) * 64, 2.0f);
+        bkvo_prefill(3, P1, 64, 16, 32, qp, qb, qcnt, sl);
+        free(qp); free(qb);
+    }
+    float ps[5] = {1.0f, 2.0f, 3.0f, 4.0f, 5.0f};
+    bkvo_pairwise_sum(ps, 5);
+    bkvo_pairwise_sum(ps, 0);
     printf("ok\n");
     return 0;
 }

@@ -228,6 +228,99 @@ def test_fps_small_n_returns_all():
     assert O.fps(X, 9) == [0, 1, 2, 3, 4]
 
 
+# --------------------------------------------------------------------------
+# FPS over a long query set (prefill initialisation, Notes §2.2).
+
+def test_pairwise_sum_order_and_bounds():
+    # hand-derived: pairwise ((1 + 2^-24) + (2^-24 + 2^-24)); 1 + 2^-24 is a tie that rounds to even (1),
+    # 2^-24 + 2^-24 = 2^-23 exactly, 1 + 2^-23 is representable.  Left to right gives 1.
+    x = np.array([1.0, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24], np.float32)
+    assert O.pairwise_sum(x) == 1.0 + 2.0 ** -23
+    assert np.float32(np.float32(np.float32(x[0] + x[1]) + x[2]) + x[3]) == 1.0
+    rng = np.random.default_rng(30)
+    for n in (1, 2, 3, 7, 64, 100, 513, 4096):
+        ints = rng.integers(-1000, 1000, size=n).astype(np.float32)
+        assert O.pairwise_sum(ints) == float(ints.astype(np.int64).sum())    # exact on small integers
+        v = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3, size=n)).astype(np.float32)
+        exact = math.fsum(v.astype(np.float64))
+        bound = max(1, math.ceil(math.log2(n))) * 2.0 ** -24 * float(np.abs(v).astype(np.float64).sum())
+        assert abs(O.pairwise_sum(v) - exact) <= bound * 1.0001
+        # padding with zeros to any length leaves the sum bit-identical
+        assert O.pairwise_sum(np.concatenate([v, np.zeros(n + 5, np.float32)])) == O.pairwise_sum(v)
+
+
+@pytest.mark.parametrize("case", _read_fps_cases(), ids=lambda c: c["name"])
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_fps_long_hand_cases(case, d):
+    assert O.fps_long(rows(case["rows"], d), case["m"]) == case["order"]
+
+
+def test_fps_long_brute_force():
+    """The O(n d) seed gives the FPS of the definition (fp64 brute force) away from near-ties."""
+    rng = np.random.default_rng(31)
+    checked = 0
+    for trial in range(60):
+        n = int(rng.integers(33, 400))
+        d = int(rng.choice([8, 64, 128]))
+        m = int(rng.integers(1, 20))
+        X = bf16(rng.standard_normal((n, d)) * rng.uniform(0.1, 10))
+        ref, margin = _fps_brute(X, m)
+        if margin < 1e-5:
+            continue
+        assert O.fps_long(X, m) == ref, (trial, n, d, m)
+        checked += 1
+    assert checked > 30
+
+
+def test_fps_long_equals_buffer_fps_away_from_ties():
+    rng = np.random.default_rng(32)
+    checked = 0
+    for trial in range(200):
+        n = int(rng.integers(5, 33))
+        d = int(rng.choice([8, 64, 128]))
+        m = int(rng.integers(1, n))
+        X = bf16(rng.standard_normal((n, d)))
+        _, margins = O.fps_f64(X, m)
+        if margins.min() < 1e-5:
+            continue
+        assert O.fps_long(X, m) == O.fps(X, m)
+        checked += 1
+    assert checked > 150
+
+
+def test_fps_long_scaling_clusters_and_duplicates():
+    rng = np.random.default_rng(33)
+    n, d, m = 700, 128, 16
+    X = bf16(rng.standard_normal((n, d)))
+    sel = O.fps_long(X, m)
+    sc = 2.0 ** rng.integers(-6, 7, size=(n, 1))
+    assert O.fps_long(bf16(f32(X) * sc), m) == sel      # unit rows and cosines are bit-identical
+    Xd = X.copy()
+    Xd[sel[3]] = Xd[sel[5]]
+    assert len(set(O.fps_long(Xd, m))) == m
+    # eight tight clusters along orthogonal axes: the first eight picks cover all of them
+    lab = rng.integers(0, 8, size=n)
+    Xc = bf16(np.eye(d)[lab] * 8 + 0.05 * rng.standard_normal((n, d)))
+    assert sorted(lab[O.fps_long(Xc, 8)].tolist()) == list(range(8))
+
+
+def test_prefill_buffers():
+    rng = np.random.default_rng(34)
+    nb, d, qcap = 16, 64, 32
+    for P in (0, 5, 16, 17, 300):
+        q = bf16(rng.standard_normal((3, P, d)))
+        qbuf = np.zeros((3, qcap, d), np.uint16)
+        qc = np.full(3, 99, np.int32)
+        sel = O.prefill(q, qbuf, qc, nb)
+        for b in range(3):
+            ref = O.fps_long(q[b], nb) if P else []
+            assert sel[b, :len(ref)].tolist() == ref and np.all(sel[b, len(ref):] == -1)
+            assert qc[b] == min(P, nb)
+            assert np.array_equal(qbuf[b, :qc[b]], q[b][sorted(ref)])
+            if P <= nb:
+                assert ref == list(range(P))
+
+
 def test_fps_update_continual_buffer():
     """Eq. 9: append; at B_Q^max rows the buffer becomes FPS(buffer, n_beacon)
     in ascending slot order with count n_beacon; below it, only the append."""
