@@ -27,10 +27,14 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import EVICT_CONFIGS, QWEN3_4B, STREAM, STREAM_CONFIGS
+from long_reasoning_decode_amd.configs import (EVICT_CONFIGS, PREFILL, PREFILL_CONFIGS, QWEN3_4B, STREAM,
+                                               STREAM_CONFIGS)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+# fp32 multiply-add issue rate without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz.  The
+# packed-math figure (157.3 TFLOP/s) needs v_pk_fma_f32, which these kernels are built without.
+FP32_VALU_PEAK_TFS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 METRIC = "eviction steps/s (all layers x KV heads) at Qwen3-4B shape; % of HBM peak"
 # kernel -> the .hip file it is compiled from; its stored counters hold only while that file, everything it
 # includes and the build flags are unchanged
@@ -199,6 +203,81 @@ def stream_bench(args) -> int:
     return 0
 
 
+def prefill_flops_per_row(d: int, m: int) -> int:
+    """Algorithmic fp32 flops per prompt row of the prefill sampling: norm (d multiply-adds), unit row (d
+    products), column sum (d adds), mean cosine (d multiply-adds), and m - 1 cosine updates (d multiply-adds
+    each), a multiply-add counting 2."""
+    return (2 + 1 + 1 + 2 + 2 * (m - 1)) * d
+
+
+def prefill_cpu_baseline(cfg, q: torch.Tensor, target_s: float) -> dict:
+    """The CPU oracle's prefill sampling on a bounded sample of buffers."""
+    import oracle as O
+    b, P = cfg.base, cfg.n_prompt
+    qn = q.reshape(b.qbufs, P, b.d)
+    n, dt = 8, 0.0
+    while True:
+        x = synth.to_u16(qn[:n])
+        qbuf = np.zeros((n, b.qcap, b.d), np.uint16)
+        qc = np.zeros(n, np.int32)
+        t0 = time.perf_counter()
+        O.prefill(x, qbuf, qc, b.n_beacon)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= b.qbufs:
+            break
+        n = min(b.qbufs, max(n + 8, int(n * target_s / max(dt, 1e-3) * 1.05)))
+    return {"value": n / dt / b.qbufs, "unit": "prefill initialisations/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {b.qbufs} buffers of the same workload, {dt:.1f} s on one thread; scaled to whole "
+                      f"initialisations"}
+
+
+def prefill_bench(args) -> int:
+    """Prefill initialisation of every query buffer (bkv_fps_prefill) on the model-shaped batch."""
+    pc = PREFILL_CONFIGS[args.prefill_config]
+    b, P = pc.base, pc.n_prompt
+    torch.cuda.set_device(0)
+    L.load()
+    print(f"# prefill {pc.name}: {b.qbufs} buffers x {P} prompt queries", file=sys.stderr, flush=True)
+    q = synth.make_prompt_queries(b, P, device="cuda")
+    shape = L.shape_of(b)
+    qbuf = torch.empty((b.qbufs, b.qcap, b.d), dtype=torch.bfloat16, device="cuda")
+    qc = torch.empty((b.qbufs,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        L.fps_prefill(shape, q, P, qbuf, qc, None, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        L.fps_prefill(shape, q, P, qbuf, qc, None, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = float(b.qbufs) * P * prefill_flops_per_row(b.d, b.n_beacon)
+    q_bytes = float(b.qbufs) * P * b.d * 2
+    ach = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "prefill initialisations/s (FPS of every query head's prompt queries to its beacons)",
+        "value": 1000.0 / ms, "unit": "prefill initialisations/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{pc.name}: {b.n_layers} layers x batch {b.batch} x {b.hq} query heads "
+                               f"({b.qbufs} buffers), {P} prompt queries each, head_dim {b.d}, "
+                               f"{b.n_beacon} beacons kept", "buffers": b.qbufs, "n_prompt": P},
+        "roofline": {"bound": "alu", "kernel": "prefill_kernel", "achieved": ach, "peak": FP32_VALU_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": ach / FP32_VALU_PEAK_TFS, "traffic": None,
+                     "alg_flops_per_launch": flops},
+        "hbm": {"query_bytes": q_bytes, "achieved_GBs": q_bytes / (ms * 1e-3) / 1e9,
+                "frac": q_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "prompt_rows_per_s": float(b.qbufs) * P / (ms * 1e-3),
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = prefill_cpu_baseline(pc, q, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +294,10 @@ def main() -> int:
                          "(bkv_decode_step every step, bkv_evict when the cache is full) and print its own line")
     ap.add_argument("--stream-config", default=STREAM.name, choices=sorted(STREAM_CONFIGS))
     ap.add_argument("--stream-steps", type=int, default=0, help="decode steps (default: the config's)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the eviction-step benchmark, time the prefill initialisation of every query "
+                         "buffer (bkv_fps_prefill) and print its own line")
+    ap.add_argument("--prefill-config", default=PREFILL.name, choices=sorted(PREFILL_CONFIGS))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: print per-kernel HBM bytes from two rocprofv3 --pmc runs of this script "
                          "(FETCH_SIZE, then WRITE_SIZE, --output-format csv) made with --copy-calibration-mib")
@@ -234,6 +317,8 @@ def main() -> int:
         return 2
     if args.stream:
         return stream_bench(args)
+    if args.prefill:
+        return prefill_bench(args)
     cfg = EVICT_CONFIGS[args.config]
     torch.cuda.set_device(0)
     L.load()

@@ -113,6 +113,27 @@ int bkv_rope_table(double theta, int32_t head_dim, int32_t p0, int32_t p1, float
 int bkv_fps_update(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
                    const bkv_bf16 *q_new, int32_t *fps_sel, void *stream);
 
+/* Longest prompt bkv_fps_prefill takes. */
+#define BKV_PREFILL_MAX 8192
+
+/* Prefill initialisation of the query buffers (Notes §2.2: at prefill the
+ * first representatives are sampled from the prompt's queries, by the FPS of
+ * App. Alg. 1).  For every buffer uq, q_prompt[uq][0 : n_prompt) holds the
+ * head's pre-RoPE prompt queries (bf16 [qbufs][n_prompt][head_dim]); the
+ * buffer becomes FPS(prompt, n_beacon), survivors in ascending prompt order,
+ * and qcount[uq] their number, min(n_prompt, n_beacon).  fps_sel (nullable)
+ * receives the selection order, -1 past the last pick.
+ * The FPS is that of bkv_fps_update except the seed: the mean cosine of row i
+ * is computed as u_i . s / n with u_j = q_j * (1 / |q_j|) (0 for a zero row)
+ * and s[k] the pairwise sum of u_j[k] over j (a balanced binary tree over the
+ * row index, zero rows padding it to a power of two), which costs O(n d)
+ * instead of O(n^2 d); the fma chains, norms, cosines, argmins and ties are
+ * as in bkv_fps_update.  Inputs must be finite with finite squared norms.
+ * Errors: BKV_EINVAL (null or misaligned pointer, n_prompt < 0),
+ * BKV_EUNSUPPORTED (n_prompt > BKV_PREFILL_MAX). */
+int bkv_fps_prefill(const bkv_shape *shape, const bkv_bf16 *q_prompt, int32_t n_prompt,
+                    bkv_bf16 *qbuf, int32_t *qcount, int32_t *fps_sel, void *stream);
+
 /* Scores of every cached key (Notes §2.1 Eq. 4-5, §2.3 Eq. 7).  Per unit,
  * the observation rows of each of its G query heads are the beacons
  * qbuf[uq][0 : min(qcount, n_beacon)) rotated to t[b] and the recent queries

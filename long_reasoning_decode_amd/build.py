@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbkv.so")
-SOURCES = ["bkv_api.hip", "bkv_fps.hip", "bkv_score.hip", "bkv_select.hip", "bkv_compact.hip", "bkv_stream.hip", "bkv_evict.hip"]
+SOURCES = ["bkv_api.hip", "bkv_fps.hip", "bkv_score.hip", "bkv_select.hip", "bkv_compact.hip", "bkv_stream.hip",
+           "bkv_evict.hip", "bkv_prefill.hip"]
 
 
 def hipcc() -> str:

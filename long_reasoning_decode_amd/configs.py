@@ -95,6 +95,22 @@ EVICT_CONFIGS = {c.name: c for c in (TINY, QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, Q
 
 
 @dataclass(frozen=True)
+class PrefillConfig:
+    """Prefill initialisation of every query buffer of a model-shaped batch: FPS of each query head's
+    n_prompt pre-RoPE prompt queries down to n_beacon representatives (§2.2)."""
+    name: str
+    base: EvictConfig
+    n_prompt: int
+
+
+# a 1024-token prompt (the tasks' problem statements are a few hundred to about a thousand tokens)
+PREFILL = PrefillConfig("prefill-qwen3-4b", QWEN3_4B, 1024)
+# a 4096-token prompt: rows beyond the registers and LDS of a CU are re-read from memory
+PREFILL_4K = PrefillConfig("prefill-qwen3-4b-p4096", QWEN3_4B, 4096)
+PREFILL_CONFIGS = {c.name: c for c in (PREFILL, PREFILL_4K)}
+
+
+@dataclass(frozen=True)
 class StreamConfig:
     """Streaming decode from an empty cache: every step appends one token per
     sequence and routes its queries (buffer update or recent ring); the cache

@@ -162,6 +162,26 @@ int bkv_fps_merge(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const bkv
     return hip_status(bkv::launch_fps(a, s->head_dim, true, (hipStream_t)stream));
 }
 
+int bkv_fps_prefill(const bkv_shape* s, const bkv_bf16* q_prompt, int32_t n_prompt, bkv_bf16* qbuf,
+                    int32_t* qcount, int32_t* fps_sel, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (n_prompt < 0 || !qbuf || !qcount || (n_prompt > 0 && !q_prompt)) return BKV_EINVAL;
+    if (n_prompt > BKV_PREFILL_MAX) return BKV_EUNSUPPORTED;
+    if (!aligned16(qbuf) || (q_prompt && !aligned16(q_prompt)) || !aligned4(qcount)) return BKV_EINVAL;
+    if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
+    bkv::PrefillArgs a;
+    a.q = q_prompt;
+    a.qbuf = qbuf;
+    a.qcount = qcount;
+    a.fps_sel = fps_sel;
+    a.nbuf = qbufs_of(s);
+    a.P = n_prompt;
+    a.qcap = s->qcap;
+    a.n_beacon = s->n_beacon;
+    return hip_status(bkv::launch_prefill(a, s->head_dim, (hipStream_t)stream));
+}
+
 int bkv_score(const bkv_shape* s, const bkv_bf16* K, int32_t n_len, const bkv_bf16* qbuf,
               const int32_t* qcount, const bkv_bf16* q_recent, const int32_t* pos_recent, const int32_t* t,
               const float* rope_cs, int32_t rope_rows, float* scores, void* stream) {

@@ -17,6 +17,15 @@ struct FpsArgs {
     int nbuf, qcap, n_beacon, n_recent_q;
 };
 
+struct PrefillArgs {
+    const bkv_bf16* q;         // [nbuf][P][d] prompt queries
+    bkv_bf16* qbuf;            // [nbuf][qcap][d]
+    int32_t* qcount;           // [nbuf]
+    int32_t* fps_sel;          // [nbuf][n_beacon] or null
+    int nbuf, P, qcap, n_beacon;
+    int lds_bytes;             // LDS a workgroup may take (set at launch)
+};
+
 struct ScoreArgs {
     const bkv_bf16* K;         // [units][cap][d]
     const bkv_bf16* qbuf;      // [qbufs][qcap][d]
@@ -69,6 +78,7 @@ struct RingArgs {
 };
 
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, int d, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 hipError_t launch_compact(const CompactArgs& a, int d, hipStream_t st);

@@ -1,0 +1,569 @@
+// bkv_prefill.hip -- prefill initialisation of the query buffers: farthest
+// point sampling of each query head's prompt queries down to n_beacon rows
+// (Notes §2.2: at prefill the first representatives are sampled from the
+// prompt's queries; the steps are those of App. Alg. 1).
+//
+// One 512-thread workgroup per buffer (one per CU: eight waves of up to 256
+// VGPRs); thread tid owns rows j = c * 512 + tid (chunk c).  The rows of the
+// first 128 / d chunks stay in registers as packed bf16 (64 VGPRs); the next
+// ones stay in LDS (bf16, swizzled so that a wave's row reads are
+// conflict-free), up to the 160 KB a CU has; rows beyond that (prompts of
+// several thousand queries) are re-read from global memory on every pass.
+// The norms and S values of rows outside the registers live in LDS.
+//
+// Arithmetic, in one fixed fp32 order (bit-identical selections):
+//   nrm_j = sqrt(fma chain of x_j . x_j over k ascending, from +0);
+//   inv_j = 1 / nrm_j (0 if nrm_j is 0), u_j[k] = x_j[k] * inv_j;
+//   s[k]  = pairwise sum of u_j[k] over j: a balanced binary tree over the
+//           row index, padded with zero rows to a power of two.  Lanes form
+//           the low six levels (DPP), waves the next three (LDS), chunks
+//           the rest;
+//   a_j   = (fma chain of u_j[k] * s[k]) / P, the mean cosine of row j to all
+//           rows (cos is the dot product of unit rows), seed p = argmin a;
+//   then n_beacon - 1 steps: S_j = max(S_j, cos(x_j, x_r)) for the last pick
+//   r with cos = (fma chain of x_j . x_r) / (nrm_j * nrm_r) (0 if a norm is
+//   0), next pick = argmin of S over the rows not taken.
+// Every argmin takes the lowest row index among equal values.  The
+// survivors are written to the buffer in ascending prompt order.
+#include "bkv_device.hpp"
+#include "bkv_internal.hpp"
+
+namespace bkv {
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxChunks = BKV_PREFILL_MAX / kThreads;
+constexpr int kLdsBytes = 160 * 1024;   // LDS of one CU (the most a workgroup is given)
+
+template <int D>
+struct Pre {
+    static constexpr int kRegChunks = 128 / D;          // chunks of rows in registers (64 VGPRs)
+    static constexpr int kRegRows = kRegChunks * kThreads;
+    // LDS layout (bytes)
+    static constexpr int kXrOff = 0;                                 // float [2][D]   picked row
+    static constexpr int kXnOff = kXrOff + 2 * D * 4;                // float [2]      its norm
+    static constexpr int kWvOff = kXnOff + 16;                       // float [2][waves] wave minima
+    static constexpr int kWiOff = kWvOff + 2 * kWaves * 4;           // int   [2][waves]
+    static constexpr int kPartOff = kWiOff + 2 * kWaves * 4;         // float [waves][D] wave column sums
+    static constexpr int kCsumOff = kPartOff + kWaves * D * 4;       // float [chunks][D]
+    static constexpr int kSsumOff = kCsumOff + kMaxChunks * D * 4;   // float [D]
+    static constexpr int kSelOff = kSsumOff + D * 4;                 // int [32]
+    static constexpr int kOtherOff = kSelOff + 32 * 4;               // float nrm[n_other], S[n_other]; then rows
+    static constexpr int kRowBytes = 2 * D;
+    // rows outside the registers, and how many of them fit in LDS
+    __host__ __device__ static int n_other(int P) { return P > kRegRows ? P - kRegRows : 0; }
+    __host__ __device__ static int rows_off(int P) { return (kOtherOff + n_other(P) * 8 + 15) & ~15; }
+    __host__ __device__ static int n_lds_rows(int P, int lds_bytes) {
+        const int room = (lds_bytes - rows_off(P)) / kRowBytes;
+        return room < 0 ? 0 : (n_other(P) < room ? n_other(P) : room);
+    }
+    __host__ __device__ static size_t bytes(int P, int lds_bytes) {
+        return (size_t)rows_off(P) + (size_t)n_lds_rows(P, lds_bytes) * kRowBytes;
+    }
+};
+
+// Ends the work on one 8-element piece of a row: the accumulator must be
+// final here and no memory access moves across, so the compiler neither reads
+// the next pieces' fp32 operands early nor sinks the multiply-adds past the
+// loop (either keeps a whole fp32 row live and spills the resident rows).
+__device__ __forceinline__ void piece_fence(float& acc) { asm volatile("" : "+v"(acc)::"memory"); }
+
+// bf16 halves of a packed word.  The shift and the mask are made opaque
+// (fresh() at the top of every pass), so the compiler can neither hoist the
+// unpacking of the resident rows out of the loop over the greedy steps nor
+// share it between passes: either would keep a second, fp32 copy of the rows
+// in registers and spill.
+struct Bf {
+    uint32_t sh, mk;
+    static __device__ __forceinline__ Bf fresh() {
+        Bf u;
+        asm volatile("s_mov_b32 %0, 16" : "=s"(u.sh));
+        asm volatile("s_mov_b32 %0, 0xffff0000" : "=s"(u.mk));
+        return u;
+    }
+    __device__ __forceinline__ float lo(uint32_t w) const { return __uint_as_float(w << sh); }
+    __device__ __forceinline__ float hi(uint32_t w) const { return __uint_as_float(w & mk); }
+};
+
+template <int D>
+__device__ __forceinline__ void load_row(const bkv_bf16* Q, int P, int j, u32x4_t (&x)[D / 8]) {
+    if (j < P) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Q + (size_t)j * D);
+#pragma unroll
+        for (int p = 0; p < D / 8; ++p) x[p] = src[p];
+    } else {
+#pragma unroll
+        for (int p = 0; p < D / 8; ++p) x[p] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+}
+
+// fma chain over k ascending of x[k] * y[k], y fp32 in LDS (the same address
+// for every lane: broadcast reads)
+template <int D>
+__device__ __forceinline__ float dot_lds(const u32x4_t (&x)[D / 8], const float* y) {
+    const Bf u = Bf::fresh();
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+        const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(y + 8 * p);
+        const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(y + 8 * p + 4);
+        const u32x4_t w = x[p];
+        acc = __builtin_fmaf(u.lo(w[0]), y0[0], acc);
+        acc = __builtin_fmaf(u.hi(w[0]), y0[1], acc);
+        acc = __builtin_fmaf(u.lo(w[1]), y0[2], acc);
+        acc = __builtin_fmaf(u.hi(w[1]), y0[3], acc);
+        acc = __builtin_fmaf(u.lo(w[2]), y1[0], acc);
+        acc = __builtin_fmaf(u.hi(w[2]), y1[1], acc);
+        acc = __builtin_fmaf(u.lo(w[3]), y1[2], acc);
+        acc = __builtin_fmaf(u.hi(w[3]), y1[3], acc);
+        piece_fence(acc);
+    }
+    return acc;
+}
+
+// The same for the RC resident rows at once, so that each 8-float piece of y
+// is read once and used by every row while it is live.
+template <int D, int RC>
+__device__ __forceinline__ void dots_lds(const u32x4_t (&x)[RC][D / 8], const float* y, float (&acc)[RC]) {
+    const Bf u = Bf::fresh();
+#pragma unroll
+    for (int c = 0; c < RC; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+        const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(y + 8 * p);
+        const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(y + 8 * p + 4);
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            const u32x4_t w = x[c][p];
+            float a = acc[c];
+            a = __builtin_fmaf(u.lo(w[0]), y0[0], a);
+            a = __builtin_fmaf(u.hi(w[0]), y0[1], a);
+            a = __builtin_fmaf(u.lo(w[1]), y0[2], a);
+            a = __builtin_fmaf(u.hi(w[1]), y0[3], a);
+            a = __builtin_fmaf(u.lo(w[2]), y1[0], a);
+            a = __builtin_fmaf(u.hi(w[2]), y1[1], a);
+            a = __builtin_fmaf(u.lo(w[3]), y1[2], a);
+            a = __builtin_fmaf(u.hi(w[3]), y1[3], a);
+            piece_fence(a);
+            acc[c] = a;
+        }
+    }
+}
+
+// Mean cosines (fma chain of u[k] * s[k], then / P) of the RC resident rows.
+template <int D, int RC>
+__device__ __forceinline__ void mean_cos_rows(const u32x4_t (&x)[RC][D / 8], const float (&inv)[RC],
+                                              const float* ssum, float fP, float (&out)[RC]) {
+    const Bf u = Bf::fresh();
+    float acc[RC];
+#pragma unroll
+    for (int c = 0; c < RC; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p);
+        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p + 4);
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            const u32x4_t w = x[c][p];
+            const float iv = inv[c];
+            float a = acc[c];
+            a = __builtin_fmaf(u.lo(w[0]) * iv, s0[0], a);
+            a = __builtin_fmaf(u.hi(w[0]) * iv, s0[1], a);
+            a = __builtin_fmaf(u.lo(w[1]) * iv, s0[2], a);
+            a = __builtin_fmaf(u.hi(w[1]) * iv, s0[3], a);
+            a = __builtin_fmaf(u.lo(w[2]) * iv, s1[0], a);
+            a = __builtin_fmaf(u.hi(w[2]) * iv, s1[1], a);
+            a = __builtin_fmaf(u.lo(w[3]) * iv, s1[2], a);
+            a = __builtin_fmaf(u.hi(w[3]) * iv, s1[3], a);
+            piece_fence(a);
+            acc[c] = a;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < RC; ++c) out[c] = acc[c] / fP;
+}
+
+template <int D>
+__device__ __forceinline__ float norm_of(const u32x4_t (&x)[D / 8]) {
+    const Bf u = Bf::fresh();
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = u.lo(x[p][e]), b = u.hi(x[p][e]);
+            acc = __builtin_fmaf(a, a, acc);
+            acc = __builtin_fmaf(b, b, acc);
+        }
+    }
+    return __builtin_sqrtf(acc);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+// Pairwise sum over the 64 lanes: lane pairs (2i, 2i+1), then blocks of 4, 8,
+// 16 inside each 16-lane row, then rows (0 + 1) and (2 + 3), then the two
+// halves.  Lanes 48..63 receive the total.
+__device__ __forceinline__ float wave_pairwise_sum(float v) {
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+__device__ __forceinline__ bool less_vi(float v2, int i2, float v, int i) {
+    return v2 < v || (v2 == v && i2 < i);
+}
+
+// Workgroup argmin of (v, i); every thread gets the winning index.
+__device__ __forceinline__ int block_argmin(float v, int i, float* wv, int* wi, int wave, int lane) {
+    wave_argmin(v, i);
+    if (lane == 0) {
+        wv[wave] = v;
+        wi[wave] = i;
+    }
+    __syncthreads();
+    float bv = wv[0];
+    int bi = wi[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        if (less_vi(wv[w], wi[w], bv, bi)) {
+            bv = wv[w];
+            bi = wi[w];
+        }
+    return bi;
+}
+
+// Column sums of one chunk's unit rows u = x * inv into csum[c][0 .. D):
+// pairwise over the lanes (DPP), then over the waves.  All threads call it.
+template <int D>
+__device__ __forceinline__ void chunk_colsum(const u32x4_t (&x)[D / 8], float inv, int c, float* part, float* csum,
+                                             int wave, int lane, int tid) {
+    const Bf u = Bf::fresh();
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+        const u32x4_t w = x[p];
+        float s8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s8[2 * e] = wave_pairwise_sum(u.lo(w[e]) * inv);
+            s8[2 * e + 1] = wave_pairwise_sum(u.hi(w[e]) * inv);
+        }
+        if (lane == 63) {
+            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p) = f32x4_t{s8[0], s8[1], s8[2], s8[3]};
+            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p + 4) = f32x4_t{s8[4], s8[5], s8[6], s8[7]};
+        }
+        asm volatile("" ::: "memory");
+    }
+    __syncthreads();
+    if (tid < D) {
+        const float* q = part + tid;
+        const float s01 = q[0 * D] + q[1 * D], s23 = q[2 * D] + q[3 * D];
+        const float s45 = q[4 * D] + q[5 * D], s67 = q[6 * D] + q[7 * D];
+        csum[c * D + tid] = (s01 + s23) + (s45 + s67);
+    }
+    __syncthreads();
+}
+
+// Mean cosine of a row to all rows: (fma chain of u[k] * s[k]) / P.
+template <int D>
+__device__ __forceinline__ float mean_cos(const u32x4_t (&x)[D / 8], float inv, const float* ssum, float fP) {
+    const Bf u = Bf::fresh();
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p);
+        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p + 4);
+        const u32x4_t w = x[p];
+        acc = __builtin_fmaf(u.lo(w[0]) * inv, s0[0], acc);
+        acc = __builtin_fmaf(u.hi(w[0]) * inv, s0[1], acc);
+        acc = __builtin_fmaf(u.lo(w[1]) * inv, s0[2], acc);
+        acc = __builtin_fmaf(u.hi(w[1]) * inv, s0[3], acc);
+        acc = __builtin_fmaf(u.lo(w[2]) * inv, s1[0], acc);
+        acc = __builtin_fmaf(u.hi(w[2]) * inv, s1[1], acc);
+        acc = __builtin_fmaf(u.lo(w[3]) * inv, s1[2], acc);
+        acc = __builtin_fmaf(u.hi(w[3]) * inv, s1[3], acc);
+        piece_fence(acc);
+    }
+    return acc / fP;
+}
+
+// cos(x, y) with y fp32 in LDS: dot / (|x| |y|), 0 if a norm is 0.
+template <int D>
+__device__ __forceinline__ float cos_to(const u32x4_t (&x)[D / 8], float nx, const float* y, float ny) {
+    const float dt = dot_lds<D>(x, y);
+    return (nx == 0.0f || ny == 0.0f) ? 0.0f : dt / (nx * ny);
+}
+
+template <int D>
+__device__ __forceinline__ void store_row_f32(const u32x4_t (&x)[D / 8], float* dst) {
+    const Bf u = Bf::fresh();
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+        const u32x4_t w = x[p];
+        *reinterpret_cast<f32x4_t*>(dst + 8 * p) = f32x4_t{u.lo(w[0]), u.hi(w[0]), u.lo(w[1]), u.hi(w[1])};
+        *reinterpret_cast<f32x4_t*>(dst + 8 * p + 4) = f32x4_t{u.lo(w[2]), u.hi(w[2]), u.lo(w[3]), u.hi(w[3])};
+    }
+}
+
+__device__ __forceinline__ float inv_of(float nr) { return nr == 0.0f ? 0.0f : 1.0f / nr; }
+
+// A zero the compiler cannot see through.  Added to an LDS index inside a
+// loop over rows, it keeps the reads of a whole fp32 row (128 VGPRs) from
+// being hoisted out of the loop, while the pointer keeps its LDS provenance.
+__device__ __forceinline__ int opaque_zero() {
+    int z = 0;
+    asm volatile("" : "+s"(z));
+    return z;
+}
+
+constexpr int kNone = 0x7FFFFFFF;
+
+// 16-byte slot of piece p of LDS row s: the piece index is XORed with bits
+// of the row so that the 64 lanes of a wave, reading one piece of 64
+// consecutive rows, hit every bank once per 256 bytes.
+template <int D>
+__device__ __forceinline__ int lds_slot(int s, int p) {
+    constexpr int kPer256 = 256 / (2 * D);   // rows per 256 bytes: 1 (d = 128) or 2 (d = 64)
+    return s * (D / 8) + (p ^ ((s / kPer256) & (D / 8 - 1)));
+}
+
+// Row j = RC * 512 + s outside the registers: from LDS when s < n_lds, else
+// from global memory.  Rows past the prompt are zero.
+template <int D>
+__device__ __forceinline__ void fetch_row(const bkv_bf16* Q, int P, int j, int s, int n_lds, const u32x4_t* lrows,
+                                          u32x4_t (&x)[D / 8]) {
+    if (j < P && s < n_lds) {
+#pragma unroll
+        for (int p = 0; p < D / 8; ++p) x[p] = lrows[lds_slot<D>(s, p)];
+    } else {
+        load_row<D>(Q, P, j, x);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+    using L = Pre<D>;
+    constexpr int RC = L::kRegChunks;
+    constexpr int RR = L::kRegRows;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float* xr = reinterpret_cast<float*>(smem + L::kXrOff);
+    float* xn = reinterpret_cast<float*>(smem + L::kXnOff);
+    float* wv = reinterpret_cast<float*>(smem + L::kWvOff);
+    int* wi = reinterpret_cast<int*>(smem + L::kWiOff);
+    float* part = reinterpret_cast<float*>(smem + L::kPartOff);
+    float* csum = reinterpret_cast<float*>(smem + L::kCsumOff);
+    float* ssum = reinterpret_cast<float*>(smem + L::kSsumOff);
+    int* sel = reinterpret_cast<int*>(smem + L::kSelOff);
+
+    const int b = blockIdx.x;
+    if (b >= a.nbuf) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int P = a.P, m = a.n_beacon;
+    const bkv_bf16* Q = a.q + (size_t)b * P * D;
+    bkv_bf16* buf = a.qbuf + (size_t)b * a.qcap * D;
+
+    if (m <= 0) {   // no representatives kept
+        if (tid == 0) a.qcount[b] = 0;
+        return;
+    }
+    if (P <= m) {   // nothing to sample: the prompt's rows are the representatives
+        for (int e = tid; e < P * (D / 8); e += kThreads)
+            reinterpret_cast<u32x4_t*>(buf)[e] = reinterpret_cast<const u32x4_t*>(Q)[e];
+        if (a.fps_sel)
+            for (int i = tid; i < m; i += kThreads) a.fps_sel[(size_t)b * m + i] = i < P ? i : -1;
+        if (tid == 0) a.qcount[b] = P;
+        return;
+    }
+
+    const int C = (P + kThreads - 1) / kThreads;   // chunks of rows (uniform over the workgroup)
+    const int n_other = L::n_other(P);
+    const int n_lds = L::n_lds_rows(P, a.lds_bytes);
+    float* nst = reinterpret_cast<float*>(smem + L::kOtherOff);   // norms of the rows outside the registers
+    float* Sst = nst + n_other;                                   // their S (NaN once taken)
+    u32x4_t* lrows = reinterpret_cast<u32x4_t*>(smem + L::rows_off(P));
+
+    u32x4_t xv[RC][D / 8];
+    float nrm[RC];
+#pragma unroll
+    for (int c = 0; c < RC; ++c) load_row<D>(Q, P, c * kThreads + tid, xv[c]);
+
+    // ---- norms and column sums of the unit rows, chunk by chunk; rows past
+    // the registers are copied into LDS on the way while there is room
+#pragma unroll
+    for (int c = 0; c < RC; ++c) nrm[c] = norm_of<D>(xv[c]);
+#pragma unroll
+    for (int c = 0; c < RC; ++c)
+        if (c < C) chunk_colsum<D>(xv[c], inv_of(nrm[c]), c, part, csum, wave, lane, tid);
+#pragma unroll 1
+    for (int c = RC; c < C; ++c) {
+        const int j = c * kThreads + tid, s = j - RR;
+        u32x4_t tmp[D / 8];
+        load_row<D>(Q, P, j, tmp);
+        const float nr = norm_of<D>(tmp);
+        if (j < P) {
+            nst[s] = nr;
+            if (s < n_lds) {
+#pragma unroll
+                for (int p = 0; p < D / 8; ++p) lrows[lds_slot<D>(s, p)] = tmp[p];
+            }
+        }
+        chunk_colsum<D>(tmp, inv_of(nr), c, part, csum, wave, lane, tid);
+    }
+    // pairwise over the chunks, bottom-up in place; chunks past the last are zero
+    if (tid < D) {
+        int Cp = 1;
+        while (Cp < C) Cp *= 2;
+        for (int w = 1; w < Cp; w *= 2)
+            for (int c = 0; c < C; c += 2 * w)
+                csum[c * D + tid] = csum[c * D + tid] + (c + w < C ? csum[(c + w) * D + tid] : 0.0f);
+        ssum[tid] = csum[tid];
+    }
+    __syncthreads();
+
+    // ---- seed: the lowest mean cosine.  Selections are branch-free so that
+    // the compiler cannot sink a row's arithmetic past the loop over pieces.
+    const float fP = (float)P;
+    float bv = __builtin_inff();
+    int bi = kNone;
+    {
+        float inv[RC], av[RC];
+#pragma unroll
+        for (int c = 0; c < RC; ++c) inv[c] = inv_of(nrm[c]);
+        mean_cos_rows<D, RC>(xv, inv, ssum, fP, av);
+#pragma unroll
+        for (int c = 0; c < RC; ++c) {
+            const int j = c * kThreads + tid;
+            const bool take = (j < P) & ((bi == kNone) | (av[c] < bv));
+            bv = take ? av[c] : bv;
+            bi = take ? j : bi;
+        }
+    }
+#pragma unroll 1
+    for (int c = RC; c < C; ++c) {
+        const int j = c * kThreads + tid, s = j - RR;
+        if (j >= P) break;
+        u32x4_t tmp[D / 8];
+        fetch_row<D>(Q, P, j, s, n_lds, lrows, tmp);
+        const float av = mean_cos<D>(tmp, inv_of(nst[s]), ssum + opaque_zero(), fP);
+        if (bi == kNone || av < bv) {
+            bv = av;
+            bi = j;
+        }
+    }
+    int r = block_argmin(bv, bi, wv, wi, wave, lane);
+
+    // ---- greedy steps
+    float S[RC];
+    uint32_t taken = 0u;
+#pragma unroll
+    for (int c = 0; c < RC; ++c) S[c] = -__builtin_inff();
+    for (int s = tid; s < n_other; s += kThreads) Sst[s] = -__builtin_inff();
+    for (int t = 0;; ++t) {
+        const int par = t & 1;
+        // publish pick t: the selection order, its row and norm for the update
+        if (tid == 0) sel[t] = r;
+        if (tid == (r & (kThreads - 1))) {
+            const int c = r / kThreads;
+            float* dst = xr + par * D;
+            if (c < RC) {
+#pragma unroll
+                for (int cc = 0; cc < RC; ++cc)
+                    if (cc == c) {
+                        taken |= 1u << cc;
+                        xn[par] = nrm[cc];
+                        store_row_f32<D>(xv[cc], dst);
+                    }
+            } else {
+                const int s = r - RR;
+                u32x4_t tmp[D / 8];
+                fetch_row<D>(Q, P, r, s, n_lds, lrows, tmp);
+                xn[par] = nst[s];
+                Sst[s] = __builtin_nanf("");
+                store_row_f32<D>(tmp, dst);
+            }
+        }
+        __syncthreads();
+        if (t + 1 == m) break;
+        const float* y = xr + par * D;
+        const float ny = xn[par];
+        bv = __builtin_inff();
+        bi = kNone;
+        {
+            float dt[RC];
+            dots_lds<D, RC>(xv, y, dt);
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                const int j = c * kThreads + tid;
+                const bool live = (j < P) & !(taken & (1u << c));
+                const float cs = (nrm[c] == 0.0f || ny == 0.0f) ? 0.0f : dt[c] / (nrm[c] * ny);
+                const float sv = (live & (cs > S[c])) ? cs : S[c];
+                S[c] = sv;
+                const bool take = live & ((bi == kNone) | (sv < bv));
+                bv = take ? sv : bv;
+                bi = take ? j : bi;
+            }
+        }
+#pragma unroll 1
+    for (int c = RC; c < C; ++c) {
+            const int j = c * kThreads + tid, s = j - RR;
+            if (j >= P) break;
+            float sv = Sst[s];
+            if (sv != sv) continue;   // taken
+            u32x4_t tmp[D / 8];
+            fetch_row<D>(Q, P, j, s, n_lds, lrows, tmp);
+            const float cs = cos_to<D>(tmp, nst[s], y + opaque_zero(), ny);
+            if (cs > sv) sv = cs;
+            Sst[s] = sv;
+            if (bi == kNone || sv < bv) {
+                bv = sv;
+                bi = j;
+            }
+        }
+        const int q = (t + 1) & 1;
+        r = block_argmin(bv, bi, wv + q * kWaves, wi + q * kWaves, wave, lane);
+    }
+
+    // ---- survivors in ascending prompt order, the selection order, the count
+    if (a.fps_sel)
+        for (int i = tid; i < m; i += kThreads) a.fps_sel[(size_t)b * m + i] = sel[i];
+    for (int e = tid; e < m * (D / 8); e += kThreads) {
+        const int i = e / (D / 8), p = e % (D / 8);
+        const int ji = sel[i];
+        int rank = 0;
+        for (int k = 0; k < m; ++k) rank += sel[k] < ji ? 1 : 0;
+        reinterpret_cast<u32x4_t*>(buf + (size_t)rank * D)[p] =
+            reinterpret_cast<const u32x4_t*>(Q + (size_t)ji * D)[p];
+    }
+    if (tid == 0) a.qcount[b] = m;
+}
+
+template <int D>
+hipError_t launch_d(PrefillArgs a, hipStream_t st) {
+    // LDS for the rows past the registers: what one workgroup may take, at most a CU's 160 KB
+    int dev = 0, lim = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    a.lds_bytes = lim < kLdsBytes ? lim : kLdsBytes;
+    if ((int)Pre<D>::rows_off(a.P) > a.lds_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_kernel<D>), dim3(a.nbuf), dim3(kThreads), Pre<D>::bytes(a.P, a.lds_bytes), st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t st) {
+    if (a.nbuf <= 0) return hipSuccess;
+    return d == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+}  // namespace bkv

@@ -25,7 +25,8 @@ BKV_POOL_MEAN = 2
 ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE", -4: "BKV_EHIP"}
 
 EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_fps_update",
-           "bkv_fps_merge", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict", "bkv_decode_step")
+           "bkv_fps_merge", "bkv_fps_prefill", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict",
+           "bkv_decode_step")
 
 
 class Shape(C.Structure):
@@ -59,6 +60,7 @@ def load():
         L.bkv_rope_table.argtypes = [C.c_double, i32, i32, i32, P]
         L.bkv_fps_update.argtypes = [SP, P, P, P, P, st]
         L.bkv_fps_merge.argtypes = [SP, P, P, P, P, st]
+        L.bkv_fps_prefill.argtypes = [SP, P, i32, P, P, P, st]
         L.bkv_score.argtypes = [SP, P, i32, P, P, P, P, P, P, i32, P, st]
         L.bkv_select.argtypes = [SP, P, i32, P, st]
         L.bkv_compact.argtypes = [SP, P, P, i32, P, st]
@@ -116,6 +118,22 @@ def _check(code: int, where: str) -> None:
 
 bf16, i32, f32 = torch.bfloat16, torch.int32, torch.float32
 
+BKV_PREFILL_MAX = 8192
+
+
+def _need(shape: Shape, **req) -> None:
+    """Reject tensors smaller than the layout of include/bkv.h needs for this shape, before anything
+    reaches the device.  Each keyword maps a name to (tensor or None, element count)."""
+    for name, (t, n) in req.items():
+        if t is not None and isinstance(t, torch.Tensor) and t.numel() < max(int(n), 0):
+            raise ValueError(f"{name}: {t.numel()} elements, the shape needs {int(n)}")
+
+
+def _counts(shape: Shape):
+    units = shape.n_layers * shape.batch * shape.n_kv_heads
+    qbufs = shape.n_layers * shape.batch * shape.n_q_heads
+    return units, qbufs, shape.head_dim
+
 
 def rope_table(theta: float, head_dim: int, p0: int, p1: int) -> np.ndarray:
     """Host-built {cos, sin} table [p1 - p0, head_dim/2, 2] (float32)."""
@@ -126,19 +144,38 @@ def rope_table(theta: float, head_dim: int, p0: int, p1: int) -> np.ndarray:
 
 
 def fps_update(shape: Shape, qbuf, qcount, q_new, fps_sel=None, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, qbuf=(qbuf, Qb * shape.qcap * d), qcount=(qcount, Qb), q_new=(q_new, Qb * d),
+          fps_sel=(fps_sel, Qb * shape.n_beacon))
     _check(load().bkv_fps_update(C.byref(shape), _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"),
                                  _ptr(q_new, bf16, "q_new"), _ptr(fps_sel, i32, "fps_sel"), _stream(stream)),
            "bkv_fps_update")
 
 
 def fps_merge(shape: Shape, qbuf, qcount, q_recent, fps_sel=None, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, qbuf=(qbuf, Qb * shape.qcap * d), qcount=(qcount, Qb),
+          q_recent=(q_recent, Qb * shape.n_recent_q * d), fps_sel=(fps_sel, Qb * shape.n_beacon))
     _check(load().bkv_fps_merge(C.byref(shape), _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"),
                                 _ptr(q_recent, bf16, "q_recent"), _ptr(fps_sel, i32, "fps_sel"), _stream(stream)),
            "bkv_fps_merge")
 
 
+def fps_prefill(shape: Shape, q_prompt, n_prompt: int, qbuf, qcount, fps_sel=None, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, q_prompt=(q_prompt, Qb * n_prompt * d), qbuf=(qbuf, Qb * shape.qcap * d), qcount=(qcount, Qb),
+          fps_sel=(fps_sel, Qb * shape.n_beacon))
+    _check(load().bkv_fps_prefill(C.byref(shape), _ptr(q_prompt, bf16, "q_prompt"), int(n_prompt),
+                                  _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(fps_sel, i32, "fps_sel"),
+                                  _stream(stream)), "bkv_fps_prefill")
+
+
 def score(shape: Shape, K, n_len: int, qbuf, qcount, q_recent, pos_recent, t, rope_cs, scores,
           stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, K=(K, U * shape.cap * d), qbuf=(qbuf, Qb * shape.qcap * d), qcount=(qcount, Qb),
+          q_recent=(q_recent, Qb * shape.n_recent_q * d), pos_recent=(pos_recent, shape.batch * shape.n_recent_q),
+          t=(t, shape.batch), rope_cs=(rope_cs, rope_cs.shape[0] * d), scores=(scores, U * n_len))
     _check(load().bkv_score(C.byref(shape), _ptr(K, bf16, "K"), int(n_len), _ptr(qbuf, bf16, "qbuf"),
                             _ptr(qcount, i32, "qcount"), _ptr(q_recent, bf16, "q_recent"),
                             _ptr(pos_recent, i32, "pos_recent"), _ptr(t, i32, "t"),
@@ -147,17 +184,27 @@ def score(shape: Shape, K, n_len: int, qbuf, qcount, q_recent, pos_recent, t, ro
 
 
 def select(shape: Shape, scores, n_len: int, idx, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, scores=(scores, U * n_len), idx=(idx, U * shape.budget))
     _check(load().bkv_select(C.byref(shape), _ptr(scores, f32, "scores"), int(n_len), _ptr(idx, i32, "idx"),
                              _stream(stream)), "bkv_select")
 
 
 def compact(shape: Shape, K, V, n_len: int, idx, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, K=(K, U * shape.cap * d), V=(V, U * shape.cap * d), idx=(idx, U * shape.budget))
     _check(load().bkv_compact(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(n_len),
                               _ptr(idx, i32, "idx"), _stream(stream)), "bkv_compact")
 
 
 def evict(shape: Shape, K, V, n_len: int, qbuf, qcount, q_recent, pos_recent, t, rope_cs,
           idx_out=None, scores_out=None, fps_sel_out=None, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, K=(K, U * shape.cap * d), V=(V, U * shape.cap * d), qbuf=(qbuf, Qb * shape.qcap * d),
+          qcount=(qcount, Qb), q_recent=(q_recent, Qb * shape.n_recent_q * d),
+          pos_recent=(pos_recent, shape.batch * shape.n_recent_q), t=(t, shape.batch),
+          rope_cs=(rope_cs, rope_cs.shape[0] * d), idx_out=(idx_out, U * shape.budget),
+          scores_out=(scores_out, U * n_len), fps_sel_out=(fps_sel_out, Qb * shape.n_beacon))
     _check(load().bkv_evict(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(n_len),
                             _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(q_recent, bf16, "q_recent"),
                             _ptr(pos_recent, i32, "pos_recent"), _ptr(t, i32, "t"), _ptr(rope_cs, f32, "rope_cs"),
@@ -167,6 +214,11 @@ def evict(shape: Shape, K, V, n_len: int, qbuf, qcount, q_recent, pos_recent, t,
 
 def decode_step(shape: Shape, K, V, L: int, k_new, v_new, pos, qbuf, qcount, q_new, q_recent, pos_recent,
                 rope_cs, fps_sel=None, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, K=(K, U * shape.cap * d), V=(V, U * shape.cap * d), k_new=(k_new, U * d), v_new=(v_new, U * d),
+          pos=(pos, shape.batch), qbuf=(qbuf, Qb * shape.qcap * d), qcount=(qcount, Qb), q_new=(q_new, Qb * d),
+          q_recent=(q_recent, Qb * shape.n_recent_q * d), pos_recent=(pos_recent, shape.batch * shape.n_recent_q),
+          rope_cs=(rope_cs, rope_cs.shape[0] * d), fps_sel=(fps_sel, Qb * shape.n_beacon))
     _check(load().bkv_decode_step(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(L),
                                   _ptr(k_new, bf16, "k_new"), _ptr(v_new, bf16, "v_new"), _ptr(pos, i32, "pos"),
                                   _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(q_new, bf16, "q_new"),

@@ -142,6 +142,20 @@ def make_query_buffers(cfg: EvictConfig, device="cpu", seed: int | None = None,
             "q_new": q_new}
 
 
+def make_prompt_queries(cfg: EvictConfig, n_prompt: int, device="cpu", seed: int | None = None) -> torch.Tensor:
+    """Pre-RoPE prompt queries for the prefill sampling, bf16 [L, B, Hq, n_prompt, d], drawn from the
+    workload's query mixture with centres of their own per (layer, batch, query head)."""
+    device = torch.device(device)
+    g = _gen(device, (cfg.seed if seed is None else seed) + 11)
+    L, B, Hq, d = cfg.n_layers, cfg.batch, cfg.hq, cfg.d
+    C = n_centres(cfg.mix)
+    q = torch.empty(L, B, Hq, n_prompt, d, dtype=torch.bfloat16, device=device)
+    for l in range(L):
+        cen = _unit_rows(g, (B, Hq, C), d, device)
+        q[l] = query_rows(g, cen, n_prompt, cfg.mix).to(torch.bfloat16)
+    return q
+
+
 # ---------------------------------------------------------------------------
 # Streaming decode inputs.
 

@@ -120,6 +120,17 @@ def test_pointer_and_range_validation(so):
                         None, None, None, None) == -3
 
 
+def test_prefill_validation(so):
+    s = _shape()
+    assert so.bkv_fps_prefill(C.byref(s), FAKE, -1, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_prefill(C.byref(s), FAKE, 8193, FAKE, FAKE, None, None) == -2
+    assert so.bkv_fps_prefill(C.byref(s), None, 10, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_prefill(C.byref(s), MISALIGNED, 10, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_prefill(C.byref(s), FAKE, 10, None, FAKE, None, None) == -1
+    assert so.bkv_fps_prefill(C.byref(s), FAKE, 10, FAKE, FAKE, MISALIGNED, None) == -1
+    assert so.bkv_fps_prefill(C.byref(_shape(n_beacon=20)), FAKE, 10, FAKE, FAKE, None, None) == -2
+
+
 def test_all_configs_are_supported_shapes():
     for cfg in EVICT_CONFIGS.values():
         assert cfg.d in (64, 128) and cfg.hq % cfg.hkv == 0 and cfg.G <= 8
