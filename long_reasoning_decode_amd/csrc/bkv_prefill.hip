@@ -99,90 +99,55 @@ __device__ __forceinline__ void load_row(const bkv_bf16* Q, int P, int j, u32x4_
     }
 }
 
-// fma chain over k ascending of x[k] * y[k], y fp32 in LDS (the same address
-// for every lane: broadcast reads)
+// For R rows at once: acc[r] = fma chain over k ascending (from +0) of
+// x_r[k] * y[k], or of (x_r[k] * inv[r]) * y[k] with SCALE, y fp32 in LDS
+// (the same address for every lane: broadcast reads).  The next piece of y is
+// read while the current one is used, and each piece of y serves every row.
+template <int D, int R, bool SCALE>
+__device__ __forceinline__ void fma_rows(const u32x4_t (&x)[R][D / 8], const float* y, const float* inv,
+                                         float (&acc)[R]) {
+    const Bf u = Bf::fresh();
+    constexpr int NP = D / 8;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    f32x4_t ya = *reinterpret_cast<const f32x4_t*>(y);
+    f32x4_t yb = *reinterpret_cast<const f32x4_t*>(y + 4);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        f32x4_t na = ya, nb = yb;
+        if (p + 1 < NP) {
+            na = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1));
+            nb = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1) + 4);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4_t w = x[r][p];
+            float e[8] = {u.lo(w[0]), u.hi(w[0]), u.lo(w[1]), u.hi(w[1]),
+                          u.lo(w[2]), u.hi(w[2]), u.lo(w[3]), u.hi(w[3])};
+            if constexpr (SCALE) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) e[k] = e[k] * inv[r];
+            }
+            float a = acc[r];
+            a = __builtin_fmaf(e[0], ya[0], a);
+            a = __builtin_fmaf(e[1], ya[1], a);
+            a = __builtin_fmaf(e[2], ya[2], a);
+            a = __builtin_fmaf(e[3], ya[3], a);
+            a = __builtin_fmaf(e[4], yb[0], a);
+            a = __builtin_fmaf(e[5], yb[1], a);
+            a = __builtin_fmaf(e[6], yb[2], a);
+            a = __builtin_fmaf(e[7], yb[3], a);
+            piece_fence(a);
+            acc[r] = a;
+        }
+        ya = na;
+        yb = nb;
+    }
+}
+
 template <int D>
-__device__ __forceinline__ float dot_lds(const u32x4_t (&x)[D / 8], const float* y) {
-    const Bf u = Bf::fresh();
-    float acc = 0.0f;
-#pragma unroll
-    for (int p = 0; p < D / 8; ++p) {
-        const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(y + 8 * p);
-        const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(y + 8 * p + 4);
-        const u32x4_t w = x[p];
-        acc = __builtin_fmaf(u.lo(w[0]), y0[0], acc);
-        acc = __builtin_fmaf(u.hi(w[0]), y0[1], acc);
-        acc = __builtin_fmaf(u.lo(w[1]), y0[2], acc);
-        acc = __builtin_fmaf(u.hi(w[1]), y0[3], acc);
-        acc = __builtin_fmaf(u.lo(w[2]), y1[0], acc);
-        acc = __builtin_fmaf(u.hi(w[2]), y1[1], acc);
-        acc = __builtin_fmaf(u.lo(w[3]), y1[2], acc);
-        acc = __builtin_fmaf(u.hi(w[3]), y1[3], acc);
-        piece_fence(acc);
-    }
-    return acc;
-}
-
-// The same for the RC resident rows at once, so that each 8-float piece of y
-// is read once and used by every row while it is live.
-template <int D, int RC>
-__device__ __forceinline__ void dots_lds(const u32x4_t (&x)[RC][D / 8], const float* y, float (&acc)[RC]) {
-    const Bf u = Bf::fresh();
-#pragma unroll
-    for (int c = 0; c < RC; ++c) acc[c] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < D / 8; ++p) {
-        const f32x4_t y0 = *reinterpret_cast<const f32x4_t*>(y + 8 * p);
-        const f32x4_t y1 = *reinterpret_cast<const f32x4_t*>(y + 8 * p + 4);
-#pragma unroll
-        for (int c = 0; c < RC; ++c) {
-            const u32x4_t w = x[c][p];
-            float a = acc[c];
-            a = __builtin_fmaf(u.lo(w[0]), y0[0], a);
-            a = __builtin_fmaf(u.hi(w[0]), y0[1], a);
-            a = __builtin_fmaf(u.lo(w[1]), y0[2], a);
-            a = __builtin_fmaf(u.hi(w[1]), y0[3], a);
-            a = __builtin_fmaf(u.lo(w[2]), y1[0], a);
-            a = __builtin_fmaf(u.hi(w[2]), y1[1], a);
-            a = __builtin_fmaf(u.lo(w[3]), y1[2], a);
-            a = __builtin_fmaf(u.hi(w[3]), y1[3], a);
-            piece_fence(a);
-            acc[c] = a;
-        }
-    }
-}
-
-// Mean cosines (fma chain of u[k] * s[k], then / P) of the RC resident rows.
-template <int D, int RC>
-__device__ __forceinline__ void mean_cos_rows(const u32x4_t (&x)[RC][D / 8], const float (&inv)[RC],
-                                              const float* ssum, float fP, float (&out)[RC]) {
-    const Bf u = Bf::fresh();
-    float acc[RC];
-#pragma unroll
-    for (int c = 0; c < RC; ++c) acc[c] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < D / 8; ++p) {
-        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p);
-        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p + 4);
-#pragma unroll
-        for (int c = 0; c < RC; ++c) {
-            const u32x4_t w = x[c][p];
-            const float iv = inv[c];
-            float a = acc[c];
-            a = __builtin_fmaf(u.lo(w[0]) * iv, s0[0], a);
-            a = __builtin_fmaf(u.hi(w[0]) * iv, s0[1], a);
-            a = __builtin_fmaf(u.lo(w[1]) * iv, s0[2], a);
-            a = __builtin_fmaf(u.hi(w[1]) * iv, s0[3], a);
-            a = __builtin_fmaf(u.lo(w[2]) * iv, s1[0], a);
-            a = __builtin_fmaf(u.hi(w[2]) * iv, s1[1], a);
-            a = __builtin_fmaf(u.lo(w[3]) * iv, s1[2], a);
-            a = __builtin_fmaf(u.hi(w[3]) * iv, s1[3], a);
-            piece_fence(a);
-            acc[c] = a;
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < RC; ++c) out[c] = acc[c] / fP;
+__device__ __forceinline__ const u32x4_t (&one_row(const u32x4_t (&x)[D / 8]))[1][D / 8] {
+    return *reinterpret_cast<const u32x4_t(*)[1][D / 8]>(&x);
 }
 
 template <int D>
@@ -223,9 +188,39 @@ __device__ __forceinline__ bool less_vi(float v2, int i2, float v, int i) {
     return v2 < v || (v2 == v && i2 < i);
 }
 
+template <int CTRL>
+__device__ __forceinline__ void dpp_argmin(float& v, int& i) {
+    const float v2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    const int i2 = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+    const bool take = less_vi(v2, i2, v, i);
+    v = take ? v2 : v;
+    i = take ? i2 : i;
+}
+
+// Wave argmin of (v, i) by DPP inside each 16-lane row, then the four row
+// winners compared in order; the result is uniform (held in every lane).
+__device__ __forceinline__ void wave_argmin_dpp(float& v, int& i) {
+    dpp_argmin<0xB1>(v, i);    // quad_perm [1,0,3,2]
+    dpp_argmin<0x4E>(v, i);    // quad_perm [2,3,0,1]
+    dpp_argmin<0x141>(v, i);   // row_half_mirror
+    dpp_argmin<0x140>(v, i);   // row_mirror: every lane of a row holds the row's winner
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int row = 1; row < 4; ++row) {
+        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * row));
+        const int ri = __builtin_amdgcn_readlane(i, 16 * row);
+        const bool take = less_vi(rv, ri, bv, bi);
+        bv = take ? rv : bv;
+        bi = take ? ri : bi;
+    }
+    v = bv;
+    i = bi;
+}
+
 // Workgroup argmin of (v, i); every thread gets the winning index.
 __device__ __forceinline__ int block_argmin(float v, int i, float* wv, int* wi, int wave, int lane) {
-    wave_argmin(v, i);
+    wave_argmin_dpp(v, i);
     if (lane == 0) {
         wv[wave] = v;
         wi[wave] = i;
@@ -276,31 +271,18 @@ __device__ __forceinline__ void chunk_colsum(const u32x4_t (&x)[D / 8], float in
 // Mean cosine of a row to all rows: (fma chain of u[k] * s[k]) / P.
 template <int D>
 __device__ __forceinline__ float mean_cos(const u32x4_t (&x)[D / 8], float inv, const float* ssum, float fP) {
-    const Bf u = Bf::fresh();
-    float acc = 0.0f;
-#pragma unroll
-    for (int p = 0; p < D / 8; ++p) {
-        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p);
-        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(ssum + 8 * p + 4);
-        const u32x4_t w = x[p];
-        acc = __builtin_fmaf(u.lo(w[0]) * inv, s0[0], acc);
-        acc = __builtin_fmaf(u.hi(w[0]) * inv, s0[1], acc);
-        acc = __builtin_fmaf(u.lo(w[1]) * inv, s0[2], acc);
-        acc = __builtin_fmaf(u.hi(w[1]) * inv, s0[3], acc);
-        acc = __builtin_fmaf(u.lo(w[2]) * inv, s1[0], acc);
-        acc = __builtin_fmaf(u.hi(w[2]) * inv, s1[1], acc);
-        acc = __builtin_fmaf(u.lo(w[3]) * inv, s1[2], acc);
-        acc = __builtin_fmaf(u.hi(w[3]) * inv, s1[3], acc);
-        piece_fence(acc);
-    }
-    return acc / fP;
+    float acc[1];
+    const float iv[1] = {inv};
+    fma_rows<D, 1, true>(one_row<D>(x), ssum, iv, acc);
+    return acc[0] / fP;
 }
 
 // cos(x, y) with y fp32 in LDS: dot / (|x| |y|), 0 if a norm is 0.
 template <int D>
 __device__ __forceinline__ float cos_to(const u32x4_t (&x)[D / 8], float nx, const float* y, float ny) {
-    const float dt = dot_lds<D>(x, y);
-    return (nx == 0.0f || ny == 0.0f) ? 0.0f : dt / (nx * ny);
+    float dt[1];
+    fma_rows<D, 1, false>(one_row<D>(x), y, nullptr, dt);
+    return (nx == 0.0f || ny == 0.0f) ? 0.0f : dt[0] / (nx * ny);
 }
 
 template <int D>
@@ -438,7 +420,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         float inv[RC], av[RC];
 #pragma unroll
         for (int c = 0; c < RC; ++c) inv[c] = inv_of(nrm[c]);
-        mean_cos_rows<D, RC>(xv, inv, ssum, fP, av);
+        fma_rows<D, RC, true>(xv, ssum, inv, av);
+#pragma unroll
+        for (int c = 0; c < RC; ++c) av[c] = av[c] / fP;
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             const int j = c * kThreads + tid;
@@ -499,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         bi = kNone;
         {
             float dt[RC];
-            dots_lds<D, RC>(xv, y, dt);
+            fma_rows<D, RC, false>(xv, y, nullptr, dt);
 #pragma unroll
             for (int c = 0; c < RC; ++c) {
                 const int j = c * kThreads + tid;
