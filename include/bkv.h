@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 3
+#define BKV_ABI_VERSION 4
 
 typedef uint16_t bkv_bf16; /* raw bf16 bits */
 
@@ -72,6 +72,22 @@ enum {
 /* flags */
 #define BKV_CAUSAL_RECENT 1u /* recent query i sees only slots <= n_len - n_recent_q + i */
 #define BKV_POOL_MEAN 2u     /* scores pool the weights by their mean, not their max (see bkv_score) */
+/* Source of the beacons (at most one; neither = continual FPS, Notes §2.2).
+ * The buffer, its count and the cycle stay as for continual FPS; only the
+ * update, the merge and the prefill change:
+ *   BKV_BEACON_INITIAL (Initial+Recent, Notes §3.4 Table 3): the first
+ *     n_beacon queries a buffer is offered; later ones are ignored and the
+ *     merge keeps the buffer.
+ *   BKV_BEACON_RANDOM (random history, Notes §3.2 Fig. 6): a uniform random
+ *     sample of n_beacon of all queries offered so far, by reservoir sampling
+ *     (Vitter's Algorithm R).  qcount counts the offers; offer n (0-based)
+ *     takes slot n while n < n_beacon, else slot floor(r (n + 1) / 2^32) if
+ *     below n_beacon, where r is the first output word of Philox4x32-10
+ *     (Salmon et al., SC 2011) at counter (n, uq, 0, 0) and key (seed, 0).
+ *     Updates offer the step's query; the merge offers the recents in ring
+ *     order. */
+#define BKV_BEACON_INITIAL 4u
+#define BKV_BEACON_RANDOM 8u
 
 typedef struct bkv_shape {
     int32_t n_layers, batch, n_q_heads, n_kv_heads, head_dim; /* head_dim in {64, 128}; G <= 8 */
@@ -82,7 +98,8 @@ typedef struct bkv_shape {
     int32_t n_beacon;     /* B_Q^min: beacons kept by FPS */
     int32_t n_recent_q;   /* recent queries; B_Q^max = n_beacon + n_recent_q <= 32 */
     int32_t qcap;         /* rows allocated per query buffer, >= B_Q^max */
-    uint32_t flags;       /* BKV_CAUSAL_RECENT | BKV_POOL_MEAN */
+    uint32_t flags;       /* BKV_CAUSAL_RECENT | BKV_POOL_MEAN | one BKV_BEACON_* */
+    uint32_t seed;        /* key of the BKV_BEACON_RANDOM draws */
 } bkv_shape;
 
 /* ABI version (BKV_ABI_VERSION). */
@@ -109,7 +126,9 @@ int bkv_rope_table(double theta, int32_t head_dim, int32_t p0, int32_t p1, float
  * ascending slot order, and set qcount to n_beacon.
  * In/out: qbuf (rows [0, qcount) valid afterwards), qcount.  fps_sel may be
  * NULL; else it receives the selection order, or -1s where no sampling ran.
- * qcount is clamped to [0, B_Q^max - 1] on entry. */
+ * qcount is clamped to [0, B_Q^max - 1] on entry.  Under BKV_BEACON_INITIAL
+ * or BKV_BEACON_RANDOM the update is instead one offer of q_new[uq] by that
+ * rule (see the flags; qcount < 0 reads as 0), and fps_sel receives -1s. */
 int bkv_fps_update(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
                    const bkv_bf16 *q_new, int32_t *fps_sel, void *stream);
 
@@ -129,6 +148,10 @@ int bkv_fps_update(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
  * row index, zero rows padding it to a power of two), which costs O(n d)
  * instead of O(n^2 d); the fma chains, norms, cosines, argmins and ties are
  * as in bkv_fps_update.  Inputs must be finite with finite squared norms.
+ * Under BKV_BEACON_INITIAL the buffer takes the first min(n_prompt,
+ * n_beacon) prompt rows (count likewise); under BKV_BEACON_RANDOM every
+ * prompt row is offered in order (count n_prompt); fps_sel then holds the
+ * prompt row kept in each slot (-1 for an empty slot).
  * Errors: BKV_EINVAL (null or misaligned pointer, n_prompt < 0),
  * BKV_EUNSUPPORTED (n_prompt > BKV_PREFILL_MAX). */
 int bkv_fps_prefill(const bkv_shape *shape, const bkv_bf16 *q_prompt, int32_t n_prompt,
@@ -172,7 +195,9 @@ int bkv_compact(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t n_len,
  * qbuf[uq][0 : min(qcount, n_beacon)) followed by q_recent[uq] are reduced
  * by FPS to n_beacon rows (all of them if there are no more), written in
  * candidate order to qbuf[uq], and qcount becomes their number.  fps_sel
- * (nullable) receives the selection order (-1 padded). */
+ * (nullable) receives the selection order (-1 padded).  Under
+ * BKV_BEACON_INITIAL nothing changes; under BKV_BEACON_RANDOM the recents
+ * are offered in ring order; fps_sel receives -1s for both. */
 int bkv_fps_merge(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
                   const bkv_bf16 *q_recent, int32_t *fps_sel, void *stream);
 

@@ -34,6 +34,7 @@ class EvictConfig:
     seed: int = 20261202
     qcap: int = 32         # rows allocated per query buffer
     pool: str = "max"      # pooling of the weights: "max" (§2.3 Eq. 7) or "mean" (§2.1 Eq. 6, §3.3 Table 2)
+    beacon: str = "fps"    # source of the beacons: "fps" (§2.2), "initial" (§3.4 Table 3), "random" (§3.2 Fig. 6)
 
     @property
     def n_len(self) -> int:
@@ -136,13 +137,28 @@ class StreamConfig:
 STREAM = StreamConfig()
 TINY_STREAM = StreamConfig(name="stream-tiny", base=replace(TINY, batch=2, seed=20261202 + 510),
                            steps=600, drift_every=256, p0_max=1000)
-# the most beacon-heavy split of the recent/beacon ablation (1 recent + 31 beacons): the buffer is full after
-# every step, so every collection step runs a sampling round
-STREAM_1R31B = StreamConfig(name="stream-qwen3-4b-1r31b",
-                            base=replace(QWEN3_4B, batch=192, n_beacon=31, n_recent_q=1, seed=20261202 + 520))
-TINY_STREAM_1R31B = StreamConfig(name="stream-tiny-1r31b",
-                                 base=replace(TINY, batch=2, n_beacon=31, n_recent_q=1, seed=20261202 + 530),
-                                 steps=400, drift_every=256, p0_max=1000)
+# The recent/beacon splits of the 32 observation queries in the ablation of §3.3 Table 1: all recent (no
+# beacons), 31 + 1, 16 + 16 (the default), 4 + 28 and 1 + 31.  With 1 recent query the buffer is full after
+# every step, so every collection step runs a sampling round.
+def _split(base_cfg: StreamConfig, nrq: int, nb: int, seed: int) -> StreamConfig:
+    stem = base_cfg.name
+    return replace(base_cfg, name=f"{stem}-r{nrq}b{nb}",
+                   base=replace(base_cfg.base, n_recent_q=nrq, n_beacon=nb, seed=seed))
+
+
+SPLITS = ((32, 0), (31, 1), (4, 28), (1, 31))
+STREAM_SPLITS = tuple(_split(STREAM, nrq, nb, 20261202 + 520 + i) for i, (nrq, nb) in enumerate(SPLITS))
+TINY_STREAM_SPLITS = tuple(replace(_split(TINY_STREAM, nrq, nb, 20261202 + 530 + i), steps=400)
+                           for i, (nrq, nb) in enumerate(SPLITS))
 TINY_STREAM_MEAN = StreamConfig(name="stream-tiny-mean", base=replace(TINY, batch=2, pool="mean", seed=20261202 + 540),
                                 steps=600, drift_every=256, p0_max=1000)
-STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM, STREAM_1R31B, TINY_STREAM_1R31B, TINY_STREAM_MEAN)}
+# Other sources of beacons: the first queries (Initial+Recent, §3.4 Table 3) and a uniform random sample of
+# the history (§3.2 Fig. 6), with the 16 + 16 split.
+STREAM_SOURCES = tuple(replace(STREAM, name=f"stream-qwen3-4b-{src}", base=replace(STREAM.base, beacon=src,
+                                                                                 seed=20261202 + 560 + i))
+                       for i, src in enumerate(("initial", "random")))
+TINY_STREAM_SOURCES = tuple(replace(TINY_STREAM, name=f"stream-tiny-{src}", base=replace(TINY_STREAM.base, beacon=src,
+                                                                                        seed=20261202 + 570 + i))
+                            for i, src in enumerate(("initial", "random")))
+STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM, TINY_STREAM_MEAN) + STREAM_SPLITS + TINY_STREAM_SPLITS
+                  + STREAM_SOURCES + TINY_STREAM_SOURCES}

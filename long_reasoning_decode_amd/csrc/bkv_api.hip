@@ -27,7 +27,8 @@ int check_shape(const bkv_shape* s) {
     if (s->n_beacon + s->n_recent_q > kMaxBq) return BKV_EUNSUPPORTED;
     if (s->qcap < s->n_beacon + s->n_recent_q) return BKV_EINVAL;
     if (s->cap <= 0 || s->budget < 0 || s->n_prefix < 0 || s->n_recent_kv < 0) return BKV_EINVAL;
-    if (s->flags & ~(BKV_CAUSAL_RECENT | BKV_POOL_MEAN)) return BKV_EINVAL;
+    if (s->flags & ~(BKV_CAUSAL_RECENT | BKV_POOL_MEAN | BKV_BEACON_INITIAL | BKV_BEACON_RANDOM)) return BKV_EINVAL;
+    if ((s->flags & BKV_BEACON_INITIAL) && (s->flags & BKV_BEACON_RANDOM)) return BKV_EINVAL;
     const int64_t units = (int64_t)s->n_layers * s->batch * s->n_kv_heads;
     const int64_t qbufs = (int64_t)s->n_layers * s->batch * s->n_q_heads;
     if (units > INT32_MAX || qbufs > INT32_MAX) return BKV_ERANGE;
@@ -50,6 +51,29 @@ int units_of(const bkv_shape* s) { return s->n_layers * s->batch * s->n_kv_heads
 int qbufs_of(const bkv_shape* s) { return s->n_layers * s->batch * s->n_q_heads; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
+
+int src_of(const bkv_shape* s) {
+    if (s->flags & BKV_BEACON_INITIAL) return bkv::kSrcInitial;
+    if (s->flags & BKV_BEACON_RANDOM) return bkv::kSrcRandom;
+    return bkv::kSrcFps;
+}
+
+bkv::FpsArgs fps_args(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const bkv_bf16* q_new,
+                      const bkv_bf16* q_recent, int32_t* fps_sel) {
+    bkv::FpsArgs a;
+    a.qbuf = qbuf;
+    a.qcount = qcount;
+    a.q_new = q_new;
+    a.q_recent = q_recent;
+    a.fps_sel = fps_sel;
+    a.nbuf = qbufs_of(s);
+    a.qcap = s->qcap;
+    a.n_beacon = s->n_beacon;
+    a.n_recent_q = s->n_recent_q;
+    a.src = src_of(s);
+    a.seed = s->seed;
+    return a;
+}
 
 bkv::ScoreArgs score_args(const bkv_shape* s, const bkv_bf16* K, int32_t n_len, const bkv_bf16* qbuf,
                           const int32_t* qcount, const bkv_bf16* q_recent, const int32_t* pos_recent,
@@ -129,16 +153,7 @@ int bkv_fps_update(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const bk
     if (!qbuf || !qcount || !q_new) return BKV_EINVAL;
     if (!aligned16(qbuf) || !aligned16(q_new) || !aligned4(qcount)) return BKV_EINVAL;
     if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
-    bkv::FpsArgs a;
-    a.qbuf = qbuf;
-    a.qcount = qcount;
-    a.q_new = q_new;
-    a.q_recent = nullptr;
-    a.fps_sel = fps_sel;
-    a.nbuf = qbufs_of(s);
-    a.qcap = s->qcap;
-    a.n_beacon = s->n_beacon;
-    a.n_recent_q = s->n_recent_q;
+    bkv::FpsArgs a = fps_args(s, qbuf, qcount, q_new, nullptr, fps_sel);
     return hip_status(bkv::launch_fps(a, s->head_dim, false, (hipStream_t)stream));
 }
 
@@ -149,16 +164,7 @@ int bkv_fps_merge(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const bkv
     if (!qbuf || !qcount || (s->n_recent_q > 0 && !q_recent)) return BKV_EINVAL;
     if (!aligned16(qbuf) || (q_recent && !aligned16(q_recent)) || !aligned4(qcount)) return BKV_EINVAL;
     if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
-    bkv::FpsArgs a;
-    a.qbuf = qbuf;
-    a.qcount = qcount;
-    a.q_new = nullptr;
-    a.q_recent = q_recent;
-    a.fps_sel = fps_sel;
-    a.nbuf = qbufs_of(s);
-    a.qcap = s->qcap;
-    a.n_beacon = s->n_beacon;
-    a.n_recent_q = s->n_recent_q;
+    bkv::FpsArgs a = fps_args(s, qbuf, qcount, nullptr, q_recent, fps_sel);
     return hip_status(bkv::launch_fps(a, s->head_dim, true, (hipStream_t)stream));
 }
 
@@ -179,6 +185,10 @@ int bkv_fps_prefill(const bkv_shape* s, const bkv_bf16* q_prompt, int32_t n_prom
     a.P = n_prompt;
     a.qcap = s->qcap;
     a.n_beacon = s->n_beacon;
+    a.src = src_of(s);
+    a.seed = s->seed;
+    a.lds_bytes = 0;
+    if (a.src != bkv::kSrcFps) return hip_status(bkv::launch_prefill_src(a, s->head_dim, (hipStream_t)stream));
     return hip_status(bkv::launch_prefill(a, s->head_dim, (hipStream_t)stream));
 }
 
@@ -251,16 +261,7 @@ int bkv_evict(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, bkv_b
     ea.n_recent_kv = s->n_recent_kv;
     if ((e = hip_status(bkv::launch_evict(ea, s->head_dim, st)))) return e;
 
-    bkv::FpsArgs fa;
-    fa.qbuf = qbuf;
-    fa.qcount = qcount;
-    fa.q_new = nullptr;
-    fa.q_recent = q_recent;
-    fa.fps_sel = fps_sel_out;
-    fa.nbuf = qbufs_of(s);
-    fa.qcap = s->qcap;
-    fa.n_beacon = s->n_beacon;
-    fa.n_recent_q = s->n_recent_q;
+    bkv::FpsArgs fa = fps_args(s, qbuf, qcount, nullptr, q_recent, fps_sel_out);
     return hip_status(bkv::launch_fps(fa, s->head_dim, true, st));
 }
 
@@ -308,16 +309,7 @@ int bkv_decode_step(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t L, con
         ra.slot = L - ring0;
         return hip_status(bkv::launch_ring(ra, s->head_dim, st));
     }
-    bkv::FpsArgs fa;
-    fa.qbuf = qbuf;
-    fa.qcount = qcount;
-    fa.q_new = q_new;
-    fa.q_recent = nullptr;
-    fa.fps_sel = fps_sel;
-    fa.nbuf = qbufs_of(s);
-    fa.qcap = s->qcap;
-    fa.n_beacon = s->n_beacon;
-    fa.n_recent_q = s->n_recent_q;
+    bkv::FpsArgs fa = fps_args(s, qbuf, qcount, q_new, nullptr, fps_sel);
     return hip_status(bkv::launch_fps(fa, s->head_dim, false, st));
 }
 

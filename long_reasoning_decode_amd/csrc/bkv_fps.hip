@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void append_q_kernel(FpsArgs a) {
 
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st) {
     if (a.nbuf <= 0) return hipSuccess;
+    if (a.src != kSrcFps) return merge ? launch_offer_merge(a, d, st) : launch_offer(a, d, st);
     if (!merge) {
         const int64_t threads = (int64_t)a.nbuf * (d / 8);
         dim3 g((unsigned)((threads + 255) / 256)), blk(256);

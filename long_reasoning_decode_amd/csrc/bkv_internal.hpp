@@ -15,7 +15,11 @@ struct FpsArgs {
     const bkv_bf16* q_recent;  // [nbuf][n_recent_q][d] (merge)
     int32_t* fps_sel;          // [nbuf][n_beacon] or null
     int nbuf, qcap, n_beacon, n_recent_q;
+    int src;                   // beacon source: kSrcFps, kSrcInitial, kSrcRandom
+    uint32_t seed;             // key of the random-history draws
 };
+
+constexpr int kSrcFps = 0, kSrcInitial = 1, kSrcRandom = 2;
 
 struct PrefillArgs {
     const bkv_bf16* q;         // [nbuf][P][d] prompt queries
@@ -23,6 +27,8 @@ struct PrefillArgs {
     int32_t* qcount;           // [nbuf]
     int32_t* fps_sel;          // [nbuf][n_beacon] or null
     int nbuf, P, qcap, n_beacon;
+    int src;                   // beacon source
+    uint32_t seed;
     int lds_bytes;             // LDS a workgroup may take (set at launch)
 };
 
@@ -79,6 +85,10 @@ struct RingArgs {
 
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t st);
+// initial / random beacon sources: one offer per buffer, the merge of the recents, the prefill
+hipError_t launch_offer(const FpsArgs& a, int d, hipStream_t st);
+hipError_t launch_offer_merge(const FpsArgs& a, int d, hipStream_t st);
+hipError_t launch_prefill_src(const PrefillArgs& a, int d, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, int d, hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 hipError_t launch_compact(const CompactArgs& a, int d, hipStream_t st);

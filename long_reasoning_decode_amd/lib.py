@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libbkv.so")
 
 BKV_CAUSAL_RECENT = 1
 BKV_POOL_MEAN = 2
+BKV_BEACON_INITIAL = 4
+BKV_BEACON_RANDOM = 8
 ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE", -4: "BKV_EHIP"}
 
 EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_fps_update",
@@ -32,7 +34,7 @@ EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_fps_update",
 class Shape(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim", "cap", "budget", "n_prefix",
-        "n_recent_kv", "n_beacon", "n_recent_q", "qcap")] + [("flags", C.c_uint32)]
+        "n_recent_kv", "n_beacon", "n_recent_q", "qcap")] + [("flags", C.c_uint32), ("seed", C.c_uint32)]
 
 
 class BkvError(RuntimeError):
@@ -81,14 +83,16 @@ def version() -> int:
 
 
 def flags_of(cfg: EvictConfig) -> int:
-    """Default flags of a workload: causal recent rows, and the pooling it names."""
-    return BKV_CAUSAL_RECENT | (BKV_POOL_MEAN if cfg.pool == "mean" else 0)
+    """Default flags of a workload: causal recent rows, and the pooling and beacon source it names."""
+    src = {"fps": 0, "initial": BKV_BEACON_INITIAL, "random": BKV_BEACON_RANDOM}[cfg.beacon]
+    return BKV_CAUSAL_RECENT | (BKV_POOL_MEAN if cfg.pool == "mean" else 0) | src
 
 
 def shape_of(cfg: EvictConfig, cap: Optional[int] = None, flags: Optional[int] = None) -> Shape:
     flags = flags_of(cfg) if flags is None else flags
     return Shape(cfg.n_layers, cfg.batch, cfg.hq, cfg.hkv, cfg.d, cfg.cap if cap is None else cap,
-                 cfg.budget, cfg.n_prefix, cfg.n_recent_kv, cfg.n_beacon, cfg.n_recent_q, cfg.qcap, flags)
+                 cfg.budget, cfg.n_prefix, cfg.n_recent_kv, cfg.n_beacon, cfg.n_recent_q, cfg.qcap, flags,
+                 cfg.seed & 0xFFFFFFFF)
 
 
 def _ptr(t: Optional[torch.Tensor], dtype, name: str):

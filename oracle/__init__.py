@@ -26,11 +26,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
+SRC_FPS, SRC_INITIAL, SRC_RANDOM = 0, 1, 2
+
 
 class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int) for n in (
         "n_layers", "batch", "hq", "hkv", "d", "cap", "budget", "n_prefix",
-        "n_recent_kv", "n_beacon", "n_recent_q", "causal", "qcap", "pool_mean")] + [("theta", C.c_double)]
+        "n_recent_kv", "n_beacon", "n_recent_q", "causal", "qcap", "pool_mean", "beacon_src")] + [
+        ("seed", C.c_uint), ("theta", C.c_double)]
 
 
 @dataclass
@@ -48,13 +51,16 @@ class OracleCfg:
     qcap: int = 32
     causal: int = 1
     pool_mean: int = 0
+    beacon_src: int = 0   # SRC_FPS, SRC_INITIAL or SRC_RANDOM
+    seed: int = 0
     n_layers: int = 1
     batch: int = 1
 
     def c(self) -> _Cfg:
         return _Cfg(self.n_layers, self.batch, self.hq, self.hkv, self.d, self.cap,
                     self.budget, self.n_prefix, self.n_recent_kv, self.n_beacon,
-                    self.n_recent_q, self.causal, self.qcap, self.pool_mean, float(self.theta))
+                    self.n_recent_q, self.causal, self.qcap, self.pool_mean, self.beacon_src,
+                    self.seed & 0xFFFFFFFF, float(self.theta))
 
     @property
     def G(self) -> int:
@@ -84,7 +90,11 @@ def lib():
         L.bkvo_fps_long.restype = i32
         L.bkvo_pairwise_sum.argtypes = [P, i32]
         L.bkvo_pairwise_sum.restype = C.c_float
-        L.bkvo_prefill.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
+        L.bkvo_prefill.argtypes = [i32, i32, i32, i32, i32, i32, C.c_uint, C.c_longlong, P, P, P, P]
+        L.bkvo_philox4x32_10.argtypes = [P, P, P]
+        L.bkvo_reservoir_slot.argtypes = [C.c_uint, C.c_longlong, i32, i32]
+        L.bkvo_reservoir_slot.restype = i32
+        L.bkvo_beacon_update.argtypes = [P, i32, C.c_longlong, P, P, P, P]
         L.bkvo_row_weights.argtypes = [P, P, i32, i32, i32, P]
         L.bkvo_row_weights.restype = C.c_double
         L.bkvo_select.argtypes = [P, i32, i32, i32, i32, P]
@@ -183,16 +193,41 @@ def pairwise_sum(x) -> float:
     return float(np.float32(lib().bkvo_pairwise_sum(_p(x), x.size)))
 
 
-def prefill(q_prompt, qbuf, qcount, n_beacon: int) -> np.ndarray:
+def philox4x32_10(ctr, key) -> list[int]:
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    lib().bkvo_philox4x32_10(_p(c), _p(k), _p(out))
+    return [int(v) for v in out]
+
+
+def reservoir_slot(seed: int, uq: int, n: int, n_beacon: int) -> int:
+    return lib().bkvo_reservoir_slot(seed & 0xFFFFFFFF, uq, n, n_beacon)
+
+
+def beacon_update(cfg: OracleCfg, qbuf, qcount, q_new, buf0: int = 0) -> np.ndarray:
+    """The per-step buffer update under cfg.beacon_src, in place on qbuf [nbuf, qcap, d], qcount [nbuf]."""
+    assert qbuf.dtype == np.uint16 and qbuf.flags["C_CONTIGUOUS"]
+    assert qcount.dtype == np.int32 and qcount.flags["C_CONTIGUOUS"]
+    nbuf = qbuf.shape[0]
+    q_new = _u16(q_new).reshape(nbuf, cfg.d)
+    sel = np.empty((nbuf, cfg.n_beacon), dtype=np.int32)
+    cc = cfg.c()
+    lib().bkvo_beacon_update(C.byref(cc), nbuf, buf0, _p(qbuf), _p(qcount), _p(q_new), _p(sel))
+    return sel
+
+
+def prefill(q_prompt, qbuf, qcount, n_beacon: int, src: int = SRC_FPS, seed: int = 0, buf0: int = 0) -> np.ndarray:
     """Prefill initialisation, in place on qbuf [nbuf, qcap, d] and qcount [nbuf] from q_prompt [nbuf, P, d];
-    returns the selection order [nbuf, n_beacon] (-1 past the last pick)."""
+    returns the selection order (FPS) or the prompt row of each slot [nbuf, n_beacon] (-1 past the last)."""
     assert qbuf.dtype == np.uint16 and qbuf.flags["C_CONTIGUOUS"]
     assert qcount.dtype == np.int32 and qcount.flags["C_CONTIGUOUS"]
     q_prompt = _u16(q_prompt)
     nbuf, P, d = q_prompt.shape
     assert qbuf.shape[0] == nbuf and qbuf.shape[2] == d and qcount.shape == (nbuf,)
     sel = np.empty((nbuf, n_beacon), dtype=np.int32)
-    lib().bkvo_prefill(nbuf, P, d, n_beacon, qbuf.shape[1], _p(q_prompt), _p(qbuf), _p(qcount), _p(sel))
+    lib().bkvo_prefill(nbuf, P, d, n_beacon, qbuf.shape[1], src, seed & 0xFFFFFFFF, buf0, _p(q_prompt), _p(qbuf),
+                       _p(qcount), _p(sel))
     return sel
 
 

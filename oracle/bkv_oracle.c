@@ -48,8 +48,14 @@ typedef struct {
     int causal;       /* recent query i sees only slots <= N - n_recent_q + i */
     int qcap;         /* rows allocated per query buffer (>= B_Q^max) */
     int pool_mean;    /* 0: max pooling (Eq. 7); 1: mean pooling (Eq. 6) */
+    int beacon_src;   /* 0: continual FPS; 1: initial queries; 2: random history (reservoir) */
+    unsigned seed;    /* key of the random-history draws */
     double theta;     /* RoPE base */
 } bkvo_cfg;
+
+enum { BKVO_SRC_FPS = 0, BKVO_SRC_INITIAL = 1, BKVO_SRC_RANDOM = 2 };
+
+int bkvo_reservoir_slot(unsigned seed, long long uq, int n, int n_beacon);
 
 /* ------------------------------------------------------------------------ */
 /* bf16 <-> fp32.                                                            */
@@ -374,28 +380,51 @@ int bkvo_fps_long(const uint16_t *X, int n, int d, int m, int *sel)
     return cnt;
 }
 
-/* Prefill initialisation of nbuf query buffers: buffer b becomes
- * FPS_long(q_prompt[b][0 .. P), n_beacon) with the survivors in ascending
- * prompt order, qcount[b] their number (min(P, n_beacon)), and
- * sel_out[b][i] (nullable) the i-th pick or -1 past the last.
+/* Prefill initialisation of nbuf query buffers (global indices from buf0)
+ * from their prompt queries q_prompt[b][0 .. P), under the beacon source src:
+ *   FPS     -- the buffer becomes FPS_long(prompt, n_beacon), survivors in
+ *              ascending prompt order, count min(P, n_beacon);
+ *   initial -- the first min(P, n_beacon) prompt rows, count min(P, n_beacon);
+ *   random  -- the prompt rows offered in order to the reservoir, count P.
+ * sel_out[b][i] (nullable): the i-th pick (FPS) or the prompt row held in
+ * slot i (the other sources), -1 past the last.
  * q_prompt: [nbuf][P][d]; qbuf: [nbuf][qcap][d]; qcount: [nbuf].           */
-void bkvo_prefill(int nbuf, int P, int d, int n_beacon, int qcap, const uint16_t *q_prompt,
-                  uint16_t *qbuf, int32_t *qcount, int32_t *sel_out)
+void bkvo_prefill(int nbuf, int P, int d, int n_beacon, int qcap, int src, unsigned seed, long long buf0,
+                  const uint16_t *q_prompt, uint16_t *qbuf, int32_t *qcount, int32_t *sel_out)
 {
     int *sel = (int *)malloc(sizeof(int) * (size_t)(n_beacon + 1));
     char *keep = (char *)malloc((size_t)(P > 0 ? P : 1));
     for (int b = 0; b < nbuf; ++b) {
-        const uint16_t *src = q_prompt + (size_t)b * P * d;
+        const uint16_t *src_rows = q_prompt + (size_t)b * P * d;
         uint16_t *buf = qbuf + (size_t)b * qcap * d;
-        int got = bkvo_fps_long(src, P, d, n_beacon, sel);
+        int got;
+        if (src == BKVO_SRC_FPS) {
+            got = bkvo_fps_long(src_rows, P, d, n_beacon, sel);
+            memset(keep, 0, (size_t)(P > 0 ? P : 1));
+            for (int i = 0; i < got; ++i) keep[sel[i]] = 1;
+            int w = 0;
+            for (int i = 0; i < P; ++i)
+                if (keep[i]) { memcpy(buf + (size_t)w * d, src_rows + (size_t)i * d, sizeof(uint16_t) * (size_t)d); ++w; }
+            qcount[b] = w;
+        } else if (src == BKVO_SRC_INITIAL) {
+            got = P < n_beacon ? P : n_beacon;
+            for (int i = 0; i < got; ++i) sel[i] = i;
+            memcpy(buf, src_rows, sizeof(uint16_t) * (size_t)got * d);
+            qcount[b] = got;
+        } else {
+            got = P < n_beacon ? P : n_beacon;
+            for (int i = 0; i < n_beacon; ++i) sel[i] = -1;
+            for (int n = 0; n < P; ++n) {
+                int j = bkvo_reservoir_slot(seed, buf0 + b, n, n_beacon);
+                if (j >= 0) {
+                    memcpy(buf + (size_t)j * d, src_rows + (size_t)n * d, sizeof(uint16_t) * (size_t)d);
+                    sel[j] = n;
+                }
+            }
+            qcount[b] = P;
+        }
         if (sel_out)
             for (int i = 0; i < n_beacon; ++i) sel_out[(size_t)b * n_beacon + i] = i < got ? sel[i] : -1;
-        memset(keep, 0, (size_t)(P > 0 ? P : 1));
-        for (int i = 0; i < got; ++i) keep[sel[i]] = 1;
-        int w = 0;
-        for (int i = 0; i < P; ++i)
-            if (keep[i]) { memcpy(buf + (size_t)w * d, src + (size_t)i * d, sizeof(uint16_t) * (size_t)d); ++w; }
-        qcount[b] = w;
     }
     free(sel);
     free(keep);
@@ -447,6 +476,89 @@ void bkvo_fps_update(int nbuf, int qcap, int d, int n_beacon, int n_recent_q,
     }
     free(sel);
     free(tmp);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Other sources of beacons (the ablations of Notes §3.2 Fig. 6 and §3.4
+ * Table 3), with the same buffer, count and cycle as continual FPS:
+ *   initial  -- Initial+Recent: the beacons are the first n_beacon queries the
+ *               buffer is offered and never change (later queries are
+ *               ignored; the merge keeps the buffer);
+ *   random   -- random history: the beacons are a uniform random sample of
+ *               n_beacon of all queries offered so far, kept by reservoir
+ *               sampling (Vitter's Algorithm R).  The count is the number of
+ *               queries offered; the n-th (0-based) goes to slot n while
+ *               n < n_beacon, else to slot j = floor(r (n + 1) / 2^32) if
+ *               j < n_beacon, with r a 32-bit draw.  Collection-phase queries
+ *               are offered as they come, the cycle's recent queries at the
+ *               merge, in ring order, so the beacons stay frozen while the
+ *               recents are collected (App. Alg. 2).
+ * The draws r are the first output word of Philox4x32-10 (Salmon, Moraes,
+ * Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) with
+ * counter (n, buffer index, 0, 0) and key (seed, 0).                       */
+
+/* Philox4x32-10: ten rounds; in each, the counter words (c0, c1, c2, c3)
+ * become (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)),
+ * and the key is then bumped by the Weyl constants. */
+void bkvo_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += W0; k1 += W1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Reservoir slot of the n-th query offered to buffer uq, or -1 (dropped). */
+int bkvo_reservoir_slot(unsigned seed, long long uq, int n, int n_beacon)
+{
+    if (n < n_beacon) return n;
+    uint32_t ctr[4] = {(uint32_t)n, (uint32_t)uq, 0u, 0u}, key[2] = {seed, 0u}, out[4];
+    bkvo_philox4x32_10(ctr, key, out);
+    uint32_t j = (uint32_t)(((uint64_t)out[0] * (uint64_t)((uint32_t)n + 1u)) >> 32);
+    return j < (uint32_t)n_beacon ? (int)j : -1;
+}
+
+/* Offer one pre-RoPE query to buffer uq (rows buf, count *cnt) under the
+ * initial or random rule. */
+static void offer(const bkvo_cfg *c, long long uq, uint16_t *buf, int32_t *cnt, const uint16_t *q)
+{
+    int d = c->d, n = *cnt < 0 ? 0 : *cnt;
+    if (c->beacon_src == BKVO_SRC_INITIAL) {
+        if (n < c->n_beacon) {
+            memcpy(buf + (size_t)n * d, q, sizeof(uint16_t) * (size_t)d);
+            *cnt = n + 1;
+        }
+        return;
+    }
+    int j = bkvo_reservoir_slot(c->seed, uq, n, c->n_beacon);
+    if (j >= 0) memcpy(buf + (size_t)j * d, q, sizeof(uint16_t) * (size_t)d);
+    *cnt = n + 1;
+}
+
+/* The per-step buffer update under the configured source, for nbuf buffers
+ * whose global indices start at buf0: continual FPS (bkvo_fps_update), or one
+ * offer per buffer.  sel_out (nullable) as for bkvo_fps_update (-1s when no
+ * sampling ran, always for the other sources). */
+void bkvo_beacon_update(const bkvo_cfg *c, int nbuf, long long buf0, uint16_t *qbuf, int32_t *qcount,
+                        const uint16_t *q_new, int32_t *sel_out)
+{
+    if (c->beacon_src == BKVO_SRC_FPS) {
+        bkvo_fps_update(nbuf, c->qcap, c->d, c->n_beacon, c->n_recent_q, qbuf, qcount, q_new, sel_out);
+        return;
+    }
+    for (int b = 0; b < nbuf; ++b) {
+        offer(c, buf0 + b, qbuf + (size_t)b * c->qcap * c->d, qcount + b, q_new + (size_t)b * c->d);
+        if (sel_out)
+            for (int i = 0; i < c->n_beacon; ++i) sel_out[(size_t)b * c->n_beacon + i] = -1;
+    }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -633,6 +745,19 @@ static void merge_unit(const bkvo_cfg *c, int u, uint16_t *qbuf, int32_t *qcount
                        const uint16_t *q_recent, int32_t *fps_sel)
 {
     int d = c->d, G = c->hq / c->hkv;
+    if (c->beacon_src != BKVO_SRC_FPS) {
+        /* initial: nothing changes; random: the recents are offered in ring order */
+        for (int h = 0; h < G; ++h) {
+            size_t b = (size_t)u * G + h;
+            if (c->beacon_src == BKVO_SRC_RANDOM)
+                for (int i = 0; i < c->n_recent_q; ++i)
+                    offer(c, (long long)b, qbuf + b * c->qcap * d, qcount + b,
+                          q_recent + (b * c->n_recent_q + i) * d);
+            if (fps_sel)
+                for (int i = 0; i < c->n_beacon; ++i) fps_sel[b * c->n_beacon + i] = -1;
+        }
+        return;
+    }
     int nmax = c->n_beacon + c->n_recent_q;
     uint16_t *X = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(nmax + 1) * d);
     int *sel = (int *)malloc(sizeof(int) * (size_t)(nmax + 1));
@@ -810,8 +935,8 @@ static void *run_stream_units(void *arg)
             memcpy(Vu + (size_t)L * d, J->v_new + su * d, sizeof(uint16_t) * (size_t)d);
             const uint16_t *qn = J->q_new + su * G * d;
             if (L < ring0) {
-                bkvo_fps_update(G, c->qcap, d, c->n_beacon, nrq, J->qbuf + (size_t)u * G * c->qcap * d,
-                                J->qcount + (size_t)u * G, qn, NULL);
+                bkvo_beacon_update(c, G, (long long)u * G, J->qbuf + (size_t)u * G * c->qcap * d,
+                                   J->qcount + (size_t)u * G, qn, NULL);
             } else {
                 int i = L - ring0;
                 for (int h = 0; h < G; ++h)

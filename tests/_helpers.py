@@ -24,7 +24,17 @@ def ocfg(cfg: EvictConfig, n_len: int | None = None, flags: int | None = None) -
                        n_prefix=cfg.n_prefix, n_recent_kv=cfg.n_recent_kv, n_beacon=cfg.n_beacon,
                        n_recent_q=cfg.n_recent_q, theta=cfg.theta, qcap=cfg.qcap,
                        causal=int(bool(flags & L.BKV_CAUSAL_RECENT)), pool_mean=int(bool(flags & L.BKV_POOL_MEAN)),
+                       beacon_src=src_of(flags), seed=cfg.seed & 0xFFFFFFFF,
                        n_layers=cfg.n_layers, batch=cfg.batch)
+
+
+def src_of(flags: int) -> int:
+    """The oracle's beacon source for library flags."""
+    if flags & L.BKV_BEACON_INITIAL:
+        return O.SRC_INITIAL
+    if flags & L.BKV_BEACON_RANDOM:
+        return O.SRC_RANDOM
+    return O.SRC_FPS
 
 
 def rope_dev(cfg: EvictConfig) -> torch.Tensor:

@@ -14,7 +14,9 @@ def stream_ocfg(scfg: StreamConfig) -> O.OracleCfg:
     b = scfg.base
     return O.OracleCfg(hq=b.hq, hkv=b.hkv, d=b.d, cap=b.cap, budget=b.budget, n_prefix=b.n_prefix,
                        n_recent_kv=b.n_recent_kv, n_beacon=b.n_beacon, n_recent_q=b.n_recent_q, theta=b.theta,
-                       qcap=b.qcap, pool_mean=int(b.pool == "mean"), n_layers=b.n_layers, batch=b.batch)
+                       qcap=b.qcap, pool_mean=int(b.pool == "mean"),
+                       beacon_src={"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM}[b.beacon],
+                       seed=b.seed & 0xFFFFFFFF, n_layers=b.n_layers, batch=b.batch)
 
 
 def empty_state(scfg: StreamConfig, U: int) -> dict:

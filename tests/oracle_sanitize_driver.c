@@ -60,8 +60,10 @@ static void run_case(int hq, int hkv, int d, int N, int budget, int npf, int nrk
     bkvo_fps(qbuf, 1, d, 1, sel32);
     bkvo_fps(qbuf, 5, d, 0, sel32);
 
-    /* a short stream from an empty cache */
-    if (S > 0) {
+    /* a short stream from an empty cache, under each source of beacons */
+    for (int src = 0; src < 3 && S > 0; ++src) {
+        c.beacon_src = src;
+        c.seed = 99u;
         uint16_t *kn = malloc((size_t)S * U * d * 2), *vn = malloc((size_t)S * U * d * 2);
         uint16_t *qs = malloc((size_t)S * U * G * d * 2);
         int32_t *ps = malloc(sizeof(int32_t) * S * U);
@@ -126,7 +128,7 @@ int main(void)
         uint16_t *qp = malloc((size_t)3 * (P1 > 0 ? P1 : 1) * 64 * 2), *qb = malloc((size_t)3 * 32 * 64 * 2);
         int32_t qcnt[3], sl[3 * 16];
         fill_bf16(qp, (size_t)3 * (P1 > 0 ? P1 : 1) * 64, 2.0f);
-        bkvo_prefill(3, P1, 64, 16, 32, qp, qb, qcnt, sl);
+        for (int src = 0; src < 3; ++src) bkvo_prefill(3, P1, 64, 16, 32, src, 7u, 5, qp, qb, qcnt, sl);
         free(qp); free(qb);
     }
     float ps[5] = {1.0f, 2.0f, 3.0f, 4.0f, 5.0f};

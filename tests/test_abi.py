@@ -42,15 +42,15 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strerror(so):
-    assert L.version() == 3
+    assert L.version() == 4
     for code in (0, -1, -2, -3, -4):
         assert len(L.strerror(code)) > 0
     assert L.strerror(-99) == "unknown error"
 
 
 def test_shape_struct_layout():
-    # 12 int32 fields and one uint32, no padding
-    assert C.sizeof(L.Shape) == 13 * 4
+    # 12 int32 fields and two uint32, no padding
+    assert C.sizeof(L.Shape) == 14 * 4
 
 
 def test_rope_table_matches_oracle(so):
@@ -85,7 +85,8 @@ MISALIGNED = C.c_void_p(0x10002)
 
 @pytest.mark.parametrize("field,value,code", [
     ("head_dim", 96, -2), ("n_q_heads", 5, -1), ("n_kv_heads", 0, -1), ("n_q_heads", 18, -2),
-    ("n_beacon", 20, -2), ("qcap", 16, -1), ("flags", 4, -1), ("cap", 0, -1), ("n_beacon", -1, -1),
+    ("n_beacon", 20, -2), ("qcap", 16, -1), ("flags", 16, -1), ("flags", 12, -1), ("cap", 0, -1),
+    ("n_beacon", -1, -1),
 ])
 def test_shape_validation(so, field, value, code):
     s = _shape(**{field: value})

@@ -321,6 +321,128 @@ def test_prefill_buffers():
                 assert ref == list(range(P))
 
 
+# --------------------------------------------------------------------------
+# Other sources of beacons (Notes §3.2 Fig. 6 random history, §3.4 Table 3 Initial+Recent).
+
+def test_philox_known_answers():
+    """Philox4x32-10 known-answer values published with the generator (Salmon, Moraes, Dror, Shaw,
+    "Parallel random numbers: as easy as 1, 2, 3", SC 2011; counter, key -> output)."""
+    cases = [
+        ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+        ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+        ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+         (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+    ]
+    for ctr, key, want in cases:
+        assert O.philox4x32_10(ctr, key) == list(want)
+
+
+def test_reservoir_slot_fill_and_inclusion_rate():
+    nb = 16
+    for n in range(nb):
+        assert O.reservoir_slot(5, 3, n, nb) == n
+    # Algorithm R: the n-th offer (n >= nb) is kept with probability nb / (n + 1), into a uniform slot
+    rng = np.random.default_rng(40)
+    for n in (16, 40, 1000):
+        trials = 20000
+        js = np.array([O.reservoir_slot(int(rng.integers(0, 2**32)), int(u), n, nb) for u in range(trials)])
+        p = nb / (n + 1)
+        kept = (js >= 0).mean()
+        assert abs(kept - p) < 5 * math.sqrt(p * (1 - p) / trials)
+        counts = np.bincount(js[js >= 0], minlength=nb)
+        assert counts.min() > 0 and js.max() < nb
+        exp = (js >= 0).sum() / nb
+        assert ((counts - exp) ** 2 / exp).sum() < 60          # chi-square, 15 dof, far tail
+
+
+def _src_cfg(src, **kw):
+    base = dict(hq=2, hkv=1, d=16, cap=40, budget=30, n_prefix=2, n_recent_kv=3, n_beacon=4, n_recent_q=3,
+                theta=1e4, qcap=8, beacon_src=src, seed=1234)
+    base.update(kw)
+    return O.OracleCfg(**base)
+
+
+def test_initial_source_keeps_the_first_queries():
+    cfg = _src_cfg(O.SRC_INITIAL)
+    rng = np.random.default_rng(41)
+    qbuf = np.zeros((2, cfg.qcap, cfg.d), np.uint16)
+    qc = np.zeros(2, np.int32)
+    qs = bf16(rng.standard_normal((20, 2, cfg.d)))
+    for s in range(20):
+        sel = O.beacon_update(cfg, qbuf, qc, qs[s])
+        assert np.all(sel == -1)
+        assert qc.tolist() == [min(s + 1, cfg.n_beacon)] * 2
+    for b in range(2):
+        assert np.array_equal(qbuf[b, :cfg.n_beacon], qs[:cfg.n_beacon, b])
+
+
+def test_random_source_is_a_reservoir_of_the_offers():
+    """Every kept row is one of the offered queries, each offer at most once; the count is the number of
+    offers; and over many buffers each offer is kept with probability n_beacon / offers."""
+    cfg = _src_cfg(O.SRC_RANDOM)
+    nbuf, S = 400, 50
+    rng = np.random.default_rng(42)
+    # offer s of buffer b is the row whose first element encodes s (distinct, exactly representable)
+    qs = np.zeros((S, nbuf, cfg.d), np.float32)
+    qs[:, :, 0] = np.arange(1, S + 1)[:, None]
+    qs[:, :, 1:] = rng.standard_normal((S, nbuf, cfg.d - 1))
+    qs = bf16(qs)
+    qbuf = np.zeros((nbuf, cfg.qcap, cfg.d), np.uint16)
+    qc = np.zeros(nbuf, np.int32)
+    for s in range(S):
+        O.beacon_update(cfg, qbuf, qc, qs[s])
+    assert np.all(qc == S)
+    ids = f32(qbuf[:, :cfg.n_beacon, 0]).astype(int) - 1
+    hits = np.zeros(S)
+    for b in range(nbuf):
+        assert len(set(ids[b].tolist())) == cfg.n_beacon and ids[b].min() >= 0
+        for k, i in enumerate(ids[b]):
+            assert np.array_equal(qbuf[b, k], qs[i, b])
+        hits[ids[b]] += 1
+    p = cfg.n_beacon / S
+    assert np.all(np.abs(hits / nbuf - p) < 5 * math.sqrt(p * (1 - p) / nbuf))
+
+
+def test_merge_under_other_sources():
+    rng = np.random.default_rng(43)
+    for src in (O.SRC_INITIAL, O.SRC_RANDOM):
+        cfg = _src_cfg(src)
+        qbuf = np.ascontiguousarray(bf16(rng.standard_normal((1, cfg.G, cfg.qcap, cfg.d))))
+        qc = np.full((1, cfg.G), 6 if src == O.SRC_RANDOM else 4, np.int32)
+        qr = bf16(rng.standard_normal((1, cfg.G, cfg.n_recent_q, cfg.d)))
+        want_buf, want_qc = qbuf.copy(), qc.copy()
+        if src == O.SRC_RANDOM:   # the recents are offered in ring order
+            for i in range(cfg.n_recent_q):
+                O.beacon_update(cfg, want_buf[0], want_qc[0], qr[0, :, i])
+        sel = O.merge(cfg, qbuf, qc, qr)
+        assert np.all(sel == -1)
+        assert np.array_equal(qbuf, want_buf) and np.array_equal(qc, want_qc)
+
+
+def test_prefill_other_sources():
+    rng = np.random.default_rng(44)
+    nb, d = 16, 32
+    for P in (0, 7, 300):
+        q = bf16(rng.standard_normal((3, P, d)))
+        qbuf = np.zeros((3, 32, d), np.uint16)
+        qc = np.zeros(3, np.int32)
+        sel = O.prefill(q, qbuf, qc, nb, src=O.SRC_INITIAL)
+        m = min(P, nb)
+        assert np.all(qc == m) and np.array_equal(qbuf[:, :m], q[:, :m])
+        assert np.all(sel[:, :m] == np.arange(m)) and np.all(sel[:, m:] == -1)
+        # random: the same as offering the prompt rows one by one
+        cfg = _src_cfg(O.SRC_RANDOM, d=d, n_beacon=nb, qcap=32, seed=77)
+        qbuf2, qc2 = np.zeros((3, 32, d), np.uint16), np.zeros(3, np.int32)
+        sel = O.prefill(q, qbuf2, qc2, nb, src=O.SRC_RANDOM, seed=77)
+        wb, wc = np.zeros((3, 32, d), np.uint16), np.zeros(3, np.int32)
+        for n in range(P):
+            O.beacon_update(cfg, wb, wc, q[:, n])
+        assert np.array_equal(qc2, wc) and np.array_equal(qbuf2[:, :m], wb[:, :m])
+        for b in range(3):
+            for k in range(m):
+                assert np.array_equal(qbuf2[b, k], q[b, sel[b, k]])
+
+
 def test_fps_update_continual_buffer():
     """Eq. 9: append; at B_Q^max rows the buffer becomes FPS(buffer, n_beacon)
     in ascending slot order with count n_beacon; below it, only the append."""

@@ -106,6 +106,51 @@ def test_fps_update_many_random_buffers(cfg):
     assert np.array_equal(g[:, :cfgx.n_beacon], qbuf_h[:, :cfgx.n_beacon])
 
 
+@pytest.mark.parametrize("src", ["initial", "random"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_source_update_matches_oracle(src, d):
+    """Initial and random-history beacons: three successive per-step updates from mixed counts."""
+    rng = np.random.default_rng(300 + d + len(src))
+    cfg = TINY.scaled(d=d, n_layers=3, batch=5, hq=8, hkv=2, beacon=src, seed=4242 + d)
+    nbuf, qcap = cfg.qbufs, cfg.qcap
+    oc = H.ocfg(cfg)
+    qbuf_h = synth.to_u16(torch.from_numpy(rng.standard_normal((nbuf, qcap, d)).astype(np.float32))
+                          .to(torch.bfloat16)).copy()
+    qc_h = rng.integers(-2, 40, size=nbuf).astype(np.int32)
+    qc_h[::9] = 1000 + rng.integers(0, 5000, size=len(qc_h[::9]))
+    qbuf_d = torch.from_numpy(qbuf_h.view(np.int16)).cuda().view(torch.bfloat16)
+    qc_d = torch.from_numpy(qc_h.copy()).cuda()
+    shape = L.shape_of(cfg)
+    for step in range(3):
+        qn = torch.from_numpy(rng.standard_normal((nbuf, d)).astype(np.float32)).to(torch.bfloat16)
+        sel_o = O.beacon_update(oc, qbuf_h, qc_h, synth.to_u16(qn))
+        sel_d = torch.full((nbuf, cfg.n_beacon), -7, dtype=torch.int32, device="cuda")
+        L.fps_update(shape, qbuf_d, qc_d, qn.cuda(), sel_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(qc_d.cpu().numpy(), qc_h), step
+        assert np.array_equal(sel_d.cpu().numpy(), sel_o), step
+        assert np.array_equal(synth.to_u16(qbuf_d), qbuf_h), step
+
+
+@pytest.mark.parametrize("src", ["initial", "random"])
+def test_source_merge_matches_oracle(src):
+    cfg = QWEN3_4B.scaled(n_layers=2, batch=3, beacon=src, seed=777)
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    qc = inp["qcount"].clone()
+    qc.view(-1)[::5] = 3
+    qc.view(-1)[1::7] = 5000
+    v = synth.oracle_views(cfg, {**inp, "qcount": qc})
+    sel_o = O.merge(H.ocfg(cfg), v["qbuf"], v["qcount"], v["q_recent"])
+    qbuf = inp["qbuf"].clone()
+    sel_d = torch.full((cfg.qbufs, cfg.n_beacon), -7, dtype=torch.int32, device="cuda")
+    L.fps_merge(L.shape_of(cfg), qbuf, qc, inp["q_recent"], sel_d)
+    torch.cuda.synchronize()
+    G = cfg.G
+    assert np.array_equal(sel_d.cpu().numpy().reshape(cfg.units, G, -1), sel_o)
+    assert np.array_equal(qc.cpu().numpy().reshape(cfg.units, G), v["qcount"])
+    assert np.array_equal(synth.to_u16(qbuf).reshape(cfg.units, G, cfg.qcap, cfg.d), v["qbuf"])
+
+
 @pytest.mark.parametrize("qcount", [16, 9, 0, 20])
 def test_fps_merge_matches_oracle(qcount):
     cfg = QWEN3_4B.scaled(n_layers=2, batch=3)
@@ -277,6 +322,10 @@ EVICT_CASES = [
     (TINY.scaled(n_beacon=0, name="nb0"), 160, 1),
     # the longest cache the kernels take (8192 keys)
     (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 1),
+    # initial / random-history beacons (flags 5: causal + initial, 9: causal + random)
+    (TINY.scaled(seed=91), None, 5),
+    (TINY.scaled(seed=92), None, 9),
+    (QWEN3_4B.scaled(n_layers=2, batch=2), None, 9),
     # mean pooling (flags 3: causal + mean, 2: mean alone)
     (TINY, None, 3),
     (TINY, 150, 2),

@@ -89,6 +89,23 @@ def test_prefill_ties(d, P):
     _check(cfg, q, P, where=f"ties d={d} P={P}")
 
 
+@pytest.mark.parametrize("src", ["initial", "random"])
+@pytest.mark.parametrize("P", [0, 9, 16, 300, 5000])
+def test_prefill_other_sources(src, P):
+    cfg = SMALL.scaled(d=128, beacon=src, seed=31 + P)
+    _flush(f"prefill {src} P={P}")
+    q = synth.make_prompt_queries(cfg, P, device="cuda", seed=500 + P)
+    g_buf, g_qc, g_sel = _run(cfg, q, P)
+    qn = synth.to_u16(q).reshape(cfg.qbufs, P, cfg.d)
+    ob = np.full((cfg.qbufs, cfg.qcap, cfg.d), 0x7F7F, np.uint16)
+    oc = np.zeros(cfg.qbufs, np.int32)
+    osel = O.prefill(qn, ob, oc, cfg.n_beacon, src={"initial": O.SRC_INITIAL, "random": O.SRC_RANDOM}[src],
+                     seed=cfg.seed)
+    assert np.array_equal(g_qc, oc)
+    assert np.array_equal(g_sel, osel)
+    assert np.array_equal(g_buf, ob)
+
+
 def test_prefill_full_size_sampled_buffers():
     """The benchmark's workload (every query head of the Qwen3-4B-shaped batch, 1024-query prompts), same
     launch; the oracle checks a sample of buffers."""

@@ -8,7 +8,8 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import STREAM, TINY_STREAM, TINY_STREAM_1R31B, TINY_STREAM_MEAN
+from long_reasoning_decode_amd.configs import (STREAM, TINY_STREAM, TINY_STREAM_MEAN, TINY_STREAM_SOURCES,
+                                               TINY_STREAM_SPLITS)
 from long_reasoning_decode_amd.stream import StreamRun
 
 from _stream_helpers import compare_stream, replay
@@ -62,14 +63,25 @@ def test_stream_tiny_resumes_across_calls():
     _check(scfg, run, units, "stream-tiny resumed")
 
 
-def test_stream_tiny_one_recent_31_beacons():
-    """The 1 recent + 31 beacon split: a sampling round after every collection step."""
-    scfg = TINY_STREAM_1R31B
+@pytest.mark.parametrize("scfg", TINY_STREAM_SPLITS, ids=lambda c: c.name)
+def test_stream_tiny_recent_beacon_splits(scfg):
+    """The recent/beacon splits of the 32 observation queries; with 1 recent query a sampling round follows
+    every collection step, with none (all recent) the buffers keep no beacons."""
     units = range(scfg.base.units)
     run = StreamRun(scfg, record_units=units, block=64)
     run.run()
-    assert run.fps_rounds_per_buffer() > 0.8 * scfg.steps   # nearly every step samples
-    _check(scfg, run, units, "stream-tiny 1r31b")
+    if scfg.base.n_recent_q == 1:
+        assert run.fps_rounds_per_buffer() > 0.8 * scfg.steps   # nearly every step samples
+    _check(scfg, run, units, scfg.name)
+
+
+@pytest.mark.parametrize("scfg", TINY_STREAM_SOURCES, ids=lambda c: c.name)
+def test_stream_tiny_beacon_sources(scfg):
+    """The whole cycle with the initial queries or a random sample of the history as beacons."""
+    units = range(scfg.base.units)
+    run = StreamRun(scfg, record_units=units, block=64)
+    run.run()
+    _check(scfg, run, units, scfg.name)
 
 
 def test_stream_tiny_mean_pooling():

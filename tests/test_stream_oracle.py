@@ -9,7 +9,8 @@ import pytest
 
 import oracle as O
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import TINY_STREAM, TINY_STREAM_1R31B, TINY_STREAM_MEAN
+from long_reasoning_decode_amd.configs import (TINY_STREAM, TINY_STREAM_MEAN, TINY_STREAM_SOURCES,
+                                               TINY_STREAM_SPLITS)
 
 from _stream_helpers import empty_state, replay, stream_ocfg
 
@@ -26,7 +27,8 @@ def _inputs(scfg, S, seed=None):
             "pos": np.ascontiguousarray(blk["pos"].numpy()[:, b_of]).astype(np.int32)}
 
 
-@pytest.mark.parametrize("scfg", [TINY_STREAM, TINY_STREAM_1R31B, TINY_STREAM_MEAN], ids=lambda c: c.name)
+@pytest.mark.parametrize("scfg", (TINY_STREAM, TINY_STREAM_MEAN) + TINY_STREAM_SPLITS + TINY_STREAM_SOURCES,
+                         ids=lambda c: c.name)
 def test_stream_equals_composition_of_calls(scfg):
     b = scfg.base
     S = 260    # first eviction after 160 steps, then every 32
@@ -43,7 +45,7 @@ def test_stream_equals_composition_of_calls(scfg):
             st["K"][u, L] = O.rope_row(x["k_new"][s, u], b.theta, int(x["pos"][s, u]))
             st["V"][u, L] = x["v_new"][s, u]
             if L < ring0:
-                O.fps_update(st["qbuf"][u], st["qcount"][u], x["q_new"][s, u], b.n_beacon, b.n_recent_q)
+                O.beacon_update(oc, st["qbuf"][u], st["qcount"][u], x["q_new"][s, u], buf0=u * b.G)
             else:
                 st["q_recent"][u, :, L - ring0] = x["q_new"][s, u]
                 st["pos_recent"][u, L - ring0] = x["pos"][s, u]
