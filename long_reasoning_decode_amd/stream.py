@@ -154,9 +154,12 @@ class StreamRun:
 
     def fps_rounds_per_buffer(self, steps: int | None = None) -> int:
         """Sampling rounds each query buffer goes through in `steps` decode steps from an empty state
-        (the count evolves the same way in every buffer)."""
+        (the count evolves the same way in every buffer).  Only continual FPS samples; the other beacon
+        sources never do."""
         b = self.base
         steps = self.scfg.steps if steps is None else steps
+        if b.beacon != "fps":
+            return 0
         bqmax, ring0 = b.n_beacon + b.n_recent_q, b.cap - b.n_recent_q
         L = qc = rounds = 0
         for _ in range(steps):
