@@ -95,6 +95,7 @@ def lib():
         L.bkvo_reservoir_slot.argtypes = [C.c_uint, C.c_longlong, i32, i32]
         L.bkvo_reservoir_slot.restype = i32
         L.bkvo_beacon_update.argtypes = [P, i32, C.c_longlong, P, P, P, P]
+        L.bkvo_decode_attention.argtypes = [P, i32, i32, P, P, P, P, P, P]
         L.bkvo_row_weights.argtypes = [P, P, i32, i32, i32, P]
         L.bkvo_row_weights.restype = C.c_double
         L.bkvo_select.argtypes = [P, i32, i32, i32, i32, P]
@@ -304,6 +305,18 @@ def compact(cfg: OracleCfg, K, V, idx, n_len: int | None = None) -> None:
     N = cfg.cap if n_len is None else n_len
     cc = cfg.c()
     lib().bkvo_compact(C.byref(cc), U, N, _p(K), _p(V), _p(_i32(idx)))
+
+
+def decode_attention(cfg: OracleCfg, K, V, q, pos, n_len: int):
+    """One decode step's attention: K, V [U, cap, d] (uint16 bf16, K post-RoPE), q [U, G, d] pre-RoPE, pos [U]
+    (the position q is rotated to).  Returns (out, scale) [U, G, d] fp64."""
+    K, V, q = _u16(K), _u16(V), _u16(q)
+    U = K.shape[0]
+    out = np.empty((U, cfg.G, cfg.d), dtype=np.float64)
+    scale = np.empty_like(out)
+    cc = cfg.c()
+    lib().bkvo_decode_attention(C.byref(cc), U, n_len, _p(K), _p(V), _p(q), _p(_i32(pos)), _p(out), _p(scale))
+    return out, scale
 
 
 def stream(cfg: OracleCfg, k_new, v_new, q_new, pos, K, V, L: int, qbuf, qcount, q_recent, pos_recent,

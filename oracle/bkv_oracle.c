@@ -1004,4 +1004,42 @@ int bkvo_stream(const bkvo_cfg *cfg, int U, int S, const uint16_t *k_new, const 
     return n_ev;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Decode attention of one step over the (compressed) cache (Notes §2.1, the
+ * second formula: the new token's query attends over [K || k] and takes the
+ * softmax-weighted sum of [V || v]; the new key and value are already rows of
+ * the cache).  For query buffer uq = u * G + h, the bf16 pre-RoPE query
+ * q[uq] is rotated to the unit's position pos[u] (bkvo_rope_row) and
+ *   out[uq][k] = sum_{j < L} w_j V[u][j][k],  w = softmax_j(q . K[u][j] / sqrt(d)),
+ * in fp64 (bkvo_row_weights).  scale[uq][k] = sum_j w_j |V[u][j][k]|, the
+ * magnitude against which an fp32 evaluation's rounding is judged.
+ * K, V: [U][cap][d]; q: [U][G][d]; out, scale: [U][G][d].                   */
+void bkvo_decode_attention(const bkvo_cfg *c, int U, int L, const uint16_t *K, const uint16_t *V,
+                           const uint16_t *q, const int32_t *pos, double *out, double *scale)
+{
+    int d = c->d, G = c->hq / c->hkv;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    uint16_t *qr = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+    for (int u = 0; u < U; ++u) {
+        const uint16_t *Ku = K + (size_t)u * c->cap * d, *Vu = V + (size_t)u * c->cap * d;
+        for (int h = 0; h < G; ++h) {
+            size_t uq = (size_t)u * G + h;
+            bkvo_rope_row(q + uq * d, d, c->theta, pos[u], qr);
+            bkvo_row_weights(qr, Ku, L, d, L - 1, w);
+            for (int k = 0; k < d; ++k) {
+                double acc = 0.0, mag = 0.0;
+                for (int j = 0; j < L; ++j) {
+                    double v = (double)bf2f(Vu[(size_t)j * d + k]);
+                    acc += w[j] * v;
+                    mag += w[j] * fabs(v);
+                }
+                out[uq * d + k] = acc;
+                if (scale) scale[uq * d + k] = mag;
+            }
+        }
+    }
+    free(w);
+    free(qr);
+}
+
 int bkvo_cfg_size(void) { return (int)sizeof(bkvo_cfg); }

@@ -131,6 +131,17 @@ int main(void)
         for (int src = 0; src < 3; ++src) bkvo_prefill(3, P1, 64, 16, 32, src, 7u, 5, qp, qb, qcnt, sl);
         free(qp); free(qb);
     }
+    {   /* decode attention, including a one-row cache */
+        bkvo_cfg c;
+        memset(&c, 0, sizeof c);
+        c.hq = 4; c.hkv = 2; c.d = 64; c.cap = 30; c.theta = 10000.0;
+        uint16_t K[2 * 30 * 64], V[2 * 30 * 64], q[4 * 64];
+        int32_t pos[2] = {5, 40};
+        double o[4 * 64], sc[4 * 64];
+        fill_bf16(K, sizeof K / 2, 2.0f); fill_bf16(V, sizeof V / 2, 1.0f); fill_bf16(q, sizeof q / 2, 2.0f);
+        bkvo_decode_attention(&c, 2, 30, K, V, q, pos, o, sc);
+        bkvo_decode_attention(&c, 2, 1, K, V, q, pos, o, NULL);
+    }
     float ps[5] = {1.0f, 2.0f, 3.0f, 4.0f, 5.0f};
     bkvo_pairwise_sum(ps, 5);
     bkvo_pairwise_sum(ps, 0);

@@ -626,6 +626,48 @@ def test_no_beacons_reduces_to_recent_only():
 
 
 # --------------------------------------------------------------------------
+# Decode attention over the cache (Notes §2.1, the second formula).
+
+def _attn_inputs(rng, U, G, N, d, cap=None):
+    cap = N if cap is None else cap
+    K = bf16(rng.standard_normal((U, cap, d)) * np.where(rng.random((U, cap, 1)) < 0.05, 6, 1))
+    V = bf16(rng.standard_normal((U, cap, d)))
+    q = bf16(rng.standard_normal((U, G, d)) * 1.5)
+    pos = rng.integers(0, 5000, size=U).astype(np.int32)
+    return K, V, q, pos
+
+
+def test_decode_attention_is_softmax_times_values():
+    rng = np.random.default_rng(50)
+    cfg = _cfg(hq=6, hkv=2, cap=70)
+    K, V, q, pos = _attn_inputs(rng, 3, cfg.G, 70, cfg.d)
+    for N in (70, 33, 1):
+        out, scale = O.decode_attention(cfg, K, V, q, pos, N)
+        for u in range(3):
+            Kf, Vf = f32(K[u, :N]).astype(np.float64), f32(V[u, :N]).astype(np.float64)
+            for h in range(cfg.G):
+                qr = f32(O.rope_row(q[u, h], cfg.theta, int(pos[u]))).astype(np.float64)
+                w = scipy.special.softmax(Kf @ qr / math.sqrt(cfg.d))
+                assert np.allclose(out[u, h], w @ Vf, rtol=1e-12, atol=1e-14)
+                assert np.allclose(scale[u, h], w @ np.abs(Vf), rtol=1e-12, atol=1e-14)
+        if N == 1:   # one row: its value, whatever the query
+            assert np.array_equal(out, np.repeat(f32(V[:, :1]).astype(np.float64), cfg.G, axis=1))
+
+
+def test_decode_attention_special_cases():
+    rng = np.random.default_rng(51)
+    cfg = _cfg(hq=2, hkv=1, cap=40)
+    K, V, q, pos = _attn_inputs(rng, 2, cfg.G, 40, cfg.d)
+    # identical keys: uniform weights, the mean of the values
+    Ks = np.repeat(K[:, :1], 40, axis=1)
+    out, _ = O.decode_attention(cfg, np.ascontiguousarray(Ks), V, q, pos, 40)
+    assert np.allclose(out, f32(V).astype(np.float64).mean(axis=1)[:, None, :], rtol=1e-12, atol=1e-14)
+    # a zero query: uniform weights too
+    out0, _ = O.decode_attention(cfg, K, V, np.zeros_like(q), pos, 25)
+    assert np.allclose(out0, f32(V[:, :25]).astype(np.float64).mean(axis=1)[:, None, :], rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
 # Keep set.
 
 def _select_ref(s, B, npf, nr):
