@@ -243,6 +243,28 @@ int bkv_decode_step(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t L,
                     bkv_bf16 *q_recent, int32_t *pos_recent,
                     const float *rope_cs, int32_t rope_rows, int32_t *fps_sel, void *stream);
 
+/* Append of one decode step's key and value (the cache growth of Notes §2.1,
+ * the second formula): per unit, K[u][L] = k_new[u] rotated to pos[b] (fp32,
+ * each product and sum rounded, then bf16 round to nearest even) and V[u][L]
+ * = v_new[u].  k_new, v_new: bf16 [units][head_dim] (k_new pre-RoPE); pos:
+ * int32 [batch], clamped to [0, rope_rows).  This is the first half of
+ * bkv_decode_step, for callers that run the plain decode loop (no
+ * eviction).  Errors: BKV_ERANGE (L < 0, L >= cap, rope_rows <= 0). */
+int bkv_append_kv(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t L, const bkv_bf16 *k_new,
+                  const bkv_bf16 *v_new, const int32_t *pos, const float *rope_cs, int32_t rope_rows,
+                  void *stream);
+
+/* One decode step's attention over the cache (Notes §2.1, the second
+ * formula; the new key and value already appended): for every query buffer
+ * uq = u * G + h, q[uq] (bf16 pre-RoPE, [qbufs][head_dim]) is rotated to
+ * pos[b] as the scoring queries are, and
+ *   out[uq][k] = sum_{j < n_len} w_j V[u][j][k],  w = softmax_j(q . K[u][j] / sqrt(head_dim)),
+ * fp32 [qbufs][head_dim].  Logits by bf16 MFMA with fp32 accumulation, the
+ * rest in fp32.  Errors: BKV_ERANGE (n_len < 1 or > cap, rope_rows <= 0). */
+int bkv_decode_attention(const bkv_shape *shape, const bkv_bf16 *K, const bkv_bf16 *V, int32_t n_len,
+                         const bkv_bf16 *q, const int32_t *pos, const float *rope_cs, int32_t rope_rows,
+                         float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

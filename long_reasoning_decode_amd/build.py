@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbkv.so")
 SOURCES = ["bkv_api.hip", "bkv_fps.hip", "bkv_score.hip", "bkv_select.hip", "bkv_compact.hip", "bkv_stream.hip",
-           "bkv_evict.hip", "bkv_prefill.hip", "bkv_sources.hip"]
+           "bkv_evict.hip", "bkv_prefill.hip", "bkv_sources.hip", "bkv_attention.hip"]
 
 
 def hipcc() -> str:

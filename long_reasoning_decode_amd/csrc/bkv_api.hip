@@ -265,6 +265,57 @@ int bkv_evict(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t n_len, bkv_b
     return hip_status(bkv::launch_fps(fa, s->head_dim, true, st));
 }
 
+int bkv_append_kv(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t L, const bkv_bf16* k_new,
+                  const bkv_bf16* v_new, const int32_t* pos, const float* rope_cs, int32_t rope_rows, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (L < 0 || L >= s->cap || rope_rows <= 0) return BKV_ERANGE;
+    if (!K || !V || !k_new || !v_new || !pos || !rope_cs) return BKV_EINVAL;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rope_cs) ||
+        !aligned4(pos))
+        return BKV_EINVAL;
+    bkv::AppendArgs aa;
+    aa.K = K;
+    aa.V = V;
+    aa.k_new = k_new;
+    aa.v_new = v_new;
+    aa.pos = pos;
+    aa.rope_cs = rope_cs;
+    aa.units = units_of(s);
+    aa.cap = s->cap;
+    aa.L = L;
+    aa.batch = s->batch;
+    aa.hkv = s->n_kv_heads;
+    aa.rope_rows = rope_rows;
+    return hip_status(bkv::launch_append(aa, s->head_dim, (hipStream_t)stream));
+}
+
+int bkv_decode_attention(const bkv_shape* s, const bkv_bf16* K, const bkv_bf16* V, int32_t n_len,
+                         const bkv_bf16* q, const int32_t* pos, const float* rope_cs, int32_t rope_rows, float* out,
+                         void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (n_len <= 0 || n_len > s->cap || rope_rows <= 0) return BKV_ERANGE;
+    if (!K || !V || !q || !pos || !rope_cs || !out) return BKV_EINVAL;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(q) || !aligned16(rope_cs) || !aligned4(pos) || !aligned4(out))
+        return BKV_EINVAL;
+    bkv::AttnArgs a;
+    a.K = K;
+    a.V = V;
+    a.q = q;
+    a.pos = pos;
+    a.rope_cs = rope_cs;
+    a.out = out;
+    a.units = units_of(s);
+    a.n_len = n_len;
+    a.cap = s->cap;
+    a.batch = s->batch;
+    a.hkv = s->n_kv_heads;
+    a.G = s->n_q_heads / s->n_kv_heads;
+    a.rope_rows = rope_rows;
+    return hip_status(bkv::launch_attention(a, s->head_dim, (hipStream_t)stream));
+}
+
 int bkv_decode_step(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t L, const bkv_bf16* k_new,
                     const bkv_bf16* v_new, const int32_t* pos, bkv_bf16* qbuf, int32_t* qcount,
                     const bkv_bf16* q_new, bkv_bf16* q_recent, int32_t* pos_recent, const float* rope_cs,

@@ -75,6 +75,16 @@ struct AppendArgs {
     int units, cap, L, batch, hkv, rope_rows;
 };
 
+struct AttnArgs {
+    const bkv_bf16* K;         // [units][cap][d] post-RoPE
+    const bkv_bf16* V;
+    const bkv_bf16* q;         // [qbufs][d] pre-RoPE
+    const int32_t* pos;        // [batch]
+    const float* rope_cs;      // [rope_rows][d/2][2]
+    float* out;                // [qbufs][d]
+    int units, n_len, cap, batch, hkv, G, rope_rows;
+};
+
 struct RingArgs {
     bkv_bf16* q_recent;        // [qbufs][n_recent_q][d]
     int32_t* pos_recent;       // [batch][n_recent_q]
@@ -95,5 +105,6 @@ hipError_t launch_compact(const CompactArgs& a, int d, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int d, hipStream_t st);
 hipError_t launch_evict(const EvictArgs& a, int d, hipStream_t st);
 hipError_t launch_ring(const RingArgs& a, int d, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int d, hipStream_t st);
 
 }  // namespace bkv

@@ -28,7 +28,7 @@ ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE
 
 EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_fps_update",
            "bkv_fps_merge", "bkv_fps_prefill", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict",
-           "bkv_decode_step")
+           "bkv_decode_step", "bkv_append_kv", "bkv_decode_attention")
 
 
 class Shape(C.Structure):
@@ -68,6 +68,8 @@ def load():
         L.bkv_compact.argtypes = [SP, P, P, i32, P, st]
         L.bkv_evict.argtypes = [SP, P, P, i32, P, P, P, P, P, P, i32, P, P, P, st]
         L.bkv_decode_step.argtypes = [SP, P, P, i32, P, P, P, P, P, P, P, P, P, i32, P, st]
+        L.bkv_append_kv.argtypes = [SP, P, P, i32, P, P, P, P, i32, st]
+        L.bkv_decode_attention.argtypes = [SP, P, P, i32, P, P, P, i32, P, st]
         for f in EXPORTS[3:]:
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -229,3 +231,22 @@ def decode_step(shape: Shape, K, V, L: int, k_new, v_new, pos, qbuf, qcount, q_n
                                   _ptr(q_recent, bf16, "q_recent"), _ptr(pos_recent, i32, "pos_recent"),
                                   _ptr(rope_cs, f32, "rope_cs"), int(rope_cs.shape[0]),
                                   _ptr(fps_sel, i32, "fps_sel"), _stream(stream)), "bkv_decode_step")
+
+
+def append_kv(shape: Shape, K, V, L: int, k_new, v_new, pos, rope_cs, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, K=(K, U * shape.cap * d), V=(V, U * shape.cap * d), k_new=(k_new, U * d), v_new=(v_new, U * d),
+          pos=(pos, shape.batch), rope_cs=(rope_cs, rope_cs.shape[0] * d))
+    _check(load().bkv_append_kv(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(L),
+                                _ptr(k_new, bf16, "k_new"), _ptr(v_new, bf16, "v_new"), _ptr(pos, i32, "pos"),
+                                _ptr(rope_cs, f32, "rope_cs"), int(rope_cs.shape[0]), _stream(stream)), "bkv_append_kv")
+
+
+def decode_attention(shape: Shape, K, V, n_len: int, q, pos, rope_cs, out, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, K=(K, U * shape.cap * d), V=(V, U * shape.cap * d), q=(q, Qb * d), pos=(pos, shape.batch),
+          rope_cs=(rope_cs, rope_cs.shape[0] * d), out=(out, Qb * d))
+    _check(load().bkv_decode_attention(C.byref(shape), _ptr(K, bf16, "K"), _ptr(V, bf16, "V"), int(n_len),
+                                       _ptr(q, bf16, "q"), _ptr(pos, i32, "pos"), _ptr(rope_cs, f32, "rope_cs"),
+                                       int(rope_cs.shape[0]), _ptr(out, f32, "out"), _stream(stream)),
+           "bkv_decode_attention")

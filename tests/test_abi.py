@@ -132,6 +132,19 @@ def test_prefill_validation(so):
     assert so.bkv_fps_prefill(C.byref(_shape(n_beacon=20)), FAKE, 10, FAKE, FAKE, None, None) == -2
 
 
+def test_attention_and_append_validation(so):
+    s = _shape()
+    args = lambda n: (C.byref(s), FAKE, FAKE, n, FAKE, FAKE, FAKE, 10, FAKE, None)
+    assert so.bkv_decode_attention(*args(0)) == -3
+    assert so.bkv_decode_attention(*args(s.cap + 1)) == -3
+    assert so.bkv_decode_attention(C.byref(s), FAKE, FAKE, 10, FAKE, FAKE, FAKE, 0, FAKE, None) == -3
+    assert so.bkv_decode_attention(C.byref(s), FAKE, None, 10, FAKE, FAKE, FAKE, 10, FAKE, None) == -1
+    assert so.bkv_decode_attention(C.byref(s), FAKE, FAKE, 10, MISALIGNED, FAKE, FAKE, 10, FAKE, None) == -1
+    assert so.bkv_append_kv(C.byref(s), FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, 10, None) == -3
+    assert so.bkv_append_kv(C.byref(s), FAKE, FAKE, s.cap, FAKE, FAKE, FAKE, FAKE, 10, None) == -3
+    assert so.bkv_append_kv(C.byref(s), FAKE, FAKE, 3, None, FAKE, FAKE, FAKE, 10, None) == -1
+
+
 def test_all_configs_are_supported_shapes():
     for cfg in EVICT_CONFIGS.values():
         assert cfg.d in (64, 128) and cfg.hq % cfg.hkv == 0 and cfg.G <= 8
