@@ -278,6 +278,52 @@ def prefill_bench(args) -> int:
     return 0
 
 
+def decode_bench(args) -> int:
+    """The synthetic decode-attention loop: tokens/s of the attention side of decoding, full cache against
+    BeaconKV (the framing of the pages' Table 4), and the attention kernel's HBM roofline."""
+    from long_reasoning_decode_amd.decode import DECODE_CONFIGS, DecodeRun, cache_bytes, mean_rows
+    torch.cuda.set_device(0)
+    L.load()
+    lines = []
+    for name in args.decode_configs.split(","):
+        dc = DECODE_CONFIGS[name]
+        b = dc.base
+        print(f"# decode {dc.name}: batch {b.batch}, cache {dc.n0} rows of {dc.cap}, {dc.steps} steps",
+              file=sys.stderr, flush=True)
+        torch.cuda.reset_peak_memory_stats()
+        run = DecodeRun(dc)
+        r = run.run()
+        rows = r["rows"] / dc.steps
+        att_ms = run.time_attention(int(round(rows)))
+        att_bytes = cache_bytes(dc, int(round(rows)))
+        ach = att_bytes / (att_ms * 1e-3) / 1e9
+        ms = r["gpu_ms"] / dc.steps
+        lines.append({
+            "metric": "decode tokens/s, attention side (append + attention over the cache + eviction manager; "
+                      "no weights)",
+            "value": b.batch / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": dc.steps, "warmup": 0,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"{dc.name}: {b.n_layers} layers x batch {b.batch} x {b.hkv} KV heads "
+                                   f"({b.units} units), {b.hq} query heads, head_dim {b.d}, "
+                                   + (f"budget {b.budget} (cache {b.budget}..{b.cap} rows), evict every "
+                                      f"{b.n_new} steps" if dc.mode == "beacon" else
+                                      f"full cache, {dc.n0}..{dc.n0 + dc.steps} rows (the middle of a "
+                                      f"{dc.gen_len}-token generation)"),
+                       "mode": dc.mode, "mean_rows": rows, "expected_mean_rows": mean_rows(dc),
+                       "evictions": r["evictions"]},
+            "roofline": {"bound": "hbm", "kernel": "attn_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                         "alg_bytes_per_launch": att_bytes, "attention_ms": att_ms},
+            "cache_bytes_peak": cache_bytes(dc, dc.cap),
+            "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
+        })
+        print(json.dumps(lines[-1]), flush=True)
+        del run
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +344,10 @@ def main() -> int:
                     help="instead of the eviction-step benchmark, time the prefill initialisation of every query "
                          "buffer (bkv_fps_prefill) and print its own line")
     ap.add_argument("--prefill-config", default=PREFILL.name, choices=sorted(PREFILL_CONFIGS))
+    ap.add_argument("--decode", action="store_true",
+                    help="instead of the eviction-step benchmark, run the synthetic decode-attention loop (full "
+                         "cache and BeaconKV) and print one line per config")
+    ap.add_argument("--decode-configs", default="decode-qwen3-4b-full,decode-qwen3-4b-beacon")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: print per-kernel HBM bytes from two rocprofv3 --pmc runs of this script "
                          "(FETCH_SIZE, then WRITE_SIZE, --output-format csv) made with --copy-calibration-mib")
@@ -319,6 +369,8 @@ def main() -> int:
         return stream_bench(args)
     if args.prefill:
         return prefill_bench(args)
+    if args.decode:
+        return decode_bench(args)
     cfg = EVICT_CONFIGS[args.config]
     torch.cuda.set_device(0)
     L.load()

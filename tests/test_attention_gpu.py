@@ -123,3 +123,28 @@ def test_attention_rejects_bad_lengths():
     for row in (-1, cfg.n_len):
         assert so.bkv_append_kv(C.byref(shape), ptr(inp["K"]), ptr(inp["V"]), row, ptr(q), ptr(q), ptr(inp["t"]),
                                 ptr(rope), rope.shape[0], None) == -3
+
+
+@pytest.mark.parametrize("mode", ["beacon", "full"])
+def test_decode_loop_tiny(mode):
+    """The synthetic decode loop on a tiny shape: the step count, the evictions, and the last step's attention
+    output against the oracle on the cache the loop left."""
+    from dataclasses import replace
+    from long_reasoning_decode_amd.decode import DecodeConfig, DecodeRun
+    dc = DecodeConfig(f"decode-tiny-{mode}", replace(TINY, batch=2, seed=20261202 + 620), mode, 70, gen_len=400)
+    run = DecodeRun(dc, block=16)
+    r = run.run()
+    b = dc.base
+    if mode == "beacon":
+        assert r["evictions"] == 2 and run.L == b.budget + 70 - 2 * b.n_new
+    else:
+        assert r["evictions"] == 0 and run.L == dc.n0 + 70
+    q, pos, n = run.last
+    U, G, D = b.units, b.G, b.d
+    cap = run.K.shape[-2]
+    Kh = synth.to_u16(run.K).reshape(U, cap, D)
+    Vh = synth.to_u16(run.V).reshape(U, cap, D)
+    p_u = pos.cpu().numpy()[[(u // b.hkv) % b.batch for u in range(U)]].astype(np.int32)
+    o, scale = O.decode_attention(H.ocfg(b, n_len=cap), Kh, Vh, synth.to_u16(q).reshape(U, G, D), p_u, n)
+    g = run.out.reshape(U, G, D).cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(g - o) <= RTOL_SCALE * scale + ATOL)
