@@ -1,9 +1,11 @@
 // bkv_fps.hip -- kernels of the continual FPS buffer update and of the
-// end-of-cycle merge (Notes §2.2, Eq. 9 and App. Alg. 1-2).  The update is an
-// append kernel (16 bytes per lane) followed by the sampling round, which only
-// the buffers that filled up do; the sampling rounds and the merge run four
-// independent wavefronts per workgroup, one query buffer each (the per-buffer
-// work is in bkv_fps_impl.hpp).
+// end-of-cycle merge (Notes §2.2, Eq. 9 and App. Alg. 1-2): four independent
+// wavefronts per workgroup (the per-buffer work is in bkv_fps_impl.hpp).  The
+// update appends each buffer's query and samples the buffers that filled up,
+// a few buffers per wave when there are many; the merge takes one buffer per
+// wave.
+#include <atomic>
+
 #include "bkv_fps_impl.hpp"
 
 namespace bkv {
@@ -12,32 +14,51 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
+// MERGE: one buffer per wave.  Update: wave w of W takes the contiguous
+// buffers [w nbuf / W, (w + 1) nbuf / W), kMaxBuffersPerWave at a time, so
+// every wave has the same share (to one buffer) when all of them sample.
 template <int D, bool MERGE>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void fps_kernel(FpsArgs a) {
     __shared__ fps::Smem s[kWavesPerBlock];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int b = blockIdx.x * kWavesPerBlock + wave;
-    if (b >= a.nbuf) return;
-    if (MERGE) fps::merge_one<D>(a, b, s[wave], lane);
-    else fps::compress_one<D>(a, b, s[wave], lane);
+    const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    if (MERGE) {
+        if (w >= a.nbuf) return;
+        fps::merge_one<D>(a, (int)w, s[wave], lane);
+    } else {
+        const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
+        const int64_t lo = w * a.nbuf / n_waves, hi = (w + 1) * a.nbuf / n_waves;
+        for (int64_t b0 = lo; b0 < hi; b0 += fps::kMaxBuffersPerWave) {
+            const int nw = (int)(hi - b0 < fps::kMaxBuffersPerWave ? hi - b0 : fps::kMaxBuffersPerWave);
+            fps::update_wave<D>(a, (int)b0, nw, s[wave], lane);
+        }
+    }
 }
 
-// First half of the buffer update: append each buffer's new query at slot
-// qcount (clamped to [0, B_Q^max - 1]) and count it.  16 lanes per buffer
-// for d = 128 (8 for d = 64), each copying 16 bytes; a buffer's lanes sit in
-// one wave, so all of them read the count before any of them writes it.
-template <int D>
-__global__ __launch_bounds__(256) void append_q_kernel(FpsArgs a) {
-    constexpr int kPieces = D / 8;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t b = t / kPieces;
-    const int piece = (int)(t % kPieces);
-    if (b >= a.nbuf) return;
-    const int bqmax = a.n_beacon + a.n_recent_q;
-    const int c = clampi(a.qcount[b], 0, bqmax - 1);
-    const u32x4_t v = reinterpret_cast<const u32x4_t*>(a.q_new + b * D)[piece];
-    reinterpret_cast<u32x4_t*>(a.qbuf + (b * a.qcap + c) * D)[piece] = v;
-    if (piece == 0) a.qcount[b] = c + 1;
+// Workgroups of the update kernel resident on the current device at once (queried once per device).
+hipError_t resident_blocks(int d, int64_t* out) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int64_t> cache[2][kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int di = d == 64 ? 0 : 1;
+    if (dev >= 0 && dev < kMaxDev && cache[di][dev].load(std::memory_order_relaxed) > 0) {
+        *out = cache[di][dev].load(std::memory_order_relaxed);
+        return hipSuccess;
+    }
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = d == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fps_kernel<64, false>,
+                                                                   64 * kWavesPerBlock, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fps_kernel<128, false>,
+                                                                   64 * kWavesPerBlock, 0);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    if (dev >= 0 && dev < kMaxDev) cache[di][dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -45,15 +66,14 @@ __global__ __launch_bounds__(256) void append_q_kernel(FpsArgs a) {
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st) {
     if (a.nbuf <= 0) return hipSuccess;
     if (a.src != kSrcFps) return merge ? launch_offer_merge(a, d, st) : launch_offer(a, d, st);
-    if (!merge) {
-        const int64_t threads = (int64_t)a.nbuf * (d / 8);
-        dim3 g((unsigned)((threads + 255) / 256)), blk(256);
-        if (d == 64) hipLaunchKernelGGL(append_q_kernel<64>, g, blk, 0, st, a);
-        else hipLaunchKernelGGL(append_q_kernel<128>, g, blk, 0, st, a);
-        hipError_t e = hipGetLastError();
+    int64_t blocks = (a.nbuf + kWavesPerBlock - 1) / kWavesPerBlock;   // one buffer per wave
+    if (!merge) {   // the update: at most the workgroups the chip holds at once
+        int64_t fit = 0;
+        const hipError_t e = resident_blocks(d, &fit);
         if (e != hipSuccess) return e;
+        if (blocks > fit) blocks = fit;
     }
-    dim3 grid((a.nbuf + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
+    dim3 grid((unsigned)blocks), block(64 * kWavesPerBlock);
     if (d == 64) {
         if (merge) hipLaunchKernelGGL((fps_kernel<64, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((fps_kernel<64, false>), grid, block, 0, st, a);

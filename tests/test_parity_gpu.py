@@ -86,6 +86,38 @@ def test_fps_update_matches_oracle(d, fill):
         assert np.array_equal(g[b, :n], qbuf_h[b, :n]), b
 
 
+@pytest.mark.parametrize("d,nbuf,nb", [(64, 100_000, 16), (128, 30_000, 16), (128, 30_000, 31)])
+def test_fps_update_several_buffers_per_wave(d, nbuf, nb):
+    """More buffers than the chip holds waves at once, so each wave updates a run of them (one or more
+    groups of up to 16): full and non-full buffers mixed within a run, adversarial contents in the
+    first few hundred."""
+    rng = np.random.default_rng(300 + d + nb)
+    cfg = TINY.scaled(d=d, n_layers=1, batch=nbuf // 8, hq=8, hkv=2, n_beacon=nb, n_recent_q=32 - nb)
+    assert cfg.qbufs == nbuf
+    X = rng.standard_normal((nbuf, cfg.qcap, d), dtype=np.float32)
+    X[:600] = _adversarial_buffers(600, d, cfg.qcap, rng)
+    qb = torch.from_numpy(X).to(torch.bfloat16)
+    del X
+    qn = torch.randn(nbuf, d, generator=torch.Generator().manual_seed(301 + d)).to(torch.bfloat16)
+    qc = np.where(rng.random(nbuf) < 0.6, 31, rng.integers(0, 31, nbuf)).astype(np.int32)
+    qbuf_h = synth.to_u16(qb).copy()
+    qc_h = qc.copy()
+    _flush(f"fps update d={d} nbuf={nbuf} n_beacon={nb}: oracle")
+    sel_o = O.fps_update(qbuf_h, qc_h, synth.to_u16(qn), cfg.n_beacon, cfg.n_recent_q)
+    qbuf_d = qb.cuda()
+    qc_d = torch.from_numpy(qc).cuda()
+    sel_d = torch.full((nbuf, cfg.n_beacon), -7, dtype=torch.int32, device="cuda")
+    _flush("  device")
+    L.fps_update(L.shape_of(cfg), qbuf_d, qc_d, qn.cuda(), sel_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc_d.cpu().numpy(), qc_h)
+    assert np.array_equal(sel_d.cpu().numpy(), sel_o)
+    g = synth.to_u16(qbuf_d)
+    n = qc_h[:, None, None]
+    live = np.arange(cfg.qcap)[None, :, None] < n
+    assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
+
+
 @pytest.mark.parametrize("cfg", [TINY, QWEN3_4B.scaled(n_layers=2, batch=3), R1_QWEN_7B.scaled(n_layers=1, batch=2)],
                          ids=lambda c: c.name)
 def test_fps_update_many_random_buffers(cfg):
