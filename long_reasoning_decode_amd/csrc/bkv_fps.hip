@@ -2,8 +2,8 @@
 // end-of-cycle merge (Notes §2.2, Eq. 9 and App. Alg. 1-2): four independent
 // wavefronts per workgroup (the per-buffer work is in bkv_fps_impl.hpp).  The
 // update appends each buffer's query and samples the buffers that filled up,
-// a few buffers per wave when there are many; the merge takes one buffer per
-// wave.
+// a run of buffers per wave when there are many; the merge takes two buffers
+// per wave.
 #include <atomic>
 
 #include "bkv_fps_impl.hpp"
@@ -14,7 +14,7 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-// MERGE: one buffer per wave.  Update: wave w of W takes the contiguous
+// MERGE: two buffers per wave.  Update: wave w of W takes the contiguous
 // buffers [w nbuf / W, (w + 1) nbuf / W), kMaxBuffersPerWave at a time, so
 // every wave has the same share (to one buffer) when all of them sample.
 template <int D, bool MERGE>
@@ -23,8 +23,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void fps_kernel(FpsArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     if (MERGE) {
-        if (w >= a.nbuf) return;
-        fps::merge_one<D>(a, (int)w, s[wave], lane);
+        if (2 * w >= a.nbuf) return;
+        fps::merge_pair<D>(a, (int)(2 * w), s[wave], lane);
     } else {
         const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
         const int64_t lo = w * a.nbuf / n_waves, hi = (w + 1) * a.nbuf / n_waves;
@@ -66,7 +66,8 @@ hipError_t resident_blocks(int d, int64_t* out) {
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st) {
     if (a.nbuf <= 0) return hipSuccess;
     if (a.src != kSrcFps) return merge ? launch_offer_merge(a, d, st) : launch_offer(a, d, st);
-    int64_t blocks = (a.nbuf + kWavesPerBlock - 1) / kWavesPerBlock;   // one buffer per wave
+    // merge: two buffers per wave; update: at most one buffer per wave
+    int64_t blocks = ((merge ? (a.nbuf + 1) / 2 : a.nbuf) + kWavesPerBlock - 1) / kWavesPerBlock;
     if (!merge) {   // the update: at most the workgroups the chip holds at once
         int64_t fit = 0;
         const hipError_t e = resident_blocks(d, &fit);

@@ -1,11 +1,13 @@
-// bkv_fps_impl.hpp -- continual farthest point sampling of pre-RoPE queries,
-// one wavefront per query buffer (device functions of the buffer-update and
-// merge kernels).
+// bkv_fps_impl.hpp -- continual farthest point sampling of pre-RoPE queries
+// (device functions of the buffer-update and merge kernels).  One wavefront
+// samples two buffers at a time, one per half-wave (lanes 0-31 and 32-63):
+// lane i of a half holds candidate row i.
 //
-// The Gram matrix of the (at most 32) candidates is register-blocked 4 x 4
-// per lane (64 lanes cover the 32 x 32 entries); the rows stream through LDS
-// in stages of 32 columns, transposed ([k][row]) so one 16-byte read gives
-// four rows' k-th elements.
+// The Gram matrices come from the matrix cores: 128 (or 64) fp32 MFMA
+// 32x32x1 rank-1 updates, two blocks per instruction (one per buffer), each
+// lane feeding the k-th element of its row as both operands.  Each update
+// rounds once per element, so the chain is the same sequence of fused
+// multiply-adds as a scalar loop over k.
 //
 // The arithmetic follows one fixed fp32 order so that the selected indices
 // are reproducible bit for bit (Notes §2.2, App. Alg. 1):
@@ -14,7 +16,7 @@
 //   0 when a norm is 0, a_i = (left-to-right sum of cos_ij over j) / n,
 // then argmin a (seed), and n_beacon - 1 greedy steps r = argmin over the
 // untaken rows of S, S_j = max(S_j, cos_jr).  Ties go to the lower index.
-// An argmin is a DPP minimum over the 32 candidate lanes followed by the
+// An argmin is a DPP minimum over each half's 32 lanes followed by the
 // lowest lane whose value equals it (a ballot and a find-first-set), which is
 // the lowest index among equal values.  Each wave uses only its own LDS area,
 // so waves of one workgroup never wait for each other.
@@ -27,17 +29,14 @@ namespace bkv {
 namespace fps {
 
 constexpr int kMaxRows = 32;
-constexpr int kStageK = 32;              // Gram columns staged per round
-constexpr int kXStride = kMaxRows + 4;   // floats per k-row of the stage (16-B aligned)
-constexpr int kCStride = kMaxRows + 1;   // floats per row of the cosine matrix
+constexpr int kCStride = kMaxRows + 1;   // floats per row of a cosine matrix
+
+typedef float f32x32_t __attribute__((ext_vector_type(32)));
 
 struct Smem {
-    union {
-        float x[kStageK][kXStride];  // x[k - k0][row], while the Gram accumulates
-        float c[kMaxRows][kCStride]; // then the Gram, then the cosines
-    };
-    float nrm[kMaxRows];
-    int sel[kMaxRows];
+    float c[2][kMaxRows][kCStride];  // per half: the Gram, then the cosines
+    float nrm[2][kMaxRows];
+    int sel[2][kMaxRows];
     int row_of[kMaxRows];            // source row of each destination row of a compaction
 };
 
@@ -47,11 +46,20 @@ __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Source row r of the candidate set: rows r < n0 from src0, the rest from src1.
+// Source row r of a candidate set: rows r < n0 from src0, the rest from src1.
 __device__ __forceinline__ const bkv_bf16* cand_row(const bkv_bf16* src0, int n0, const bkv_bf16* src1,
                                                     int r, int D) {
     return r < n0 ? src0 + (size_t)r * D : src1 + (size_t)(r - n0) * D;
 }
+
+// The candidates of one buffer: n rows, [0, n0) from src0 and [n0, n) from
+// src1 (n = 0: no buffer in this half).
+struct Cand {
+    const bkv_bf16* src0;
+    int n0;
+    const bkv_bf16* src1;
+    int n;
+};
 
 // Integer key ordered as the float v with -0 taken as +0 (v not NaN).
 __device__ __forceinline__ int order_key(float v) {
@@ -65,111 +73,96 @@ __device__ __forceinline__ int dpp_min_step(int k) {
     return min(k, __builtin_amdgcn_update_dpp(0x7FFFFFFF, k, CTRL, ROW_MASK, 0xF, false));
 }
 
-// Lowest lane among 0..31 holding the smallest v (lanes 32..63 must hold
-// +inf, and no lane NaN); the same in every lane.  Equal values (+0 and -0
-// included) go to the lower lane, as in a scan that keeps the first minimum.
-__device__ __forceinline__ int argmin32(float v) {
+// Per half-wave: the lowest lane of the half holding the half's smallest v
+// (no lane NaN), as an index 0..31, in every lane of the half.  Equal values
+// (+0 and -0 included) go to the lower lane, as in a scan that keeps the
+// first minimum.
+__device__ __forceinline__ int argmin_halves(float v, int lane) {
     const int k = order_key(v);
     int m = dpp_min_step<0xB1>(k);        // quad_perm [1,0,3,2]
     m = dpp_min_step<0x4E>(m);            // quad_perm [2,3,0,1]
     m = dpp_min_step<0x141>(m);           // row_half_mirror
     m = dpp_min_step<0x140>(m);           // row_mirror: every lane of a row holds the row's minimum
     m = dpp_min_step<0x142, 0xA>(m);      // row_bcast15: rows 1 and 3 also take the previous row's
-    return __builtin_ctzll(__ballot(k == __builtin_amdgcn_readlane(m, 31)));
+    const int m0 = __builtin_amdgcn_readlane(m, 31), m1 = __builtin_amdgcn_readlane(m, 63);
+    const uint64_t eq = __ballot(k == (lane < 32 ? m0 : m1));
+    const int r0 = __builtin_ctz((uint32_t)eq), r1 = __builtin_ctz((uint32_t)(eq >> 32));
+    return lane < 32 ? r0 : r1;
 }
 
-// FPS over candidate rows [0, n) (n > m >= 1); leaves the selection order in
-// s.sel[0..m) and returns the 32-bit mask of taken rows.
+// FPS of the two candidate sets (half h takes set h; each with n > m >= 1,
+// or n = 0 for an empty half).  Leaves the selection orders in s.sel[h][0..m)
+// and returns the taken rows, half h in bits 32h .. 32h + 31.
 template <int D>
-__device__ uint32_t select(Smem& s, const bkv_bf16* src0, int n0, const bkv_bf16* src1, int n, int m, int lane) {
-    const int bi = lane >> 3, bj = lane & 7;
-    float acc[4][4];
+__device__ uint64_t select2(Smem& s, const Cand& c0, const Cand& c1, int m, int lane) {
+    constexpr int kPieces = D / 8;
+    const int h = lane >> 5, i = lane & 31;
+    const int n = h ? c1.n : c0.n;
+
+    // row i of this half's set, 8 bf16 per piece (zeros past n)
+    u32x4_t row[kPieces];
+    {
+        const bkv_bf16* p = h ? cand_row(c1.src0, c1.n0, c1.src1, i, D) : cand_row(c0.src0, c0.n0, c0.src1, i, D);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
-    // each lane stages two 16-byte pieces (row r, 8 consecutive k) per round
-    const int r_a = lane & 31, kc_a = lane >> 5;
-    for (int k0 = 0; k0 < D; k0 += kStageK) {
-        u32x4_t w[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int kc = kc_a + 2 * q;                    // 0..3: 8-column piece within the stage
-            w[q] = u32x4_t{0u, 0u, 0u, 0u};
-            if (r_a < n) w[q] = *reinterpret_cast<const u32x4_t*>(cand_row(src0, n0, src1, r_a, D) + k0 + kc * 8);
+        for (int q = 0; q < kPieces; ++q) {
+            row[q] = u32x4_t{0u, 0u, 0u, 0u};
+            if (i < n) row[q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
         }
-        wave_lds_sync();  // the previous round's reads of s.x are done
+    }
+    // Gram of both halves: acc[r] = dot of rows (8 ((r % 16) / 4) + 4 h + r % 4, i) of half r / 16
+    f32x32_t acc = f32x32_t{};
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int kc = kc_a + 2 * q;
+    for (int k = 0; k < D; ++k) {
+        const uint32_t w = row[k / 8][(k % 8) / 2];
+        const float v = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(v, v, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 32; ++r) s.c[r / 16][8 * ((r % 16) / 4) + 4 * h + (r % 4)][i] = acc[r];
+    wave_lds_sync();
+    s.nrm[h][i] = __builtin_sqrtf(s.c[h][i][i]);
+    wave_lds_sync();
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const float nj = s.nrm[bb][i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4_t ni4 = *reinterpret_cast<const f32x4_t*>(&s.nrm[bb][8 * q + 4 * h]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                s.x[kc * 8 + 2 * e][r_a] = __uint_as_float(w[q][e] << 16);
-                s.x[kc * 8 + 2 * e + 1][r_a] = __uint_as_float(w[q][e] & 0xFFFF0000u);
+                const int r = 16 * bb + 4 * q + e;
+                const float ni = ni4[e];
+                const float cq = acc[r] / (ni * nj);
+                s.c[bb][8 * q + 4 * h + e][i] = ((ni == 0.0f) | (nj == 0.0f)) ? 0.0f : cq;
             }
         }
-        wave_lds_sync();
-#pragma unroll 8
-        for (int k = 0; k < kStageK; ++k) {
-            const f32x4_t xa = *reinterpret_cast<const f32x4_t*>(&s.x[k][4 * bi]);
-            const f32x4_t xb = *reinterpret_cast<const f32x4_t*>(&s.x[k][4 * bj]);
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(xa[a], xb[b], acc[a][b]);
-        }
     }
-    wave_lds_sync();   // the last reads of x are done before c overwrites it
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) s.c[4 * bi + a][4 * bj + b] = acc[a][b];
-    wave_lds_sync();
-    if (lane < kMaxRows) s.nrm[lane] = __builtin_sqrtf(s.c[lane][lane]);
-    wave_lds_sync();
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const float ni = s.nrm[4 * bi + a];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float nj = s.nrm[4 * bj + b];
-            const float den = ni * nj;
-            const float q = acc[a][b] / den;
-            acc[a][b] = ((ni == 0.0f) | (nj == 0.0f)) ? 0.0f : q;
-        }
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) s.c[4 * bi + a][4 * bj + b] = acc[a][b];
     wave_lds_sync();
 
-    // seed: lowest mean cosine (row sums read down the columns: the matrix is symmetric bit for bit)
-    float v = __builtin_inff();
-    {
-        const int c0 = lane & (kMaxRows - 1);
-        float sum = 0.0f;
-#pragma unroll 8
-        for (int j = 0; j < n; ++j) sum = sum + s.c[j][c0];
-        if (lane < n) v = sum / (float)n;
+    // seed: lowest mean cosine (row sums read down the columns: the matrices are symmetric bit for bit)
+    const int nmax = c0.n > c1.n ? c0.n : c1.n;
+    float sum = 0.0f;
+    for (int j = 0; j < nmax; ++j) {
+        const float cj = s.c[h][j][i];
+        sum = j < n ? sum + cj : sum;
     }
-    const int p = argmin32(v);
-    // lane j < n: S_j (cosines are read along row r, equal to column r); lane i < m: the i-th pick
-    const int col = lane & (kMaxRows - 1);
-    float S = s.c[p][col];
-    bool taken = lane == p;
+    const float v = i < n ? sum / (float)n : __builtin_inff();
+    const int p = argmin_halves(v, lane);
+    // lane i < n: S_i (cosines read along row r, equal to column r); lane i < m: the i-th pick
+    float S = s.c[h][p][i];
+    bool taken = i == p;
     int pick = p;
     for (int it = 1; it < m; ++it) {
-        const float cv = ((lane < n) & !taken) ? S : __builtin_inff();
-        const int r = argmin32(cv);
-        taken = taken | (lane == r);
-        pick = lane == it ? r : pick;
-        const float c = s.c[r][col];
+        const float cv = ((i < n) & !taken) ? S : __builtin_inff();
+        const int r = argmin_halves(cv, lane);
+        taken = taken | (i == r);
+        pick = i == it ? r : pick;
+        const float c = s.c[h][r][i];
         S = (c > S) ? c : S;
     }
-    if (lane < m) s.sel[lane] = pick;
+    if (i < m) s.sel[h][i] = pick;
     wave_lds_sync();
-    return (uint32_t)__ballot(taken);
+    return __ballot(taken);
 }
 
 // Copy the rows in `mask` (ascending) to dst[0..), dst == src0 (in place;
@@ -257,45 +250,72 @@ __device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane)
         }
     }
     uint64_t todo = __ballot(full);
-    while (todo) {
-        const int bi = __builtin_ctzll(todo);
+    while (todo) {   // two buffers per round
+        const int bi0 = __builtin_ctzll(todo);
         todo &= todo - 1;
-        const int b = b0 + bi;
-        const int c = __builtin_amdgcn_readlane(c_l, bi);   // uniform: the select's loops stay scalar
-        bkv_bf16* buf = a.qbuf + (size_t)b * a.qcap * D;
-        const bkv_bf16* qn = a.q_new + (size_t)b * D;
-        const uint32_t mask = select<D>(s, buf, c, qn, c + 1, m, lane);
-        write_rows<D>(s, mask, buf, c, qn, lane);
-        if (lane == 0) a.qcount[b] = m;
+        const int bi1 = todo ? __builtin_ctzll(todo) : bi0;
+        const bool two = todo != 0;
+        todo &= todo - 1;
+        const int c0 = __builtin_amdgcn_readlane(c_l, bi0), c1 = __builtin_amdgcn_readlane(c_l, bi1);
+        bkv_bf16* buf0 = a.qbuf + (size_t)(b0 + bi0) * a.qcap * D;
+        bkv_bf16* buf1 = a.qbuf + (size_t)(b0 + bi1) * a.qcap * D;
+        const bkv_bf16* qn0 = a.q_new + (size_t)(b0 + bi0) * D;
+        const bkv_bf16* qn1 = a.q_new + (size_t)(b0 + bi1) * D;
+        const uint64_t mask = select2<D>(s, Cand{buf0, c0, qn0, c0 + 1}, Cand{buf1, c1, qn1, two ? c1 + 1 : 0},
+                                         m, lane);
+        write_rows<D>(s, (uint32_t)mask, buf0, c0, qn0, lane);
+        if (lane == 0) a.qcount[b0 + bi0] = m;
         if (a.fps_sel)
-            for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)b * m + i] = s.sel[i];
+            for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)(b0 + bi0) * m + i] = s.sel[0][i];
+        if (two) {
+            write_rows<D>(s, (uint32_t)(mask >> 32), buf1, c1, qn1, lane);
+            if (lane == 0) a.qcount[b0 + bi1] = m;
+            if (a.fps_sel)
+                for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)(b0 + bi1) * m + i] = s.sel[1][i];
+        }
     }
 }
 
-// End-of-cycle merge of buffer b: FPS over beacons ++ recents (Notes §2.2, App. Alg. 2).
+// End-of-cycle merge of buffers b and b + 1 (when below nbuf): FPS over
+// beacons ++ recents (Notes §2.2, App. Alg. 2).
 template <int D>
-__device__ void merge_one(const FpsArgs& a, int b, Smem& s, int lane) {
+__device__ void merge_pair(const FpsArgs& a, int b, Smem& s, int lane) {
     const int m = a.n_beacon;
-    bkv_bf16* buf = a.qbuf + (size_t)b * a.qcap * D;
-    const bkv_bf16* rec = a.q_recent + (size_t)b * a.n_recent_q * D;
-    const int nb = clampi(a.qcount[b], 0, m);
-    const int n = nb + a.n_recent_q;
-    if (m <= 0) {  // nothing is kept
-        if (lane == 0) a.qcount[b] = 0;
-        return;
+    const int nbuf_here = a.nbuf - b < 2 ? a.nbuf - b : 2;
+    Cand c[2];
+    bkv_bf16* bufs[2] = {a.qbuf, a.qbuf};
+    bool samples[2] = {false, false};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        c[h] = Cand{a.qbuf, 0, a.qbuf, 0};
+        if (h >= nbuf_here) continue;
+        bkv_bf16* buf = a.qbuf + (size_t)(b + h) * a.qcap * D;
+        const bkv_bf16* rec = a.q_recent + (size_t)(b + h) * a.n_recent_q * D;
+        const int nb = clampi(a.qcount[b + h], 0, m);
+        const int n = nb + a.n_recent_q;
+        if (m <= 0) {  // nothing is kept
+            if (lane == 0) a.qcount[b + h] = 0;
+        } else if (n <= m) {
+            write_rows<D>(s, n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u), buf, nb, rec, lane);
+            if (lane == 0) a.qcount[b + h] = n;
+            if (a.fps_sel)
+                for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)(b + h) * m + i] = i < n ? i : -1;
+        } else {
+            c[h] = Cand{buf, nb, rec, n};
+            bufs[h] = buf;
+            samples[h] = true;
+        }
     }
-    if (n <= m) {
-        write_rows<D>(s, n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u), buf, nb, rec, lane);
-        if (lane == 0) a.qcount[b] = n;
+    if (!samples[0] && !samples[1]) return;
+    const uint64_t mask = select2<D>(s, c[0], c[1], m, lane);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (!samples[h]) continue;
+        write_rows<D>(s, (uint32_t)(mask >> (32 * h)), bufs[h], c[h].n0, c[h].src1, lane);
+        if (lane == 0) a.qcount[b + h] = m;
         if (a.fps_sel)
-            for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)b * m + i] = i < n ? i : -1;
-        return;
+            for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)(b + h) * m + i] = s.sel[h][i];
     }
-    const uint32_t mask = select<D>(s, buf, nb, rec, n, m, lane);
-    write_rows<D>(s, mask, buf, nb, rec, lane);
-    if (lane == 0) a.qcount[b] = m;
-    if (a.fps_sel)
-        for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)b * m + i] = s.sel[i];
 }
 
 }  // namespace fps
