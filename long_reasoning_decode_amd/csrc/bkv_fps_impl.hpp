@@ -90,33 +90,41 @@ __device__ __forceinline__ int argmin_halves(float v, int lane) {
     return lane < 32 ? r0 : r1;
 }
 
-// FPS of the two candidate sets (half h takes set h; each with n > m >= 1,
-// or n = 0 for an empty half).  Leaves the selection orders in s.sel[h][0..m)
-// and returns the taken rows, half h in bits 32h .. 32h + 31.
+// Every piece passes through one point as if rewritten there, so the
+// compiler issues all of their loads before it (one wait) and cannot
+// re-issue a load later in place of keeping its registers.
+template <int N>
+__device__ __forceinline__ void hold_all(u32x4_t (&r)[N]) {
+    if constexpr (N == 8) {
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                          "+v"(r[7]));
+    } else {
+        static_assert(N == 16, "row pieces: 8 (d = 64) or 16 (d = 128)");
+        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                          "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]),
+                          "+v"(r[14]), "+v"(r[15]));
+    }
+}
+
+// Row i of half h's candidate set into `row`, 8 bf16 per piece (loads issued,
+// not waited for).  Lanes past n load a copy of row n - 1 (row 0 of src0 in
+// an empty half): their dot products are computed but never read.
 template <int D>
-__device__ uint64_t select2(Smem& s, const Cand& c0, const Cand& c1, int m, int lane) {
-    constexpr int kPieces = D / 8;
+__device__ __forceinline__ void load_rows(u32x4_t (&row)[D / 8], const Cand& c0, const Cand& c1, int lane) {
     const int h = lane >> 5, i = lane & 31;
     const int n = h ? c1.n : c0.n;
+    const bkv_bf16* src0 = h ? c1.src0 : c0.src0;
+    const bkv_bf16* src1 = h ? c1.src1 : c0.src1;
+    const int n0 = h ? c1.n0 : c0.n0;
+    const int ic = i < n ? i : (n > 0 ? n - 1 : 0);
+    const bkv_bf16* p = n > 0 ? cand_row(src0, n0, src1, ic, D) : src0;
+#pragma unroll
+    for (int q = 0; q < D / 8; ++q) row[q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
+}
 
-    // row i of this half's set, 8 bf16 per piece (zeros past n)
-    u32x4_t row[kPieces];
-    {
-        const bkv_bf16* p = h ? cand_row(c1.src0, c1.n0, c1.src1, i, D) : cand_row(c0.src0, c0.n0, c0.src1, i, D);
-#pragma unroll
-        for (int q = 0; q < kPieces; ++q) {
-            row[q] = u32x4_t{0u, 0u, 0u, 0u};
-            if (i < n) row[q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
-        }
-    }
-    // Gram of both halves: acc[r] = dot of rows (8 ((r % 16) / 4) + 4 h + r % 4, i) of half r / 16
-    f32x32_t acc = f32x32_t{};
-#pragma unroll
-    for (int k = 0; k < D; ++k) {
-        const uint32_t w = row[k / 8][(k % 8) / 2];
-        const float v = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(v, v, acc, 0, 0, 0);
-    }
+// Gram entries acc (as laid out by the rank-1 updates) into s.c, the norms
+// into s.nrm, then the cosines over the Gram entries in s.c.
+__device__ __forceinline__ void cosines2(Smem& s, const f32x32_t& acc, int h, int i) {
 #pragma unroll
     for (int r = 0; r < 32; ++r) s.c[r / 16][8 * ((r % 16) / 4) + 4 * h + (r % 4)][i] = acc[r];
     wave_lds_sync();
@@ -138,9 +146,71 @@ __device__ uint64_t select2(Smem& s, const Cand& c0, const Cand& c1, int m, int 
         }
     }
     wave_lds_sync();
+}
 
+// Cosine matrices of both halves' rows into s.c (and the norms into s.nrm).
+// The row loads are all waited for at once.
+template <int D>
+__device__ void gram2(Smem& s, u32x4_t (&row)[D / 8], int lane) {
+    const int h = lane >> 5, i = lane & 31;
+    hold_all(row);
+    // acc[r] = dot of rows (8 ((r % 16) / 4) + 4 h + r % 4, i) of half r / 16
+    f32x32_t acc = f32x32_t{};
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        const uint32_t w = row[k / 8][(k % 8) / 2];
+        const float v = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(v, v, acc, 0, 0, 0);
+    }
+    cosines2(s, acc, h, i);
+}
+
+// Row loads of one half-wave set in groups of four 16-byte pieces: the next
+// group's loads are issued before the current group's 32 rank-1 updates, so
+// only the first group's latency is exposed and at most two groups' registers
+// are held.
+template <int D>
+__device__ void gram2_paced(Smem& s, const Cand& c0, const Cand& c1, int lane) {
+    constexpr int kGroups = D / 32;
+    const int h = lane >> 5, i = lane & 31;
+    const int n = h ? c1.n : c0.n;
+    const bkv_bf16* src0 = h ? c1.src0 : c0.src0;
+    const bkv_bf16* src1 = h ? c1.src1 : c0.src1;
+    const int n0 = h ? c1.n0 : c0.n0;
+    const int ic = i < n ? i : (n > 0 ? n - 1 : 0);
+    const bkv_bf16* p = n > 0 ? cand_row(src0, n0, src1, ic, D) : src0;
+    u32x4_t g[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) g[0][q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
+    f32x32_t acc = f32x32_t{};
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+        u32x4_t (&cur)[4] = g[gi & 1];
+        if (gi + 1 < kGroups) {
+            u32x4_t (&nxt)[4] = g[(gi + 1) & 1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const u32x4_t*>(p + (gi + 1) * 32 + q * 8);
+        }
+        asm volatile("" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const uint32_t w = cur[k / 8][(k % 8) / 2];
+            const float v = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            acc = __builtin_amdgcn_mfma_f32_32x32x1f32(v, v, acc, 0, 0, 0);
+        }
+    }
+    cosines2(s, acc, h, i);
+}
+
+// FPS over the cosine matrices in s.c of the two halves' sets (n0 and n1
+// rows, each n > m >= 1 or 0 for an empty half).  Leaves the selection
+// orders in s.sel[h][0..m) and returns the taken rows, half h in bits
+// 32h .. 32h + 31.
+__device__ uint64_t fps2(Smem& s, int n0, int n1, int m, int lane) {
+    const int h = lane >> 5, i = lane & 31;
+    const int n = h ? n1 : n0;
     // seed: lowest mean cosine (row sums read down the columns: the matrices are symmetric bit for bit)
-    const int nmax = c0.n > c1.n ? c0.n : c1.n;
+    const int nmax = n0 > n1 ? n0 : n1;
     float sum = 0.0f;
     for (int j = 0; j < nmax; ++j) {
         const float cj = s.c[h][j][i];
@@ -213,7 +283,8 @@ constexpr int kMaxBuffersPerWave = 16;
 // latency per wave), and the sampling reads each new row from q_new, so
 // nothing it reads depends on the appends' stores.
 template <int D>
-__device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane) {
+__device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane_in) {
+    const int lane = lane_in;
     constexpr int kPieces = D / 8;                 // 16-byte pieces per row
     constexpr int kPerPass = kWave / kPieces;      // buffers per pass of the wave
     const int bqmax = a.n_beacon + a.n_recent_q;
@@ -251,27 +322,30 @@ __device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane)
     }
     uint64_t todo = __ballot(full);
     while (todo) {   // two buffers per round
+        int lane_r = lane_in;   // opaque per round: lane-derived addresses are not held across rounds
+        asm volatile("" : "+v"(lane_r));
         const int bi0 = __builtin_ctzll(todo);
         todo &= todo - 1;
-        const int bi1 = todo ? __builtin_ctzll(todo) : bi0;
         const bool two = todo != 0;
+        const int bi1 = two ? __builtin_ctzll(todo) : bi0;
         todo &= todo - 1;
         const int c0 = __builtin_amdgcn_readlane(c_l, bi0), c1 = __builtin_amdgcn_readlane(c_l, bi1);
         bkv_bf16* buf0 = a.qbuf + (size_t)(b0 + bi0) * a.qcap * D;
         bkv_bf16* buf1 = a.qbuf + (size_t)(b0 + bi1) * a.qcap * D;
         const bkv_bf16* qn0 = a.q_new + (size_t)(b0 + bi0) * D;
         const bkv_bf16* qn1 = a.q_new + (size_t)(b0 + bi1) * D;
-        const uint64_t mask = select2<D>(s, Cand{buf0, c0, qn0, c0 + 1}, Cand{buf1, c1, qn1, two ? c1 + 1 : 0},
-                                         m, lane);
-        write_rows<D>(s, (uint32_t)mask, buf0, c0, qn0, lane);
-        if (lane == 0) a.qcount[b0 + bi0] = m;
+        const Cand A{buf0, c0, qn0, c0 + 1}, B{buf1, c1, qn1, two ? c1 + 1 : 0};
+        gram2_paced<D>(s, A, B, lane_r);
+        const uint64_t mask = fps2(s, A.n, B.n, m, lane_r);
+        write_rows<D>(s, (uint32_t)mask, buf0, c0, qn0, lane_r);
+        if (lane_r == 0) a.qcount[b0 + bi0] = m;
         if (a.fps_sel)
-            for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)(b0 + bi0) * m + i] = s.sel[0][i];
+            for (int i = lane_r; i < m; i += kWave) a.fps_sel[(size_t)(b0 + bi0) * m + i] = s.sel[0][i];
         if (two) {
-            write_rows<D>(s, (uint32_t)(mask >> 32), buf1, c1, qn1, lane);
-            if (lane == 0) a.qcount[b0 + bi1] = m;
+            write_rows<D>(s, (uint32_t)(mask >> 32), buf1, c1, qn1, lane_r);
+            if (lane_r == 0) a.qcount[b0 + bi1] = m;
             if (a.fps_sel)
-                for (int i = lane; i < m; i += kWave) a.fps_sel[(size_t)(b0 + bi1) * m + i] = s.sel[1][i];
+                for (int i = lane_r; i < m; i += kWave) a.fps_sel[(size_t)(b0 + bi1) * m + i] = s.sel[1][i];
         }
     }
 }
@@ -307,7 +381,10 @@ __device__ void merge_pair(const FpsArgs& a, int b, Smem& s, int lane) {
         }
     }
     if (!samples[0] && !samples[1]) return;
-    const uint64_t mask = select2<D>(s, c[0], c[1], m, lane);
+    u32x4_t row[D / 8];
+    load_rows<D>(row, c[0], c[1], lane);
+    gram2<D>(s, row, lane);
+    const uint64_t mask = fps2(s, c[0].n, c[1].n, m, lane);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (!samples[h]) continue;
