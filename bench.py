@@ -199,8 +199,44 @@ def stream_bench(args) -> int:
         "fps_rounds": {"per_buffer": rounds, "total": rounds * b.qbufs},
         "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
     }
+    if b.beacon == "fps" and b.n_recent_q > 0 and b.n_beacon > 0:
+        out["fps_round"] = fps_round_bench(run)
     print(json.dumps(out), flush=True)
     return 0
+
+
+FP32_MFMA_PEAK_TFS = 157.3   # MI355X dense fp32 matrix rate
+
+
+def fps_round_bench(run, reps: int = 10) -> dict:
+    """One sampling round of every buffer: bkv_fps_update with every count at B_Q^max - 1, on a copy of
+    the stream's buffers, timed alone with HIP events (the counts are reset between the timed calls).
+    Roofline: the Gram matrices are the matrix-core work, 2 n^2 d flops per buffer (all n^2 dot products,
+    as the definition takes them; n = B_Q^max), against the dense fp32 MFMA rate."""
+    b = run.base
+    n = b.n_beacon + b.n_recent_q
+    qbuf = run.qbuf.clone()
+    qc = torch.empty_like(run.qcount)
+    q_new = run.gen.block(1, run.pool)["q_new"][0]
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(reps + 2):
+        qc.fill_(n - 1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        L.fps_update(run.shape, qbuf, qc, q_new, None, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        if i >= 2:
+            ms.append(e0.elapsed_time(e1))
+    t = float(np.mean(ms))
+    flops = 2.0 * n * n * b.d * b.qbufs
+    achieved = flops / (t * 1e-3) / 1e12
+    del qbuf, qc
+    return {"buffers": b.qbufs, "rows": n, "ms": t, "ms_min": float(min(ms)),
+            "roofline": {"bound": "mfma", "kernel": "fps_kernel (update, every buffer sampling)",
+                         "achieved": achieved, "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": achieved / FP32_MFMA_PEAK_TFS, "flops_per_launch": flops}}
 
 
 def prefill_flops_per_row(d: int, m: int) -> int:
