@@ -165,10 +165,9 @@ __device__ void gram2(Smem& s, u32x4_t (&row)[D / 8], int lane) {
     cosines2(s, acc, h, i);
 }
 
-// Row loads of one half-wave set in groups of four 16-byte pieces: the next
-// group's loads are issued before the current group's 32 rank-1 updates, so
-// only the first group's latency is exposed and at most two groups' registers
-// are held.
+// Row loads of one half-wave set in groups of four 16-byte pieces, issued two
+// groups ahead of the group whose 32 rank-1 updates run, so only the first
+// group's latency is exposed and at most three groups' registers are held.
 template <int D>
 __device__ void gram2_paced(Smem& s, const Cand& c0, const Cand& c1, int lane) {
     constexpr int kGroups = D / 32;
@@ -179,17 +178,20 @@ __device__ void gram2_paced(Smem& s, const Cand& c0, const Cand& c1, int lane) {
     const int n0 = h ? c1.n0 : c0.n0;
     const int ic = i < n ? i : (n > 0 ? n - 1 : 0);
     const bkv_bf16* p = n > 0 ? cand_row(src0, n0, src1, ic, D) : src0;
-    u32x4_t g[2][4];
+    constexpr int kAhead = 2;   // groups in flight ahead of the one in use
+    u32x4_t g[kAhead + 1][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) g[0][q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
+    for (int gi = 0; gi < kAhead && gi < kGroups; ++gi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) g[gi][q] = *reinterpret_cast<const u32x4_t*>(p + gi * 32 + q * 8);
     f32x32_t acc = f32x32_t{};
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
-        u32x4_t (&cur)[4] = g[gi & 1];
-        if (gi + 1 < kGroups) {
-            u32x4_t (&nxt)[4] = g[(gi + 1) & 1];
+        u32x4_t (&cur)[4] = g[gi % (kAhead + 1)];
+        if (gi + kAhead < kGroups) {
+            u32x4_t (&nxt)[4] = g[(gi + kAhead) % (kAhead + 1)];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const u32x4_t*>(p + (gi + 1) * 32 + q * 8);
+            for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const u32x4_t*>(p + (gi + kAhead) * 32 + q * 8);
         }
         asm volatile("" : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3]));
 #pragma unroll
