@@ -205,6 +205,35 @@ def test_fps_merge_matches_oracle(qcount):
             assert np.array_equal(g[u, h, :n], v["qbuf"][u, h, :n])
 
 
+@pytest.mark.parametrize("d,nb,batch", [(64, 16, 3), (128, 16, 1001), (128, 31, 333), (64, 4, 5)])
+def test_fps_merge_adversarial_odd_counts(d, nb, batch):
+    """Merge over an odd number of buffers (the last wave has one), with adversarial contents and counts
+    from 0 to n_beacon, so pairs mix sampling and non-sampling buffers."""
+    rng = np.random.default_rng(400 + d + nb + batch)
+    cfg = TINY.scaled(d=d, n_layers=1, batch=batch, hq=3, hkv=1, n_beacon=nb, n_recent_q=32 - nb)
+    nbuf, G = cfg.qbufs, cfg.G
+    assert nbuf % 2 == 1
+    X = _adversarial_buffers(nbuf, d, cfg.qcap, rng)
+    R = _adversarial_buffers(nbuf, d, cfg.n_recent_q, rng) if cfg.n_recent_q >= 21 else \
+        rng.standard_normal((nbuf, cfg.n_recent_q, d)).astype(np.float32)
+    qb = torch.from_numpy(X).to(torch.bfloat16)
+    qr = torch.from_numpy(R).to(torch.bfloat16)
+    qc = rng.integers(0, nb + 1, nbuf).astype(np.int32)
+    qbuf_h = synth.to_u16(qb).reshape(cfg.units, G, cfg.qcap, d).copy()
+    qc_h = qc.reshape(cfg.units, G).copy()
+    sel_o = O.merge(H.ocfg(cfg), qbuf_h, qc_h, synth.to_u16(qr).reshape(cfg.units, G, cfg.n_recent_q, d))
+    qbuf_d = qb.cuda()
+    qc_d = torch.from_numpy(qc).cuda()
+    sel_d = torch.full((nbuf, nb), -7, dtype=torch.int32, device="cuda")
+    L.fps_merge(L.shape_of(cfg), qbuf_d, qc_d, qr.cuda(), sel_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel_d.cpu().numpy().reshape(cfg.units, G, -1), sel_o)
+    assert np.array_equal(qc_d.cpu().numpy().reshape(cfg.units, G), qc_h)
+    g = synth.to_u16(qbuf_d).reshape(cfg.units, G, cfg.qcap, d)
+    live = np.arange(cfg.qcap)[None, None, :, None] < qc_h[:, :, None, None]
+    assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
+
+
 # ---------------------------------------------------------------------------
 # Scores.
 
