@@ -86,6 +86,34 @@ def test_fps_update_matches_oracle(d, fill):
         assert np.array_equal(g[b, :n], qbuf_h[b, :n]), b
 
 
+@pytest.mark.parametrize("nb,nrq", [(32, 0), (0, 32), (31, 1), (1, 31), (4, 28), (28, 4)])
+def test_fps_update_splits(nb, nrq):
+    """Every split of the 32-row buffer, the degenerate ones included: n_recent_q = 0 (a full buffer keeps
+    all its rows) and n_beacon = 0 (a full buffer keeps none)."""
+    rng = np.random.default_rng(500 + nb)
+    cfg = TINY.scaled(d=128, n_layers=3, batch=5, hq=8, hkv=2, n_beacon=nb, n_recent_q=nrq)
+    nbuf, qcap, d = cfg.qbufs, cfg.qcap, cfg.d
+    X = _adversarial_buffers(nbuf, d, qcap, rng)
+    qb = torch.from_numpy(X).to(torch.bfloat16)
+    qn = torch.from_numpy(rng.standard_normal((nbuf, d)).astype(np.float32)).to(torch.bfloat16)
+    bqmax = nb + nrq
+    qc = np.where(rng.random(nbuf) < 0.5, bqmax - 1, rng.integers(0, bqmax, nbuf)).astype(np.int32)
+    qbuf_h = synth.to_u16(qb).copy()
+    qc_h = qc.copy()
+    sel_o = O.fps_update(qbuf_h, qc_h, synth.to_u16(qn), nb, nrq)
+    qbuf_d = qb.cuda()
+    qc_d = torch.from_numpy(qc).cuda()
+    sel_d = torch.full((nbuf, nb), -7, dtype=torch.int32, device="cuda")
+    L.fps_update(L.shape_of(cfg), qbuf_d, qc_d, qn.cuda(), sel_d if nb > 0 else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc_d.cpu().numpy(), qc_h)
+    if nb > 0:
+        assert np.array_equal(sel_d.cpu().numpy(), sel_o)
+    g = synth.to_u16(qbuf_d)
+    live = np.arange(qcap)[None, :, None] < qc_h[:, None, None]
+    assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
+
+
 @pytest.mark.parametrize("d,nbuf,nb", [(64, 100_000, 16), (128, 30_000, 16), (128, 30_000, 31)])
 def test_fps_update_several_buffers_per_wave(d, nbuf, nb):
     """More buffers than the chip holds waves at once, so each wave updates a run of them (one or more
