@@ -8,8 +8,8 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import (STREAM, TINY_STREAM, TINY_STREAM_MEAN, TINY_STREAM_SOURCES,
-                                               TINY_STREAM_SPLITS)
+from long_reasoning_decode_amd.configs import (STREAM, STREAM_SPLITS, TINY_STREAM, TINY_STREAM_MEAN,
+                                               TINY_STREAM_SOURCES, TINY_STREAM_SPLITS)
 from long_reasoning_decode_amd.stream import StreamRun
 
 from _stream_helpers import compare_stream, replay
@@ -135,3 +135,20 @@ def test_stream_full_size_sampled_units():
     assert r["evictions"] == scfg.evictions() == 240
     res = _check(scfg, run, units, "stream-qwen3-4b b192", nthreads=len(units))
     assert len(res["diverged"]) <= 2
+
+
+def test_stream_full_size_fps_every_step():
+    """Batch 192 with 31 beacons + 1 recent query, so every collection step samples all 221,184 buffers
+    (the update kernel's runs of full buffers, two per wave): the first three evictions, checked on units
+    spread over layers, batch elements and KV heads."""
+    scfg = next(c for c in STREAM_SPLITS if c.name == "stream-qwen3-4b-r1b31")
+    b = scfg.base
+    steps = b.cap + 2 * b.n_new
+    units = [0, b.units - 1, 3 * b.batch * b.hkv + 17 * b.hkv + 5, 30 * b.batch * b.hkv + 191 * b.hkv + 2]
+    run = StreamRun(scfg, record_units=units)
+    r = run.run(steps)
+    assert r["evictions"] == scfg.evictions(steps) == 3
+    assert run.fps_rounds_per_buffer(steps) > 2000
+    res = _check(scfg, run, units, "stream-qwen3-4b-r1b31 b192", nthreads=len(units))
+    assert len(res["diverged"]) <= 2
+
