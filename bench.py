@@ -138,6 +138,25 @@ def alg_bytes(cfg, qcount: np.ndarray, idx: np.ndarray, n_len: int) -> dict:
             "total": k_read + q_read + compact + buf, "moved_rows": int(moved.sum())}
 
 
+BF16_MFMA_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix rate
+
+
+def qkt_mfma(cfg, n_len: int, evict_ms: float, score_ms: float) -> dict:
+    """Matrix-core rate of the scoring's Q K^T.  Algorithmic: one product of the R observation rows with
+    the N keys per unit (R N d multiply-adds).  Issued: what the kernels run, two passes over the keys with
+    each query head's rows padded to 32 and the keys to whole 32-key tiles."""
+    R = cfg.G * (cfg.n_beacon + cfg.n_recent_q)
+    alg = 2.0 * R * n_len * cfg.d * cfg.units
+    tiles = (n_len + 31) // 32
+    issued = 2 * (2.0 * cfg.G * 32 * tiles * 32 * cfg.d * cfg.units)
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    return {"alg_flops": alg, "issued_flops": issued, "peak_TFs": BF16_MFMA_PEAK_TFS,
+            "evict_kernel": {"alg_TFs": tf(alg, evict_ms), "issued_TFs": tf(issued, evict_ms),
+                             "frac_issued": tf(issued, evict_ms) / BF16_MFMA_PEAK_TFS},
+            "score_kernel": {"alg_TFs": tf(alg, score_ms), "issued_TFs": tf(issued, score_ms),
+                             "frac_issued": tf(issued, score_ms) / BF16_MFMA_PEAK_TFS}}
+
+
 def cpu_baseline(cfg, inp, target_s: float = 10.0) -> dict:
     """The CPU oracle (as it stands) on a bounded sample of units."""
     import oracle as O
@@ -200,7 +219,7 @@ def stream_bench(args) -> int:
         "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
     }
     if b.beacon == "fps" and b.n_recent_q > 0 and b.n_beacon > 0:
-        out["fps_round"] = fps_round_bench(run)
+        out["fps_round"] = fps_round_bench(b, run.shape, run.qbuf, run.gen.block(1, run.pool)["q_new"][0])
     print(json.dumps(out), flush=True)
     return 0
 
@@ -208,23 +227,21 @@ def stream_bench(args) -> int:
 FP32_MFMA_PEAK_TFS = 157.3   # MI355X dense fp32 matrix rate
 
 
-def fps_round_bench(run, reps: int = 10) -> dict:
+def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10) -> dict:
     """One sampling round of every buffer: bkv_fps_update with every count at B_Q^max - 1, on a copy of
-    the stream's buffers, timed alone with HIP events (the counts are reset between the timed calls).
+    the given buffers, timed alone with HIP events (the counts are reset between the timed calls).
     Roofline: the Gram matrices are the matrix-core work, 2 n^2 d flops per buffer (all n^2 dot products,
     as the definition takes them; n = B_Q^max), against the dense fp32 MFMA rate."""
-    b = run.base
     n = b.n_beacon + b.n_recent_q
-    qbuf = run.qbuf.clone()
-    qc = torch.empty_like(run.qcount)
-    q_new = run.gen.block(1, run.pool)["q_new"][0]
+    qbuf = qbuf_src.clone()
+    qc = torch.empty(b.qbufs, dtype=torch.int32, device=qbuf.device)
     stream = torch.cuda.current_stream()
     ms = []
     for i in range(reps + 2):
         qc.fill_(n - 1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        L.fps_update(run.shape, qbuf, qc, q_new, None, stream=stream)
+        L.fps_update(shape, qbuf, qc, q_new, None, stream=stream)
         e1.record(stream)
         e1.synchronize()
         if i >= 2:
@@ -237,6 +254,26 @@ def fps_round_bench(run, reps: int = 10) -> dict:
             "roofline": {"bound": "mfma", "kernel": "fps_kernel (update, every buffer sampling)",
                          "achieved": achieved, "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": achieved / FP32_MFMA_PEAK_TFS, "flops_per_launch": flops}}
+
+
+def fps_round_main(args) -> int:
+    """Only the FPS sampling round, on buffers of a stream workload's shape filled with its query mixture."""
+    scfg = STREAM_CONFIGS[args.stream_config]
+    b = scfg.base
+    torch.cuda.set_device(0)
+    L.load()
+    print(f"# fps round {scfg.name}: {b.qbufs} buffers", file=sys.stderr, flush=True)
+    q = synth.make_query_buffers(b, device="cuda")
+    r = fps_round_bench(b, L.shape_of(b), q["qbuf"], q["q_new"], reps=args.steps)
+    out = {"metric": "FPS sampling round of every query buffer (bkv_fps_update, every buffer full)",
+           "value": 1000.0 / r["ms"], "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
+           "higher_is_better": True, "dtype": "f32 (bf16 rows)", "data": "synthetic",
+           "config": {"workload": f"{scfg.name} buffers: {b.n_layers} layers x batch {b.batch} x {b.hq} query "
+                                  f"heads ({b.qbufs} buffers of {b.qcap} x {b.d}), {b.n_beacon} beacons + "
+                                  f"{b.n_recent_q} recent queries"},
+           **r}
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def prefill_flops_per_row(d: int, m: int) -> int:
@@ -376,6 +413,8 @@ def main() -> int:
                          "(bkv_decode_step every step, bkv_evict when the cache is full) and print its own line")
     ap.add_argument("--stream-config", default=STREAM.name, choices=sorted(STREAM_CONFIGS))
     ap.add_argument("--stream-steps", type=int, default=0, help="decode steps (default: the config's)")
+    ap.add_argument("--fps-round", action="store_true",
+                    help="time only the FPS sampling round of every buffer at --stream-config's shape")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the eviction-step benchmark, time the prefill initialisation of every query "
                          "buffer (bkv_fps_prefill) and print its own line")
@@ -403,6 +442,8 @@ def main() -> int:
         return 2
     if args.stream:
         return stream_bench(args)
+    if args.fps_round:
+        return fps_round_main(args)
     if args.prefill:
         return prefill_bench(args)
     if args.decode:
@@ -504,6 +545,7 @@ def main() -> int:
                      "compact_alg_bytes": compact_bytes},
         "kernels_ms": kern_ms,
         "separate_calls_ms": sep_ms,
+        "mfma_qkt": qkt_mfma(cfg, N, kern_ms["evict_kernel"], sep_ms["score"]),
         "wall_s": wall,
     }
     if args.copy_calibration_mib > 0:
