@@ -73,22 +73,24 @@ __device__ __forceinline__ int dpp_min_step(int k) {
     return min(k, __builtin_amdgcn_update_dpp(0x7FFFFFFF, k, CTRL, ROW_MASK, 0xF, false));
 }
 
-// Per half-wave: the lowest lane of the half holding the half's smallest v
-// (no lane NaN), as an index 0..31, in every lane of the half.  Equal values
-// (+0 and -0 included) go to the lower lane, as in a scan that keeps the
-// first minimum.
-__device__ __forceinline__ int argmin_halves(float v, int lane) {
-    const int k = order_key(v);
+// Per half-wave: the lowest lane of the half holding the half's smallest
+// key, as an index 0..31, in every lane of the half.
+__device__ __forceinline__ int argmin_keys_halves(int k, int lane) {
     int m = dpp_min_step<0xB1>(k);        // quad_perm [1,0,3,2]
     m = dpp_min_step<0x4E>(m);            // quad_perm [2,3,0,1]
     m = dpp_min_step<0x141>(m);           // row_half_mirror
     m = dpp_min_step<0x140>(m);           // row_mirror: every lane of a row holds the row's minimum
     m = dpp_min_step<0x142, 0xA>(m);      // row_bcast15: rows 1 and 3 also take the previous row's
     const int m0 = __builtin_amdgcn_readlane(m, 31), m1 = __builtin_amdgcn_readlane(m, 63);
-    const uint64_t eq = __ballot(k == (lane < 32 ? m0 : m1));
-    const int r0 = __builtin_ctz((uint32_t)eq), r1 = __builtin_ctz((uint32_t)(eq >> 32));
+    const uint32_t e0 = (uint32_t)__ballot(k == m0);           // lanes 0..31 holding half 0's minimum
+    const uint32_t e1 = (uint32_t)(__ballot(k == m1) >> 32);   // lanes 32..63 holding half 1's
+    const int r0 = __builtin_ctz(e0), r1 = __builtin_ctz(e1);
     return lane < 32 ? r0 : r1;
 }
+
+// The same for float values (no lane NaN): equal values, +0 and -0
+// included, go to the lower lane, as in a scan that keeps the first minimum.
+__device__ __forceinline__ int argmin_halves(float v, int lane) { return argmin_keys_halves(order_key(v), lane); }
 
 // Every piece passes through one point as if rewritten there, so the
 // compiler issues all of their loads before it (one wait) and cannot
@@ -220,21 +222,21 @@ __device__ uint64_t fps2(Smem& s, int n0, int n1, int m, int lane) {
     }
     const float v = i < n ? sum / (float)n : __builtin_inff();
     const int p = argmin_halves(v, lane);
-    // lane i < n: S_i (cosines read along row r, equal to column r); lane i < m: the i-th pick
-    float S = s.c[h][p][i];
-    bool taken = i == p;
+    // lane i < n: the order key of S_i (the largest cosine to the rows taken; cosines read along row r,
+    // equal to column r), kOut once taken; lane i < m: the i-th pick.  Taking the maximum of keys is
+    // taking the maximum of the cosines, and keys compare as the cosines do.
+    constexpr int kOut = 0x7FFFFFFF;   // above every finite value's key
+    int Sk = ((i < n) & (i != p)) ? order_key(s.c[h][p][i]) : kOut;
     int pick = p;
     for (int it = 1; it < m; ++it) {
-        const float cv = ((i < n) & !taken) ? S : __builtin_inff();
-        const int r = argmin_halves(cv, lane);
-        taken = taken | (i == r);
+        const int r = argmin_keys_halves(Sk, lane);
         pick = i == it ? r : pick;
-        const float c = s.c[h][r][i];
-        S = (c > S) ? c : S;
+        const int ck = order_key(s.c[h][r][i]);
+        Sk = i == r ? kOut : max(Sk, ck);
     }
     if (i < m) s.sel[h][i] = pick;
     wave_lds_sync();
-    return __ballot(taken);
+    return __ballot((Sk == kOut) & (i < n));
 }
 
 // Copy the rows in `mask` (ascending) to dst[0..), dst == src0 (in place;
