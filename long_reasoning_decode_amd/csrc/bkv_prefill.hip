@@ -331,7 +331,164 @@ __device__ __forceinline__ void fetch_row(const bkv_bf16* Q, int P, int j, int s
     }
 }
 
+// ---- register rows in fp32 (when every other row fits in LDS): no unpacking
+// of the register-resident rows on any pass.
+
+template <int D, int R, bool F32>
+struct RegRows {
+    using type = u32x4_t[R][D / 8];   // packed bf16
+};
+template <int D, int R>
+struct RegRows<D, R, true> {
+    using type = float[R][D];
+};
+
 template <int D>
+__device__ __forceinline__ void to_reg(const u32x4_t (&w)[D / 8], u32x4_t (&x)[D / 8]) {
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) x[p] = w[p];
+}
+template <int D>
+__device__ __forceinline__ void to_reg(const u32x4_t (&w)[D / 8], float (&x)[D]) {
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[8 * p + 2 * e] = __uint_as_float(w[p][e] << 16);
+            x[8 * p + 2 * e + 1] = __uint_as_float(w[p][e] & 0xFFFF0000u);
+        }
+}
+
+template <int D>
+__device__ __forceinline__ float norm_of(const float (&x)[D]) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < D; ++k) acc = __builtin_fmaf(x[k], x[k], acc);
+    return __builtin_sqrtf(acc);
+}
+
+// fma_rows for fp32 rows: the same chains, with the same piece pacing of y.
+// The scale factors pass through an opaque copy, so the products x * inv are
+// not shared with the column sums' (keeping them from one pass to the next
+// would hold a second fp32 row).
+template <int D, int R, bool SCALE>
+__device__ __forceinline__ void fma_rows(const float (&x)[R][D], const float* y, const float* inv_in,
+                                         float (&acc)[R]) {
+    constexpr int NP = D / 8;
+    float inv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        inv[r] = SCALE ? inv_in[r] : 0.0f;
+        asm volatile("" : "+v"(inv[r]));
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    f32x4_t ya = *reinterpret_cast<const f32x4_t*>(y);
+    f32x4_t yb = *reinterpret_cast<const f32x4_t*>(y + 4);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        f32x4_t na = ya, nb = yb;
+        if (p + 1 < NP) {
+            na = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1));
+            nb = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1) + 4);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = SCALE ? x[r][8 * p + k] * inv[r] : x[r][8 * p + k];
+            float a = acc[r];
+            a = __builtin_fmaf(e[0], ya[0], a);
+            a = __builtin_fmaf(e[1], ya[1], a);
+            a = __builtin_fmaf(e[2], ya[2], a);
+            a = __builtin_fmaf(e[3], ya[3], a);
+            a = __builtin_fmaf(e[4], yb[0], a);
+            a = __builtin_fmaf(e[5], yb[1], a);
+            a = __builtin_fmaf(e[6], yb[2], a);
+            a = __builtin_fmaf(e[7], yb[3], a);
+            piece_fence(a);
+            acc[r] = a;
+        }
+        ya = na;
+        yb = nb;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void chunk_colsum(const float (&x)[D], float inv, int c, float* part, float* csum, int wave,
+                                             int lane, int tid) {
+#pragma unroll
+    for (int p = 0; p < D / 8; ++p) {
+        float s8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s8[e] = wave_pairwise_sum(x[8 * p + e] * inv);
+        if (lane == 63) {
+            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p) = f32x4_t{s8[0], s8[1], s8[2], s8[3]};
+            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p + 4) = f32x4_t{s8[4], s8[5], s8[6], s8[7]};
+        }
+        asm volatile("" ::: "memory");
+    }
+    __syncthreads();
+    if (tid < D) {
+        const float* q = part + tid;
+        const float s01 = q[0 * D] + q[1 * D], s23 = q[2 * D] + q[3 * D];
+        const float s45 = q[4 * D] + q[5 * D], s67 = q[6 * D] + q[7 * D];
+        csum[c * D + tid] = (s01 + s23) + (s45 + s67);
+    }
+    __syncthreads();
+}
+
+template <int D>
+__device__ __forceinline__ void store_row_f32(const float (&x)[D], float* dst) {
+#pragma unroll
+    for (int k = 0; k < D; k += 4) *reinterpret_cast<f32x4_t*>(dst + k) = f32x4_t{x[k], x[k + 1], x[k + 2], x[k + 3]};
+}
+
+// The fma chain of LDS row s (scaled by inv with SCALE) against y, its pieces
+// read one ahead instead of the whole row at once.
+template <int D, bool SCALE>
+__device__ __forceinline__ float fma_lds_row(const u32x4_t* lrows, int s, const float* y, float inv) {
+    const Bf u = Bf::fresh();
+    constexpr int NP = D / 8;
+    float acc = 0.0f;
+    u32x4_t w = lrows[lds_slot<D>(s, 0)];
+    f32x4_t ya = *reinterpret_cast<const f32x4_t*>(y);
+    f32x4_t yb = *reinterpret_cast<const f32x4_t*>(y + 4);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        u32x4_t nw = w;
+        f32x4_t na = ya, nb = yb;
+        if (p + 1 < NP) {
+            nw = lrows[lds_slot<D>(s, p + 1)];
+            na = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1));
+            nb = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1) + 4);
+        }
+        float e[8] = {u.lo(w[0]), u.hi(w[0]), u.lo(w[1]), u.hi(w[1]),
+                      u.lo(w[2]), u.hi(w[2]), u.lo(w[3]), u.hi(w[3])};
+        if constexpr (SCALE) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = e[k] * inv;
+        }
+        acc = __builtin_fmaf(e[0], ya[0], acc);
+        acc = __builtin_fmaf(e[1], ya[1], acc);
+        acc = __builtin_fmaf(e[2], ya[2], acc);
+        acc = __builtin_fmaf(e[3], ya[3], acc);
+        acc = __builtin_fmaf(e[4], yb[0], acc);
+        acc = __builtin_fmaf(e[5], yb[1], acc);
+        acc = __builtin_fmaf(e[6], yb[2], acc);
+        acc = __builtin_fmaf(e[7], yb[3], acc);
+        piece_fence(acc);
+        w = nw;
+        ya = na;
+        yb = nb;
+    }
+    return acc;
+}
+
+// F32: the register-resident rows are kept in fp32 and the LDS rows are
+// streamed piece by piece; only when every row outside the registers is in
+// LDS (no global tier), where the registers allow it.
+template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     using L = Pre<D>;
     constexpr int RC = L::kRegChunks;
@@ -373,18 +530,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     float* Sst = nst + n_other;                                   // their S (NaN once taken)
     u32x4_t* lrows = reinterpret_cast<u32x4_t*>(smem + L::rows_off(P));
 
-    u32x4_t xv[RC][D / 8];
-    float nrm[RC];
-#pragma unroll
-    for (int c = 0; c < RC; ++c) load_row<D>(Q, P, c * kThreads + tid, xv[c]);
-
-    // ---- norms and column sums of the unit rows, chunk by chunk; rows past
-    // the registers are copied into LDS on the way while there is room
-#pragma unroll
-    for (int c = 0; c < RC; ++c) nrm[c] = norm_of<D>(xv[c]);
-#pragma unroll
-    for (int c = 0; c < RC; ++c)
-        if (c < C) chunk_colsum<D>(xv[c], inv_of(nrm[c]), c, part, csum, wave, lane, tid);
+    // ---- norms and column sums of the unit rows, chunk by chunk (each chunk's
+    // sums go to its own slot, so the order of the chunks does not matter).
+    // The rows past the registers come first, copied into LDS on the way while
+    // there is room; then the register rows are loaded.
 #pragma unroll 1
     for (int c = RC; c < C; ++c) {
         const int j = c * kThreads + tid, s = j - RR;
@@ -400,6 +549,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
         chunk_colsum<D>(tmp, inv_of(nr), c, part, csum, wave, lane, tid);
     }
+    typename RegRows<D, RC, F32>::type xv;
+    float nrm[RC];
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+        u32x4_t w[D / 8];
+        load_row<D>(Q, P, c * kThreads + tid, w);
+        to_reg<D>(w, xv[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < RC; ++c) nrm[c] = norm_of<D>(xv[c]);
+#pragma unroll
+    for (int c = 0; c < RC; ++c)
+        if (c < C) chunk_colsum<D>(xv[c], inv_of(nrm[c]), c, part, csum, wave, lane, tid);
     // pairwise over the chunks, bottom-up in place; chunks past the last are zero
     if (tid < D) {
         int Cp = 1;
@@ -435,9 +597,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     for (int c = RC; c < C; ++c) {
         const int j = c * kThreads + tid, s = j - RR;
         if (j >= P) break;
-        u32x4_t tmp[D / 8];
-        fetch_row<D>(Q, P, j, s, n_lds, lrows, tmp);
-        const float av = mean_cos<D>(tmp, inv_of(nst[s]), ssum + opaque_zero(), fP);
+        float av;
+        if constexpr (F32) {
+            av = fma_lds_row<D, true>(lrows, s, ssum + opaque_zero(), inv_of(nst[s])) / fP;
+        } else {
+            u32x4_t tmp[D / 8];
+            fetch_row<D>(Q, P, j, s, n_lds, lrows, tmp);
+            av = mean_cos<D>(tmp, inv_of(nst[s]), ssum + opaque_zero(), fP);
+        }
         if (bi == kNone || av < bv) {
             bv = av;
             bi = j;
@@ -468,11 +635,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                     }
             } else {
                 const int s = r - RR;
-                u32x4_t tmp[D / 8];
-                fetch_row<D>(Q, P, r, s, n_lds, lrows, tmp);
                 xn[par] = nst[s];
                 Sst[s] = __builtin_nanf("");
-                store_row_f32<D>(tmp, dst);
+                if constexpr (F32) {   // piece by piece from LDS
+#pragma unroll 1
+                    for (int p = 0; p < D / 8; ++p) {
+                        const u32x4_t w = lrows[lds_slot<D>(s, p)];
+                        *reinterpret_cast<f32x4_t*>(dst + 8 * p) =
+                            f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                                    __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+                        *reinterpret_cast<f32x4_t*>(dst + 8 * p + 4) =
+                            f32x4_t{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                                    __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u)};
+                    }
+                } else {
+                    u32x4_t tmp[D / 8];
+                    fetch_row<D>(Q, P, r, s, n_lds, lrows, tmp);
+                    store_row_f32<D>(tmp, dst);
+                }
             }
         }
         __syncthreads();
@@ -502,9 +682,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             if (j >= P) break;
             float sv = Sst[s];
             if (sv != sv) continue;   // taken
-            u32x4_t tmp[D / 8];
-            fetch_row<D>(Q, P, j, s, n_lds, lrows, tmp);
-            const float cs = cos_to<D>(tmp, nst[s], y + opaque_zero(), ny);
+            float cs;
+            if constexpr (F32) {
+                const float nx = nst[s];
+                const float dt = fma_lds_row<D, false>(lrows, s, y + opaque_zero(), 0.0f);
+                cs = (nx == 0.0f || ny == 0.0f) ? 0.0f : dt / (nx * ny);
+            } else {
+                u32x4_t tmp[D / 8];
+                fetch_row<D>(Q, P, j, s, n_lds, lrows, tmp);
+                cs = cos_to<D>(tmp, nst[s], y + opaque_zero(), ny);
+            }
             if (cs > sv) sv = cs;
             Sst[s] = sv;
             if (bi == kNone || sv < bv) {
@@ -539,7 +726,11 @@ hipError_t launch_d(PrefillArgs a, hipStream_t st) {
     if (e != hipSuccess) return e;
     a.lds_bytes = lim < kLdsBytes ? lim : kLdsBytes;
     if ((int)Pre<D>::rows_off(a.P) > a.lds_bytes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<D>), dim3(a.nbuf), dim3(kThreads), Pre<D>::bytes(a.P, a.lds_bytes), st, a);
+    const size_t lds = Pre<D>::bytes(a.P, a.lds_bytes);
+    if (Pre<D>::n_lds_rows(a.P, a.lds_bytes) >= Pre<D>::n_other(a.P))   // no rows re-read from memory
+        hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(a.nbuf), dim3(kThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(a.nbuf), dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 
