@@ -207,7 +207,8 @@ __device__ void gram2_paced(Smem& s, const Cand& c0, const Cand& c1, int lane) {
 }
 
 // FPS over the cosine matrices in s.c of the two halves' sets (n0 and n1
-// rows, each n > m >= 1 or 0 for an empty half).  Leaves the selection
+// rows, each n > m, or 0 for an empty half; with m = 0 only the seed is
+// marked taken, and the caller keeps no rows).  Leaves the selection
 // orders in s.sel[h][0..m) and returns the taken rows, half h in bits
 // 32h .. 32h + 31.
 __device__ uint64_t fps2(Smem& s, int n0, int n1, int m, int lane) {
@@ -241,10 +242,10 @@ __device__ uint64_t fps2(Smem& s, int n0, int n1, int m, int lane) {
 
 // Copy the rows in `mask` (ascending) to dst[0..), dst == src0 (in place;
 // rows r < n0 come from src0, the rest from src1).  Rows already in place
-// are skipped.  The rows go in groups of 8
-// destinations, each group's loads issued (and, by in-order completion,
-// returned) before its stores; a kept row's source slot is never below its
-// destination, so no group reads a slot an earlier group wrote.
+// are skipped.  The rows go in groups of 8 destinations, each group's loads
+// issued (and, by in-order completion, returned) before its stores; a kept
+// row's source slot is never below its destination, so no group reads a slot
+// an earlier group wrote.
 template <int D>
 __device__ void write_rows(Smem& s, uint32_t mask, bkv_bf16* src0, int n0, const bkv_bf16* src1, int lane) {
     constexpr int kChunks = D / 8;                          // 16-byte pieces per row
