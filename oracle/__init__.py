@@ -33,7 +33,7 @@ class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int) for n in (
         "n_layers", "batch", "hq", "hkv", "d", "cap", "budget", "n_prefix",
         "n_recent_kv", "n_beacon", "n_recent_q", "causal", "qcap", "pool_mean", "beacon_src")] + [
-        ("seed", C.c_uint), ("theta", C.c_double)]
+        ("seed", C.c_uint), ("theta", C.c_double), ("unit_ids", C.c_void_p)]
 
 
 @dataclass
@@ -55,12 +55,20 @@ class OracleCfg:
     seed: int = 0
     n_layers: int = 1
     batch: int = 1
+    unit_ids: object = None   # global unit index of each unit passed (a sample of the workload's units)
+
+    def check_units(self, U: int) -> None:
+        assert self.unit_ids is None or len(self.unit_ids) == U, "one global unit index per unit passed"
 
     def c(self) -> _Cfg:
+        ids = None
+        if self.unit_ids is not None:
+            self._ids = np.ascontiguousarray(self.unit_ids, dtype=np.int64)   # kept alive with the config
+            ids = self._ids.ctypes.data
         return _Cfg(self.n_layers, self.batch, self.hq, self.hkv, self.d, self.cap,
                     self.budget, self.n_prefix, self.n_recent_kv, self.n_beacon,
                     self.n_recent_q, self.causal, self.qcap, self.pool_mean, self.beacon_src,
-                    self.seed & 0xFFFFFFFF, float(self.theta))
+                    self.seed & 0xFFFFFFFF, float(self.theta), ids)
 
     @property
     def G(self) -> int:
@@ -278,6 +286,7 @@ def evict(cfg: OracleCfg, K, V, qbuf, qcount, q_recent, pos_recent, t, n_len: in
     for a, dt in ((K, np.uint16), (V, np.uint16), (qbuf, np.uint16), (qcount, np.int32)):
         assert a.dtype == dt and a.flags["C_CONTIGUOUS"]
     U = K.shape[0]
+    cfg.check_units(U)
     N = cfg.cap if n_len is None else n_len
     idx = np.empty((U, cfg.budget), dtype=np.int32)
     scores = np.empty((U, N), dtype=np.float64)
@@ -294,6 +303,7 @@ def merge(cfg: OracleCfg, qbuf, qcount, q_recent) -> np.ndarray:
     assert qbuf.dtype == np.uint16 and qbuf.flags["C_CONTIGUOUS"]
     assert qcount.dtype == np.int32 and qcount.flags["C_CONTIGUOUS"]
     U = qbuf.shape[0]
+    cfg.check_units(U)
     fps_sel = np.empty((U, cfg.G, cfg.n_beacon), dtype=np.int32)
     cc = cfg.c()
     lib().bkvo_merge(C.byref(cc), U, _p(qbuf), _p(qcount), _p(_u16(q_recent)), _p(fps_sel))
@@ -331,6 +341,7 @@ def stream(cfg: OracleCfg, k_new, v_new, q_new, pos, K, V, L: int, qbuf, qcount,
         assert a.dtype == dt and a.flags["C_CONTIGUOUS"]
     k_new, v_new, q_new, pos = _u16(k_new), _u16(v_new), _u16(q_new), _i32(pos)
     S, U = pos.shape
+    cfg.check_units(U)
     assert k_new.shape == (S, U, cfg.d) and v_new.shape == (S, U, cfg.d)
     assert q_new.shape == (S, U, cfg.G, cfg.d)
     idx = np.full((max_ev, U, cfg.budget), -1, dtype=np.int32) if max_ev > 0 else None

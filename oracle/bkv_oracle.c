@@ -51,7 +51,13 @@ typedef struct {
     int beacon_src;   /* 0: continual FPS; 1: initial queries; 2: random history (reservoir) */
     unsigned seed;    /* key of the random-history draws */
     double theta;     /* RoPE base */
+    /* Global unit index of each unit passed, for calls on a sample of the
+     * workload's units: the random-history draws are keyed by the global
+     * buffer index u * G + h.  NULL: the units passed are 0, 1, ... */
+    const long long *unit_ids;
 } bkvo_cfg;
+
+static long long global_unit(const bkvo_cfg *c, int u) { return c->unit_ids ? c->unit_ids[u] : (long long)u; }
 
 enum { BKVO_SRC_FPS = 0, BKVO_SRC_INITIAL = 1, BKVO_SRC_RANDOM = 2 };
 
@@ -751,7 +757,7 @@ static void merge_unit(const bkvo_cfg *c, int u, uint16_t *qbuf, int32_t *qcount
             size_t b = (size_t)u * G + h;
             if (c->beacon_src == BKVO_SRC_RANDOM)
                 for (int i = 0; i < c->n_recent_q; ++i)
-                    offer(c, (long long)b, qbuf + b * c->qcap * d, qcount + b,
+                    offer(c, global_unit(c, u) * G + h, qbuf + b * c->qcap * d, qcount + b,
                           q_recent + (b * c->n_recent_q + i) * d);
             if (fps_sel)
                 for (int i = 0; i < c->n_beacon; ++i) fps_sel[b * c->n_beacon + i] = -1;
@@ -935,7 +941,7 @@ static void *run_stream_units(void *arg)
             memcpy(Vu + (size_t)L * d, J->v_new + su * d, sizeof(uint16_t) * (size_t)d);
             const uint16_t *qn = J->q_new + su * G * d;
             if (L < ring0) {
-                bkvo_beacon_update(c, G, (long long)u * G, J->qbuf + (size_t)u * G * c->qcap * d,
+                bkvo_beacon_update(c, G, global_unit(c, u) * G, J->qbuf + (size_t)u * G * c->qcap * d,
                                    J->qcount + (size_t)u * G, qn, NULL);
             } else {
                 int i = L - ring0;

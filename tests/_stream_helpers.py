@@ -10,13 +10,16 @@ from long_reasoning_decode_amd.configs import StreamConfig
 from _helpers import check_keep, check_scores
 
 
-def stream_ocfg(scfg: StreamConfig) -> O.OracleCfg:
+def stream_ocfg(scfg: StreamConfig, units=None) -> O.OracleCfg:
+    """Oracle configuration of a stream workload; units: the global indices of the units replayed, when
+    they are a sample of the workload's (the random-history draws are keyed by the global buffer index)."""
     b = scfg.base
     return O.OracleCfg(hq=b.hq, hkv=b.hkv, d=b.d, cap=b.cap, budget=b.budget, n_prefix=b.n_prefix,
                        n_recent_kv=b.n_recent_kv, n_beacon=b.n_beacon, n_recent_q=b.n_recent_q, theta=b.theta,
                        qcap=b.qcap, pool_mean=int(b.pool == "mean"),
                        beacon_src={"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM}[b.beacon],
-                       seed=b.seed & 0xFFFFFFFF, n_layers=b.n_layers, batch=b.batch)
+                       seed=b.seed & 0xFFFFFFFF, n_layers=b.n_layers, batch=b.batch,
+                       unit_ids=None if units is None else list(units))
 
 
 def empty_state(scfg: StreamConfig, U: int) -> dict:
@@ -28,10 +31,11 @@ def empty_state(scfg: StreamConfig, U: int) -> dict:
             "pos_recent": np.zeros((U, b.n_recent_q), np.int32)}
 
 
-def replay(scfg: StreamConfig, k_new, v_new, q_new, pos, max_ev: int, nthreads=None) -> dict:
-    """Oracle stream from an empty state over step-major inputs of U units."""
+def replay(scfg: StreamConfig, k_new, v_new, q_new, pos, max_ev: int, nthreads=None, units=None) -> dict:
+    """Oracle stream from an empty state over step-major inputs of U units (units: their global indices,
+    when they are a sample of the workload's)."""
     st = empty_state(scfg, pos.shape[1])
-    o = O.stream(stream_ocfg(scfg), k_new, v_new, q_new, pos, st["K"], st["V"], 0, st["qbuf"], st["qcount"],
+    o = O.stream(stream_ocfg(scfg, units), k_new, v_new, q_new, pos, st["K"], st["V"], 0, st["qbuf"], st["qcount"],
                  st["q_recent"], st["pos_recent"], max_ev=max_ev, nthreads=nthreads)
     o.update(st)
     return o

@@ -8,7 +8,7 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import (STREAM, STREAM_SPLITS, TINY_STREAM, TINY_STREAM_MEAN,
+from long_reasoning_decode_amd.configs import (STREAM, STREAM_SOURCES, STREAM_SPLITS, TINY_STREAM, TINY_STREAM_MEAN,
                                                TINY_STREAM_SOURCES, TINY_STREAM_SPLITS)
 from long_reasoning_decode_amd.stream import StreamRun
 
@@ -34,7 +34,7 @@ def _check(scfg, run: StreamRun, units, where, nthreads=None):
     h = run.history()
     u16 = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
     o = replay(scfg, u16(h["k_new"]), u16(h["v_new"]), u16(h["q_new"]), h["pos"].numpy().astype(np.int32),
-               max_ev=run.n_ev, nthreads=nthreads)
+               max_ev=run.n_ev, nthreads=nthreads, units=units)
     assert o["n_ev"] == run.n_ev and o["L"] == run.L
     res = compare_stream(scfg, o, h["idx"].numpy(), h["scores"].numpy(), _gpu_state(run, units), where)
     print(f"{where}: {run.n_ev} evictions, L={run.L}, tie-band divergences {res['diverged']}", flush=True)
@@ -134,6 +134,22 @@ def test_stream_full_size_sampled_units():
     r = run.run(progress=prog)
     assert r["evictions"] == scfg.evictions() == 240
     res = _check(scfg, run, units, "stream-qwen3-4b b192", nthreads=len(units))
+    assert len(res["diverged"]) <= 2
+
+
+@pytest.mark.parametrize("src", ["initial", "random"])
+def test_stream_full_size_beacon_sources(src):
+    """Batch 192 with the beacons drawn from the initial queries or by reservoir sampling of the history
+    (one offer per buffer and step, the merge offering the cycle's recents): the first three evictions,
+    checked on units spread over layers, batch elements and KV heads."""
+    scfg = next(c for c in STREAM_SOURCES if c.base.beacon == src)
+    b = scfg.base
+    steps = b.cap + 2 * b.n_new
+    units = [5, b.units - 2, 11 * b.batch * b.hkv + 77 * b.hkv + 1, 27 * b.batch * b.hkv + 140 * b.hkv + 7]
+    run = StreamRun(scfg, record_units=units)
+    r = run.run(steps)
+    assert r["evictions"] == scfg.evictions(steps) == 3
+    res = _check(scfg, run, units, f"{scfg.name} b192", nthreads=len(units))
     assert len(res["diverged"]) <= 2
 
 

@@ -106,3 +106,24 @@ def test_stream_eviction_boundaries(S):
     assert o["n_ev"] == scfg.evictions(S)
     expect_L = S if S < b.cap else b.budget + (S - b.cap) % b.n_new
     assert o["L"] == expect_L
+
+
+@pytest.mark.parametrize("scfg", TINY_STREAM_SOURCES + (TINY_STREAM,), ids=lambda c: c.name)
+def test_stream_on_a_sample_of_units(scfg):
+    """Replaying a sample of the units, given their global indices, leaves each of them in the state the
+    whole workload's replay leaves it: the random history's draws are keyed by the global buffer index,
+    so without the indices the sampled replay of that source diverges."""
+    b = scfg.base
+    S = 230
+    x = _inputs(scfg, S)
+    full = replay(scfg, x["k_new"], x["v_new"], x["q_new"], x["pos"], max_ev=3, nthreads=2)
+    units = [b.units - 1, 1]
+    sub = {k: np.ascontiguousarray(v[:, units]) for k, v in x.items()}
+    part = replay(scfg, sub["k_new"], sub["v_new"], sub["q_new"], sub["pos"], max_ev=3, nthreads=2, units=units)
+    for key in ("K", "V", "qbuf", "qcount", "q_recent", "pos_recent", "idx"):
+        ref = full[key][:, units] if key == "idx" else full[key][units]
+        assert np.array_equal(part[key], ref), key
+    if b.beacon == "random":
+        blind = replay(scfg, sub["k_new"], sub["v_new"], sub["q_new"], sub["pos"], max_ev=3, nthreads=2)
+        assert not np.array_equal(blind["qbuf"], full["qbuf"][units])
+
