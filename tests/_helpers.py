@@ -104,6 +104,7 @@ def compare_evict(cfg: EvictConfig, inp: dict, out: dict, n_len: int, units=None
     units = list(range(U)) if units is None else list(units)
     v = synth.oracle_views(cfg, inp, units)
     oc = ocfg(cfg, n_len=inp["K"].shape[-2], flags=flags)
+    oc.unit_ids = units   # the random history's draws are keyed by the global buffer index
     K0, V0 = v["K"].copy(), v["V"].copy()
     o = O.evict(oc, v["K"], v["V"], v["qbuf"], v["qcount"], v["q_recent"], v["pos_recent"], v["t"],
                 n_len=n_len)

@@ -444,6 +444,23 @@ def test_evict_matches_oracle(cfg, n_len, flags):
 FULL = [QWEN3_4B, R1_QWEN_7B, QWEN3_14B_1K, QWEN3_14B_4K, QWEN3_4B_MEAN]
 
 
+@pytest.mark.parametrize("flags", [L.BKV_CAUSAL_RECENT | L.BKV_BEACON_INITIAL, L.BKV_CAUSAL_RECENT | L.BKV_BEACON_RANDOM],
+                         ids=["initial", "random"])
+def test_evict_full_size_beacon_sources(flags):
+    """Full qwen3-4b size with the other beacon sources (the merge offers the recents to the reservoir, keyed
+    by the global buffer index), checked on a sample of units."""
+    cfg = QWEN3_4B
+    _flush(f"full-size evict {cfg.name} flags {flags}")
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    out = H.run_evict_gpu(cfg, inp, cfg.n_len, flags=flags)
+    rng = np.random.default_rng(8)
+    units = sorted(set([0, cfg.units - 1] + rng.choice(cfg.units, 14, replace=False).tolist()))
+    r = H.compare_evict(cfg, inp, out, cfg.n_len, units=units, flags=flags, where=f"{cfg.name} flags {flags}")
+    _flush(f"  tie-band differences in sample: {r['n_tie_diff']}")
+    del inp, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
 def test_evict_full_size_sampled_units(cfg):
     """Full workload size, same launch as the benchmark; the oracle checks a
