@@ -192,6 +192,28 @@ def test_source_update_matches_oracle(src, d):
         assert np.array_equal(synth.to_u16(qbuf_d), qbuf_h), step
 
 
+def test_random_source_update_many_buffers():
+    """The random history at the stream's buffer count (221,184 buffers): two updates, every buffer
+    compared (the draws are keyed by each buffer's global index)."""
+    rng = np.random.default_rng(311)
+    cfg = TINY.scaled(d=128, n_layers=36, batch=192, hq=32, hkv=8, beacon="random", seed=777)
+    nbuf, qcap, d = cfg.qbufs, cfg.qcap, cfg.d
+    assert nbuf == 221184
+    oc = H.ocfg(cfg)
+    qbuf_h = (rng.integers(0, 1 << 16, size=(nbuf, qcap, d), dtype=np.uint16) & 0xBFFF).astype(np.uint16)
+    qc_h = rng.integers(0, 3000, size=nbuf).astype(np.int32)
+    qbuf_d = torch.from_numpy(qbuf_h.view(np.int16)).cuda().view(torch.bfloat16)
+    qc_d = torch.from_numpy(qc_h.copy()).cuda()
+    shape = L.shape_of(cfg)
+    for step in range(2):
+        qn = (rng.integers(0, 1 << 16, size=(nbuf, d), dtype=np.uint16) & 0xBFFF).astype(np.uint16)
+        O.beacon_update(oc, qbuf_h, qc_h, qn)
+        L.fps_update(shape, qbuf_d, qc_d, torch.from_numpy(qn.view(np.int16)).cuda().view(torch.bfloat16), None)
+        torch.cuda.synchronize()
+        assert np.array_equal(qc_d.cpu().numpy(), qc_h), step
+        assert np.array_equal(synth.to_u16(qbuf_d), qbuf_h), step
+
+
 @pytest.mark.parametrize("src", ["initial", "random"])
 def test_source_merge_matches_oracle(src):
     cfg = QWEN3_4B.scaled(n_layers=2, batch=3, beacon=src, seed=777)
