@@ -92,38 +92,6 @@ __device__ __forceinline__ int argmin_keys_halves(int k, int lane) {
 // included, go to the lower lane, as in a scan that keeps the first minimum.
 __device__ __forceinline__ int argmin_halves(float v, int lane) { return argmin_keys_halves(order_key(v), lane); }
 
-// Every piece passes through one point as if rewritten there, so the
-// compiler issues all of their loads before it (one wait) and cannot
-// re-issue a load later in place of keeping its registers.
-template <int N>
-__device__ __forceinline__ void hold_all(u32x4_t (&r)[N]) {
-    if constexpr (N == 8) {
-        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
-                          "+v"(r[7]));
-    } else {
-        static_assert(N == 16, "row pieces: 8 (d = 64) or 16 (d = 128)");
-        asm volatile("" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
-                          "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]),
-                          "+v"(r[14]), "+v"(r[15]));
-    }
-}
-
-// Row i of half h's candidate set into `row`, 8 bf16 per piece (loads issued,
-// not waited for).  Lanes past n load a copy of row n - 1 (row 0 of src0 in
-// an empty half): their dot products are computed but never read.
-template <int D>
-__device__ __forceinline__ void load_rows(u32x4_t (&row)[D / 8], const Cand& c0, const Cand& c1, int lane) {
-    const int h = lane >> 5, i = lane & 31;
-    const int n = h ? c1.n : c0.n;
-    const bkv_bf16* src0 = h ? c1.src0 : c0.src0;
-    const bkv_bf16* src1 = h ? c1.src1 : c0.src1;
-    const int n0 = h ? c1.n0 : c0.n0;
-    const int ic = i < n ? i : (n > 0 ? n - 1 : 0);
-    const bkv_bf16* p = n > 0 ? cand_row(src0, n0, src1, ic, D) : src0;
-#pragma unroll
-    for (int q = 0; q < D / 8; ++q) row[q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
-}
-
 // Gram entries acc (as laid out by the rank-1 updates) into s.c, the norms
 // into s.nrm, then the cosines over the Gram entries in s.c.
 __device__ __forceinline__ void cosines2(Smem& s, const f32x32_t& acc, int h, int i) {
@@ -150,28 +118,14 @@ __device__ __forceinline__ void cosines2(Smem& s, const f32x32_t& acc, int h, in
     wave_lds_sync();
 }
 
-// Cosine matrices of both halves' rows into s.c (and the norms into s.nrm).
-// The row loads are all waited for at once.
+// Cosine matrices of both halves' sets into s.c (and the norms into s.nrm).
+// Lane i of half h loads row i of set h (lanes past n load a copy of row
+// n - 1, or row 0 of src0 in an empty half: their dot products are computed
+// but never read) in groups of four 16-byte pieces, issued two groups ahead
+// of the group whose 32 rank-1 updates run, so only the first group's latency
+// is exposed and at most three groups' registers are held.
 template <int D>
-__device__ void gram2(Smem& s, u32x4_t (&row)[D / 8], int lane) {
-    const int h = lane >> 5, i = lane & 31;
-    hold_all(row);
-    // acc[r] = dot of rows (8 ((r % 16) / 4) + 4 h + r % 4, i) of half r / 16
-    f32x32_t acc = f32x32_t{};
-#pragma unroll
-    for (int k = 0; k < D; ++k) {
-        const uint32_t w = row[k / 8][(k % 8) / 2];
-        const float v = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(v, v, acc, 0, 0, 0);
-    }
-    cosines2(s, acc, h, i);
-}
-
-// Row loads of one half-wave set in groups of four 16-byte pieces, issued two
-// groups ahead of the group whose 32 rank-1 updates run, so only the first
-// group's latency is exposed and at most three groups' registers are held.
-template <int D>
-__device__ void gram2_paced(Smem& s, const Cand& c0, const Cand& c1, int lane) {
+__device__ void gram2(Smem& s, const Cand& c0, const Cand& c1, int lane) {
     constexpr int kGroups = D / 32;
     const int h = lane >> 5, i = lane & 31;
     const int n = h ? c1.n : c0.n;
@@ -340,7 +294,7 @@ __device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane_
         const bkv_bf16* qn0 = a.q_new + (size_t)(b0 + bi0) * D;
         const bkv_bf16* qn1 = a.q_new + (size_t)(b0 + bi1) * D;
         const Cand A{buf0, c0, qn0, c0 + 1}, B{buf1, c1, qn1, two ? c1 + 1 : 0};
-        gram2_paced<D>(s, A, B, lane_r);
+        gram2<D>(s, A, B, lane_r);
         const uint64_t mask = fps2(s, A.n, B.n, m, lane_r);
         write_rows<D>(s, (uint32_t)mask, buf0, c0, qn0, lane_r);
         if (lane_r == 0) a.qcount[b0 + bi0] = m;
@@ -386,9 +340,7 @@ __device__ void merge_pair(const FpsArgs& a, int b, Smem& s, int lane) {
         }
     }
     if (!samples[0] && !samples[1]) return;
-    u32x4_t row[D / 8];
-    load_rows<D>(row, c[0], c[1], lane);
-    gram2<D>(s, row, lane);
+    gram2<D>(s, c[0], c[1], lane);
     const uint64_t mask = fps2(s, c[0].n, c[1].n, m, lane);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
