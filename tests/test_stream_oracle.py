@@ -127,3 +127,36 @@ def test_stream_on_a_sample_of_units(scfg):
         blind = replay(scfg, sub["k_new"], sub["v_new"], sub["q_new"], sub["pos"], max_ev=3, nthreads=2)
         assert not np.array_equal(blind["qbuf"], full["qbuf"][units])
 
+
+@pytest.mark.parametrize("scfg", (TINY_STREAM,) + TINY_STREAM_SPLITS, ids=lambda c: c.name)
+def test_fps_round_count_matches_the_oracle_cycle(scfg):
+    """The stream bench's count of sampling rounds per buffer equals the number of times the oracle's
+    cycle, stepped call by call, shrinks a buffer by FPS."""
+    from types import SimpleNamespace
+    from long_reasoning_decode_amd.stream import StreamRun
+    b = scfg.base
+    S = 300
+    x = _inputs(scfg, S)
+    st = empty_state(scfg, b.units)
+    oc = stream_ocfg(scfg)
+    ring0 = b.cap - b.n_recent_q
+    L, rounds = 0, 0
+    for s in range(S):
+        for u in range(b.units):
+            st["K"][u, L] = O.rope_row(x["k_new"][s, u], b.theta, int(x["pos"][s, u]))
+            st["V"][u, L] = x["v_new"][s, u]
+            if L < ring0:
+                before = int(st["qcount"][u, 0])
+                O.beacon_update(oc, st["qbuf"][u], st["qcount"][u], x["q_new"][s, u], buf0=u * b.G)
+                if u == 0 and int(st["qcount"][0, 0]) < before + 1:
+                    rounds += 1
+            else:
+                st["q_recent"][u, :, L - ring0] = x["q_new"][s, u]
+                st["pos_recent"][u, L - ring0] = x["pos"][s, u]
+        L += 1
+        if L == b.cap:
+            O.evict(oc, st["K"], st["V"], st["qbuf"], st["qcount"], st["q_recent"], st["pos_recent"],
+                    x["pos"][s].copy(), nthreads=2)
+            L = b.budget
+    assert StreamRun.fps_rounds_per_buffer(SimpleNamespace(base=b, scfg=scfg), S) == rounds
+
