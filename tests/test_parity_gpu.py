@@ -86,6 +86,32 @@ def test_fps_update_matches_oracle(d, fill):
         assert np.array_equal(g[b, :n], qbuf_h[b, :n]), b
 
 
+def test_fps_update_out_of_range_counts():
+    """Counts outside [0, B_Q^max - 1] are clamped on entry (negative ones read as 0, large ones as a full
+    buffer), as the oracle does."""
+    rng = np.random.default_rng(321)
+    cfg = TINY.scaled(d=128, n_layers=2, batch=3, hq=8, hkv=2)
+    nbuf, qcap, d = cfg.qbufs, cfg.qcap, cfg.d
+    X = _adversarial_buffers(nbuf, d, qcap, rng)
+    qb = torch.from_numpy(X).to(torch.bfloat16)
+    qn = torch.from_numpy(rng.standard_normal((nbuf, d)).astype(np.float32)).to(torch.bfloat16)
+    vals = np.array([-5, -1, 0, 30, 31, 32, 33, 100, 1 << 30, -(1 << 30)], np.int32)
+    qc = vals[np.arange(nbuf) % len(vals)].astype(np.int32)
+    qbuf_h = synth.to_u16(qb).copy()
+    qc_h = qc.copy()
+    sel_o = O.fps_update(qbuf_h, qc_h, synth.to_u16(qn), cfg.n_beacon, cfg.n_recent_q)
+    qbuf_d = qb.cuda()
+    qc_d = torch.from_numpy(qc).cuda()
+    sel_d = torch.full((nbuf, cfg.n_beacon), -7, dtype=torch.int32, device="cuda")
+    L.fps_update(L.shape_of(cfg), qbuf_d, qc_d, qn.cuda(), sel_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc_d.cpu().numpy(), qc_h)
+    assert np.array_equal(sel_d.cpu().numpy(), sel_o)
+    g = synth.to_u16(qbuf_d)
+    live = np.arange(qcap)[None, :, None] < qc_h[:, None, None]
+    assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
+
+
 @pytest.mark.parametrize("nb,nrq", [(32, 0), (0, 32), (31, 1), (1, 31), (4, 28), (28, 4)])
 def test_fps_update_splits(nb, nrq):
     """Every split of the 32-row buffer, the degenerate ones included: n_recent_q = 0 (a full buffer keeps
