@@ -284,7 +284,8 @@ def test_fps_merge_matches_oracle(qcount):
 @pytest.mark.parametrize("d,nb,batch", [(64, 16, 3), (128, 16, 1001), (128, 31, 333), (64, 4, 5)])
 def test_fps_merge_adversarial_odd_counts(d, nb, batch):
     """Merge over an odd number of buffers (the last wave has one), with adversarial contents and counts
-    from 0 to n_beacon, so pairs mix sampling and non-sampling buffers."""
+    from 0 to n_beacon (and some outside that range, clamped), so pairs mix sampling and non-sampling
+    buffers."""
     rng = np.random.default_rng(400 + d + nb + batch)
     cfg = TINY.scaled(d=d, n_layers=1, batch=batch, hq=3, hkv=1, n_beacon=nb, n_recent_q=32 - nb)
     nbuf, G = cfg.qbufs, cfg.G
@@ -295,6 +296,8 @@ def test_fps_merge_adversarial_odd_counts(d, nb, batch):
     qb = torch.from_numpy(X).to(torch.bfloat16)
     qr = torch.from_numpy(R).to(torch.bfloat16)
     qc = rng.integers(0, nb + 1, nbuf).astype(np.int32)
+    qc[::11] = -3                 # out of range: read as 0 beacons
+    qc[5::13] = nb + 7            # out of range: read as n_beacon beacons
     qbuf_h = synth.to_u16(qb).reshape(cfg.units, G, cfg.qcap, d).copy()
     qc_h = qc.reshape(cfg.units, G).copy()
     sel_o = O.merge(H.ocfg(cfg), qbuf_h, qc_h, synth.to_u16(qr).reshape(cfg.units, G, cfg.n_recent_q, d))
