@@ -19,7 +19,10 @@
 //           lane keeps an online (max, sum) of one row; the KS partials of a
 //           row are merged in LDS into c_r;
 //   pass 2: D[row][key] = Q K^T; max over the wave's rows of z - c per key,
-//           then over the heads with LDS atomics.
+//           then over the heads with LDS atomics.  It walks the stages last
+//           to first, so the keys it reads last are the first ones the
+//           compaction of the fused eviction kernel moves (more of them are
+//           still in the MALL then).
 // Mean pooling (Notes §2.1 Eq. 6, pooled over queries and heads as in the
 // Max/Mean ablation of Notes §3.3 Table 2) replaces pass 2's max by the sum of
 // exp2(z - c) over the wave's rows; the heads' partial sums of a stage go to
@@ -316,8 +319,10 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
         if (half == 0) part[wave * 32 + r] = float2{M, Ls};
     }
     lds_barrier();   // every wave is done with the ring and has published its partials
-    dma_stage<D>(Ku, 0, n_len, stage(0), wave, lane);
-    if (n_st > 1) dma_stage<D>(Ku, 1, n_len, stage(1), wave, lane);
+    // pass 2 takes the stages last to first (ring slots still in loop order)
+    auto rev = [&](int i) { return n_st - 1 - i; };
+    dma_stage<D>(Ku, rev(0), n_len, stage(0), wave, lane);
+    if (n_st > 1) dma_stage<D>(Ku, rev(1), n_len, stage(1), wave, lane);
     if (active && ks == 0 && half == 0) {
         float M = -__builtin_inff(), Ls = 0.0f;
 #pragma unroll
@@ -350,7 +355,7 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
     auto reduce_stage = [&](int rs) {
         if (wave != rs % kWaves) return;
         const float* ps = psum + (rs & 1) * (8 * kStageKeys);
-        const int key = rs * kStageKeys + lane;
+        const int key = rev(rs) * kStageKeys + lane;
         float sum = 0.0f;
         for (int h = 0; h < a.G; ++h) sum += ps[h * kStageKeys + lane];
         if (key < n_len) codes[key] = __float_as_uint(sum * inv_rows);
@@ -359,14 +364,14 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
         if (st + 1 < n_st) wait_vm<L::kDmaPerWave>();
         else wait_vm<0>();
         lds_barrier();
-        if (st + 2 < n_st) dma_stage<D>(Ku, st + 2, n_len, stage(st + 2), wave, lane);
+        if (st + 2 < n_st) dma_stage<D>(Ku, rev(st + 2), n_len, stage(st + 2), wave, lane);
         if constexpr (MEAN) {
             if (st > 0) reduce_stage(st - 1);
         }
         if (!active) continue;
 #pragma unroll
         for (int i = 0; i < kStageTiles; ++i) {
-            const int j = st * kStageTiles + i;
+            const int j = rev(st) * kStageTiles + i;
             if (j >= n_tiles || j % KS != ks) continue;
             const bkv_bf16* tl = stage(st) + i * (L::kTileBytes / 2);
             const int key = j * kTileKeys + r;
