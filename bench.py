@@ -200,6 +200,79 @@ def cpu_baseline(cfg, inp, target_s: float = 10.0) -> dict:
                       f"on {threads} threads; scaled to whole steps"}
 
 
+def _grow_sample(run_sample, n0: int, n_max: int, target_s: float):
+    """Calls run_sample(n) -> seconds with a growing sample size n until one call takes about target_s
+    (or n reaches n_max); returns the last (n, seconds)."""
+    n = min(n0, n_max)
+    while True:
+        dt = run_sample(n)
+        if dt >= target_s or n >= n_max:
+            return n, dt
+        n = min(n_max, max(n + n0, int(n * target_s / max(dt, 1e-3) * 1.05)))
+
+
+def _spread(n: int, total: int) -> np.ndarray:
+    """n distinct indices spread evenly over [0, total)."""
+    return np.unique(np.linspace(0, total - 1, n).round().astype(np.int64))
+
+
+def _in_threads(fn, n: int, threads: int) -> None:
+    """fn(lo, hi) over `threads` contiguous slices of range(n), concurrently (the oracle's C calls
+    release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    cuts = [n * i // threads for i in range(threads + 1)]
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda i: fn(cuts[i], cuts[i + 1]), [i for i in range(threads) if cuts[i] < cuts[i + 1]]))
+
+
+def stream_cpu_baseline(run, target_s: float = 10.0) -> dict:
+    """The CPU oracle (as it stands) replaying one eviction cycle of a bounded sample of units: from the
+    state the GPU stream holds right after an eviction, the next n_new decode steps, the last of which
+    evicts.  Scaled to tokens/s of the whole batch in that steady state."""
+    import oracle as O
+    b = run.base
+    if run.L != b.budget:                 # advance the GPU stream to the start of a cycle
+        run.run(b.cap - run.L)
+    n = b.n_new
+    blk = run.gen.block(n, run.pool)
+    U, G, d, cap = b.units, b.G, b.d, b.cap
+    dev = run.K.device
+    threads = O.default_threads()
+    K, V = run.K.reshape(U, cap, d), run.V.reshape(U, cap, d)
+    qbuf, qcount = run.qbuf.reshape(U, G, b.qcap, d), run.qcount.reshape(U, G)
+    q_recent = run.q_recent.reshape(U, G, b.n_recent_q, d)
+    k_new, v_new = blk["k_new"][:n].reshape(n, U, d), blk["v_new"][:n].reshape(n, U, d)
+    q_new = blk["q_new"][:n].reshape(n, U, G, d)
+    i32 = lambda t: np.ascontiguousarray(t.cpu().numpy().astype(np.int32))
+
+    def one(ns):
+        units = _spread(ns, U)
+        ut = torch.from_numpy(units).to(dev)
+        bt = (ut // b.hkv) % b.batch
+        st = [synth.to_u16(K.index_select(0, ut)), synth.to_u16(V.index_select(0, ut)),
+              synth.to_u16(qbuf.index_select(0, ut)), i32(qcount.index_select(0, ut)),
+              synth.to_u16(q_recent.index_select(0, ut)), i32(run.pos_recent.index_select(0, bt))]
+        ins = [synth.to_u16(k_new.index_select(1, ut)), synth.to_u16(v_new.index_select(1, ut)),
+               synth.to_u16(q_new.index_select(1, ut)), i32(blk["pos"][:n].index_select(1, bt))]
+        oc = O.OracleCfg(hq=b.hq, hkv=b.hkv, d=d, cap=cap, budget=b.budget, n_prefix=b.n_prefix,
+                         n_recent_kv=b.n_recent_kv, n_beacon=b.n_beacon, n_recent_q=b.n_recent_q, theta=b.theta,
+                         qcap=b.qcap, pool_mean=int(b.pool == "mean"),
+                         beacon_src={"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM}[b.beacon],
+                         seed=b.seed & 0xFFFFFFFF, n_layers=b.n_layers, batch=b.batch, unit_ids=units.tolist())
+        t0 = time.perf_counter()
+        o = O.stream(oc, *ins, st[0], st[1], b.budget, *st[2:], nthreads=threads)
+        dt = time.perf_counter() - t0
+        assert o["n_ev"] == 1 and o["L"] == b.budget, o
+        one.n = len(units)
+        return dt
+
+    _, dt = _grow_sample(one, 4 * threads, min(U, 4096), target_s)
+    ns = one.n
+    return {"value": b.batch * n / (dt * U / ns), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{ns} of {U} units, one eviction cycle ({n} decode steps, the last evicting) from the "
+                      f"GPU stream's state, {dt:.1f} s wall on {threads} threads; scaled to the whole batch"}
+
+
 def stream_bench(args) -> int:
     """Streaming decode: tokens/s of the eviction manager (library calls only; each block's inputs are
     drawn before its timed region) and its HBM footprint."""
@@ -240,6 +313,9 @@ def stream_bench(args) -> int:
     }
     if b.beacon == "fps" and b.n_recent_q > 0 and b.n_beacon > 0:
         out["fps_round"] = fps_round_bench(b, run.shape, run.qbuf, run.gen.block(1, run.pool)["q_new"][0])
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = stream_cpu_baseline(run, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -276,6 +352,33 @@ def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10) -> dict:
                          "frac": achieved / FP32_MFMA_PEAK_TFS, "flops_per_launch": flops}}
 
 
+def fps_round_cpu_baseline(b, q: dict, target_s: float = 10.0) -> dict:
+    """The CPU oracle's buffer update (as it stands) on a bounded sample of the same full buffers, each
+    sampling once; the oracle's call is one thread, run on slices of the sample in parallel."""
+    import oracle as O
+    threads = O.default_threads()
+    nb, n = b.qbufs, b.n_beacon + b.n_recent_q
+    qb, qn = q["qbuf"].reshape(nb, b.qcap, b.d), q["q_new"].reshape(nb, b.d)
+    dev = qb.device
+
+    def one(ns):
+        t = torch.from_numpy(_spread(ns, nb)).to(dev)
+        qbh, qnh = synth.to_u16(qb.index_select(0, t)), synth.to_u16(qn.index_select(0, t))
+        qc = np.full(len(t), n - 1, np.int32)
+        t0 = time.perf_counter()
+        _in_threads(lambda lo, hi: O.fps_update(qbh[lo:hi], qc[lo:hi], qnh[lo:hi], b.n_beacon, b.n_recent_q),
+                    len(t), threads)
+        dt = time.perf_counter() - t0
+        assert (qc == b.n_beacon).all()
+        one.n = len(t)
+        return dt
+
+    _, dt = _grow_sample(one, 64 * threads, nb, target_s)
+    return {"value": one.n / dt / nb, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "sample": f"{one.n} of {nb} buffers, one sampling round each, {dt:.1f} s wall on {threads} threads; "
+                      f"scaled to a round of every buffer"}
+
+
 def fps_round_main(args) -> int:
     """Only the FPS sampling round, on buffers of a stream workload's shape filled with its query mixture."""
     scfg = STREAM_CONFIGS[args.stream_config]
@@ -292,6 +395,9 @@ def fps_round_main(args) -> int:
                                   f"heads ({b.qbufs} buffers of {b.qcap} x {b.d}), {b.n_beacon} beacons + "
                                   f"{b.n_recent_q} recent queries"},
            **r}
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = fps_round_cpu_baseline(b, q, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -304,24 +410,29 @@ def prefill_flops_per_row(d: int, m: int) -> int:
 
 
 def prefill_cpu_baseline(cfg, q: torch.Tensor, target_s: float) -> dict:
-    """The CPU oracle's prefill sampling on a bounded sample of buffers."""
+    """The CPU oracle's prefill sampling (as it stands) on a bounded sample of buffers; the oracle's call is
+    one thread, run on slices of the sample in parallel."""
     import oracle as O
     b, P = cfg.base, cfg.n_prompt
+    threads = O.default_threads()
     qn = q.reshape(b.qbufs, P, b.d)
-    n, dt = 8, 0.0
-    while True:
-        x = synth.to_u16(qn[:n])
-        qbuf = np.zeros((n, b.qcap, b.d), np.uint16)
-        qc = np.zeros(n, np.int32)
+
+    def one(ns):
+        t = torch.from_numpy(_spread(ns, b.qbufs)).to(qn.device)
+        x = synth.to_u16(qn.index_select(0, t))
+        qbuf = np.zeros((len(t), b.qcap, b.d), np.uint16)
+        qc = np.zeros(len(t), np.int32)
         t0 = time.perf_counter()
-        O.prefill(x, qbuf, qc, b.n_beacon)
+        _in_threads(lambda lo, hi: O.prefill(x[lo:hi], qbuf[lo:hi], qc[lo:hi], b.n_beacon), len(t), threads)
         dt = time.perf_counter() - t0
-        if dt >= target_s or n >= b.qbufs:
-            break
-        n = min(b.qbufs, max(n + 8, int(n * target_s / max(dt, 1e-3) * 1.05)))
-    return {"value": n / dt / b.qbufs, "unit": "prefill initialisations/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} of {b.qbufs} buffers of the same workload, {dt:.1f} s on one thread; scaled to whole "
-                      f"initialisations"}
+        assert (qc == min(P, b.n_beacon)).all()
+        one.n = len(t)
+        return dt
+
+    _, dt = _grow_sample(one, threads, b.qbufs, target_s)
+    return {"value": one.n / dt / b.qbufs, "unit": "prefill initialisations/s", "cores": threads, "kind": "oracle",
+            "sample": f"{one.n} of {b.qbufs} buffers of the same workload, {dt:.1f} s wall on {threads} threads; "
+                      f"scaled to whole initialisations"}
 
 
 def prefill_bench(args) -> int:
@@ -371,6 +482,40 @@ def prefill_bench(args) -> int:
     return 0
 
 
+def decode_cpu_baseline(run, n_len: int, target_s: float = 10.0) -> dict:
+    """The CPU oracle's decode attention (as it stands) over n_len cached rows for one decode step, on a
+    bounded sample of units (at most about 2 GB of their keys and values); the oracle's call is one thread,
+    run on slices of the sample in parallel.  Scaled to tokens/s of the attention for the whole batch."""
+    import oracle as O
+    dc, b = run.dc, run.dc.base
+    threads = O.default_threads()
+    U, G, d = b.units, b.G, b.d
+    K, V = run.K.reshape(U, dc.cap, d)[:, :n_len], run.V.reshape(U, dc.cap, d)[:, :n_len]
+    blk = run.gen.block(1, run.pool)
+    q, pos = blk["q_new"][0].reshape(U, G, d), blk["pos"][0]
+    oc = O.OracleCfg(hq=b.hq, hkv=b.hkv, d=d, cap=n_len, budget=b.budget, n_prefix=b.n_prefix,
+                     n_recent_kv=b.n_recent_kv, n_beacon=b.n_beacon, n_recent_q=b.n_recent_q, theta=b.theta,
+                     qcap=b.qcap, n_layers=b.n_layers, batch=b.batch)
+
+    def one(ns):
+        ut = torch.from_numpy(_spread(ns, U)).to(K.device)
+        Kh, Vh = synth.to_u16(K.index_select(0, ut)), synth.to_u16(V.index_select(0, ut))
+        qh = synth.to_u16(q.index_select(0, ut))
+        ph = np.ascontiguousarray(pos.index_select(0, (ut // b.hkv) % b.batch).cpu().numpy().astype(np.int32))
+        t0 = time.perf_counter()
+        _in_threads(lambda lo, hi: O.decode_attention(oc, Kh[lo:hi], Vh[lo:hi], qh[lo:hi], ph[lo:hi], n_len),
+                    len(ut), threads)
+        dt = time.perf_counter() - t0
+        one.n = len(ut)
+        return dt
+
+    n_max = min(U, max(threads, int(2e9 // (n_len * d * 4))))
+    _, dt = _grow_sample(one, threads, n_max, target_s)
+    return {"value": b.batch / (dt * U / one.n), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"attention only: {one.n} of {U} units over {n_len} cached rows, one decode step, "
+                      f"{dt:.1f} s wall on {threads} threads; scaled to the whole batch"}
+
+
 def decode_bench(args) -> int:
     """The synthetic decode-attention loop: tokens/s of the attention side of decoding, full cache against
     BeaconKV (the framing of the pages' Table 4), and the attention kernel's HBM roofline."""
@@ -411,6 +556,9 @@ def decode_bench(args) -> int:
             "cache_bytes_peak": cache_bytes(dc, dc.cap),
             "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
         })
+        if not args.no_cpu_baseline:
+            print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+            lines[-1]["cpu_baseline"] = decode_cpu_baseline(run, int(round(rows)), args.cpu_seconds)
         print(json.dumps(lines[-1]), flush=True)
         del run
         torch.cuda.empty_cache()

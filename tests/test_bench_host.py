@@ -106,3 +106,71 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+# ---------------------------------------------------------------------------
+# The CPU-baseline legs of the stream, FPS-round and decode benches, on CPU tensors standing in for the GPU
+# state (the functions only read the state and draw inputs; the oracle does the timed work).
+
+class _State:
+    pass
+
+
+def _bf16(g, *shape):
+    import torch
+    return torch.randn(*shape, generator=g).to(torch.bfloat16)
+
+
+def test_stream_cpu_baseline_replays_one_cycle():
+    import torch
+    from long_reasoning_decode_amd import synth
+    from long_reasoning_decode_amd.configs import TINY_STREAM
+    b = TINY_STREAM.base
+    g = torch.Generator().manual_seed(5)
+    run = _State()
+    run.base, run.L = b, b.budget
+    run.K = _bf16(g, b.n_layers, b.batch, b.hkv, b.cap, b.d)
+    run.V = _bf16(g, b.n_layers, b.batch, b.hkv, b.cap, b.d)
+    run.qbuf = _bf16(g, b.n_layers, b.batch, b.hq, b.qcap, b.d)
+    run.qcount = torch.full((b.n_layers, b.batch, b.hq), b.n_beacon, dtype=torch.int32)
+    run.q_recent = _bf16(g, b.n_layers, b.batch, b.hq, b.n_recent_q, b.d)
+    run.pos_recent = torch.arange(b.batch * b.n_recent_q, dtype=torch.int32).reshape(b.batch, b.n_recent_q)
+    run.gen = synth.StreamGen(TINY_STREAM, "cpu")
+    run.pool = run.gen.alloc(b.n_new)
+    r = bench.stream_cpu_baseline(run, target_s=0.0)   # one sample; the function asserts one eviction
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert f"of {b.units} units" in r["sample"] and f"{b.n_new} decode steps" in r["sample"]
+
+
+def test_fps_round_cpu_baseline_samples_every_buffer_once():
+    from long_reasoning_decode_amd import synth
+    b = TINY.scaled(n_layers=2, batch=3)
+    q = synth.make_query_buffers(b, device="cpu")
+    r = bench.fps_round_cpu_baseline(b, q, target_s=0.0)
+    assert r["unit"] == "rounds/s" and r["value"] > 0 and f"of {b.qbufs} buffers" in r["sample"]
+
+
+def test_decode_cpu_baseline_on_a_sample():
+    import torch
+    from long_reasoning_decode_amd import synth
+    from long_reasoning_decode_amd.configs import StreamConfig
+    dc = decode.DecodeConfig("decode-tiny-full", replace(TINY, batch=2), "full", 40, gen_len=200)
+    b = dc.base
+    g = torch.Generator().manual_seed(6)
+    run = _State()
+    run.dc = dc
+    run.K = _bf16(g, b.n_layers, b.batch, b.hkv, dc.cap, b.d)
+    run.V = _bf16(g, b.n_layers, b.batch, b.hkv, dc.cap, b.d)
+    run.gen = synth.StreamGen(StreamConfig(name=dc.name, base=b, steps=dc.steps, drift_every=2048, p0_max=64), "cpu")
+    run.pool = run.gen.alloc(1)
+    r = bench.decode_cpu_baseline(run, dc.cap - 3, target_s=0.0)
+    assert r["unit"] == "tokens/s" and r["value"] > 0 and f"over {dc.cap - 3} cached rows" in r["sample"]
+
+
+def test_prefill_cpu_baseline_on_a_sample():
+    from long_reasoning_decode_amd import synth
+    from long_reasoning_decode_amd.configs import PrefillConfig
+    pc = PrefillConfig("prefill-tiny", TINY.scaled(n_layers=2, batch=2), 40)
+    q = synth.make_prompt_queries(pc.base, pc.n_prompt, device="cpu")
+    r = bench.prefill_cpu_baseline(pc, q, target_s=0.0)
+    assert r["unit"] == "prefill initialisations/s" and r["value"] > 0 and f"of {pc.base.qbufs} buffers" in r["sample"]
