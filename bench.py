@@ -273,6 +273,21 @@ def stream_cpu_baseline(run, target_s: float = 10.0) -> dict:
                       f"GPU stream's state, {dt:.1f} s wall on {threads} threads; scaled to the whole batch"}
 
 
+def stream_evict_roofline(run, evict_ms: float) -> dict:
+    """HBM roofline of the stream's evictions, its dominant cost: the algorithmic bytes of one steady-state
+    eviction (from one more, untimed cycle whose eviction reports its keep sets) over the timed run's mean
+    eviction time (bkv_evict: evict_kernel and the buffer merge)."""
+    b = run.base
+    if run.L != b.budget:                 # advance to the start of a cycle
+        run.run(b.cap - run.L)
+    run.run(b.n_new, keep_idx=True)
+    ab = alg_bytes(b, run.last_qcount.reshape(b.units, b.G).cpu().numpy(), run.idx.cpu().numpy(), b.cap)
+    ach = ab["total"] / (evict_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": "bkv_evict (evict_kernel + merge)", "achieved": ach, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None, "alg_bytes_per_launch": ab["total"],
+            "moved_rows_per_unit": ab["moved_rows"] / b.units}
+
+
 def stream_bench(args) -> int:
     """Streaming decode: tokens/s of the eviction manager (library calls only; each block's inputs are
     drawn before its timed region) and its HBM footprint."""
@@ -311,6 +326,8 @@ def stream_bench(args) -> int:
         "fps_rounds": {"per_buffer": rounds, "total": rounds * b.qbufs},
         "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
     }
+    if r["evict_ms"]:
+        out["roofline"] = stream_evict_roofline(run, out["eviction_ms"]["mean"])
     if b.beacon == "fps" and b.n_recent_q > 0 and b.n_beacon > 0:
         out["fps_round"] = fps_round_bench(b, run.shape, run.qbuf, run.gen.block(1, run.pool)["q_new"][0])
     if not args.no_cpu_baseline:

@@ -87,11 +87,12 @@ class StreamRun:
         r["pos"].append(blk["pos"][:n].index_select(1, self.rec_b))
 
     def run(self, steps: int | None = None, timed: bool = False, stream=None, progress=None,
-            detail_blocks=()) -> dict:
+            detail_blocks=(), keep_idx: bool = False) -> dict:
         """Run `steps` decode steps (default: the config's).  Returns the step count, evictions and,
         when timed, the summed GPU time of the library calls (generation excluded), each eviction's
         latency, and the latency of every decode step in the blocks listed in `detail_blocks` (block
-        indices counted from this call's first block)."""
+        indices counted from this call's first block).  keep_idx: every eviction also writes its keep
+        sets to self.idx, and the counts it started from go to self.last_qcount."""
         b = self.base
         steps = self.scfg.steps if steps is None else steps
         stream = torch.cuda.current_stream() if stream is None else stream
@@ -124,11 +125,14 @@ class StreamRun:
                     step_evs[-1].record(stream)
                 if self.L == b.cap:
                     rec = self.rec is not None
+                    if keep_idx:
+                        self.last_qcount = self.qcount.clone()
                     if timed:
                         evs.append((ev(), ev()))
                         evs[-1][0].record(stream)
                     lib.evict(self.shape, self.K, self.V, b.cap, self.qbuf, self.qcount, self.q_recent,
-                              self.pos_recent, blk["pos"][i], self.rope, idx_out=self.idx if rec else None,
+                              self.pos_recent, blk["pos"][i], self.rope,
+                              idx_out=self.idx if rec or keep_idx else None,
                               scores_out=self.scores if rec else None, stream=stream)
                     if timed:
                         evs[-1][1].record(stream)
