@@ -20,9 +20,10 @@
 //           row are merged in LDS into c_r;
 //   pass 2: D[row][key] = Q K^T; max over the wave's rows of z - c per key,
 //           then over the heads with LDS atomics.  It walks the stages last
-//           to first, so the keys it reads last are the first ones the
+//           to first: its first three stages are still in the ring from
+//           pass 1, and the keys it reads last are the first ones the
 //           compaction of the fused eviction kernel moves (more of them are
-//           still in the MALL then).
+//           still in the caches then).
 // Mean pooling (Notes §2.1 Eq. 6, pooled over queries and heads as in the
 // Max/Mean ablation of Notes §3.3 Table 2) replaces pass 2's max by the sum of
 // exp2(z - c) over the wave's rows; the heads' partial sums of a stage go to
@@ -319,10 +320,9 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
         if (half == 0) part[wave * 32 + r] = float2{M, Ls};
     }
     lds_barrier();   // every wave is done with the ring and has published its partials
-    // pass 2 takes the stages last to first (ring slots still in loop order)
+    // Pass 2 takes the stages last to first.  Stage i sits in ring slot i % kStages in both passes, so
+    // the last kStages stages of pass 1, its first ones, are still in the ring and need no load.
     auto rev = [&](int i) { return n_st - 1 - i; };
-    dma_stage<D>(Ku, rev(0), n_len, stage(0), wave, lane);
-    if (n_st > 1) dma_stage<D>(Ku, rev(1), n_len, stage(1), wave, lane);
     if (active && ks == 0 && half == 0) {
         float M = -__builtin_inff(), Ls = 0.0f;
 #pragma unroll
@@ -364,7 +364,7 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
         if (st + 1 < n_st) wait_vm<L::kDmaPerWave>();
         else wait_vm<0>();
         lds_barrier();
-        if (st + 2 < n_st) dma_stage<D>(Ku, rev(st + 2), n_len, stage(st + 2), wave, lane);
+        if (st + 2 < n_st && st + 2 >= kStages) dma_stage<D>(Ku, rev(st + 2), n_len, stage(rev(st + 2)), wave, lane);
         if constexpr (MEAN) {
             if (st > 0) reduce_stage(st - 1);
         }
@@ -373,7 +373,7 @@ __device__ void unit_codes(const ScoreArgs& a, int u, unsigned char* smem, uint3
         for (int i = 0; i < kStageTiles; ++i) {
             const int j = rev(st) * kStageTiles + i;
             if (j >= n_tiles || j % KS != ks) continue;
-            const bkv_bf16* tl = stage(st) + i * (L::kTileBytes / 2);
+            const bkv_bf16* tl = stage(rev(st)) + i * (L::kTileBytes / 2);
             const int key = j * kTileKeys + r;
             f32x16_t acc = f32x16_t{};
 #pragma unroll
