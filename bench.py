@@ -39,7 +39,8 @@ METRIC = "eviction steps/s (all layers x KV heads) at Qwen3-4B shape; % of HBM p
 # kernel -> the .hip file it is compiled from; its stored counters hold only while that file, everything it
 # includes and the build flags are unchanged
 KERNEL_SOURCE = {"evict_kernel": "bkv_evict.hip", "compact_kernel": "bkv_compact.hip", "score_kernel": "bkv_score.hip",
-                 "select_kernel": "bkv_select.hip", "fps_kernel": "bkv_fps.hip"}
+                 "select_kernel": "bkv_select.hip", "fps_kernel": "bkv_fps.hip", "attn_kernel": "bkv_attention.hip",
+                 "append_kernel": "bkv_stream.hip"}
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_qwen3-4b.txt")
 
 
@@ -62,12 +63,12 @@ def kernel_sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def stored_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None when there is
+def stored_traffic(kernel: str, path: str = TRAFFIC_FILE):
+    """HBM bytes per launch of `kernel` from a committed counter summary, or None when there is
     none or the kernel's sources changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if line.startswith("#"):
             continue
         f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
@@ -568,7 +569,9 @@ def decode_bench(args) -> int:
                        "mode": dc.mode, "mean_rows": rows, "expected_mean_rows": mean_rows(dc),
                        "evictions": r["evictions"]},
             "roofline": {"bound": "hbm", "kernel": "attn_kernel", "achieved": ach, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                         "traffic": stored_traffic("attn_kernel", os.path.join(HERE, "profiles",
+                                                                               f"hbm_traffic_{dc.name}.txt")),
                          "alg_bytes_per_launch": att_bytes, "attention_ms": att_ms},
             "cache_bytes_peak": cache_bytes(dc, dc.cap),
             "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
@@ -579,6 +582,13 @@ def decode_bench(args) -> int:
         print(json.dumps(lines[-1]), flush=True)
         del run
         torch.cuda.empty_cache()
+    if args.copy_calibration_mib > 0:   # a copy of known size for counter passes (see the eviction bench)
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     return 0
 
 
