@@ -330,7 +330,8 @@ def stream_bench(args) -> int:
     if r["evict_ms"]:
         out["roofline"] = stream_evict_roofline(run, out["eviction_ms"]["mean"])
     if b.beacon == "fps" and b.n_recent_q > 0 and b.n_beacon > 0:
-        out["fps_round"] = fps_round_bench(b, run.shape, run.qbuf, run.gen.block(1, run.pool)["q_new"][0])
+        out["fps_round"] = fps_round_bench(b, run.shape, run.qbuf, run.gen.block(1, run.pool)["q_new"][0],
+                                           name=scfg.name)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = stream_cpu_baseline(run, args.cpu_seconds)
@@ -341,7 +342,7 @@ def stream_bench(args) -> int:
 FP32_MFMA_PEAK_TFS = 157.3   # MI355X dense fp32 matrix rate
 
 
-def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10) -> dict:
+def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10, name: str = "") -> dict:
     """One sampling round of every buffer: bkv_fps_update with every count at B_Q^max - 1, on a copy of
     the given buffers, timed alone with HIP events (the counts are reset between the timed calls).
     Roofline: the Gram matrices are the matrix-core work, 2 n^2 d flops per buffer (all n^2 dot products,
@@ -367,7 +368,10 @@ def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10) -> dict:
     return {"buffers": b.qbufs, "rows": n, "ms": t, "ms_min": float(min(ms)),
             "roofline": {"bound": "mfma", "kernel": "fps_kernel (update, every buffer sampling)",
                          "achieved": achieved, "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": achieved / FP32_MFMA_PEAK_TFS, "flops_per_launch": flops}}
+                         "frac": achieved / FP32_MFMA_PEAK_TFS, "flops_per_launch": flops,
+                         "traffic": stored_traffic("fps_kernel", os.path.join(HERE, "profiles",
+                                                                              f"hbm_traffic_fps-round-{name}.txt"))
+                         if name else None}}
 
 
 def fps_round_cpu_baseline(b, q: dict, target_s: float = 10.0) -> dict:
@@ -405,7 +409,7 @@ def fps_round_main(args) -> int:
     L.load()
     print(f"# fps round {scfg.name}: {b.qbufs} buffers", file=sys.stderr, flush=True)
     q = synth.make_query_buffers(b, device="cuda")
-    r = fps_round_bench(b, L.shape_of(b), q["qbuf"], q["q_new"], reps=args.steps)
+    r = fps_round_bench(b, L.shape_of(b), q["qbuf"], q["q_new"], reps=args.steps, name=scfg.name)
     out = {"metric": "FPS sampling round of every query buffer (bkv_fps_update, every buffer full)",
            "value": 1000.0 / r["ms"], "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
            "higher_is_better": True, "dtype": "f32 (bf16 rows)", "data": "synthetic",
@@ -413,6 +417,13 @@ def fps_round_main(args) -> int:
                                   f"heads ({b.qbufs} buffers of {b.qcap} x {b.d}), {b.n_beacon} beacons + "
                                   f"{b.n_recent_q} recent queries"},
            **r}
+    if args.copy_calibration_mib > 0:   # a copy of known size for counter passes (see the eviction bench)
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = fps_round_cpu_baseline(b, q, args.cpu_seconds)
