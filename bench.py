@@ -63,9 +63,10 @@ def kernel_sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def stored_traffic(kernel: str, path: str = TRAFFIC_FILE):
-    """HBM bytes per launch of `kernel` from a committed counter summary, or None when there is
-    none or the kernel's sources changed since the counters were taken."""
+def stored_traffic(kernel: str, path: str | None = None):
+    """HBM bytes per launch of `kernel` from a committed counter summary (default: the eviction step's),
+    or None when there is none or the kernel's sources changed since the counters were taken."""
+    path = TRAFFIC_FILE if path is None else path
     if not os.path.exists(path):
         return None
     for line in open(path):

@@ -86,6 +86,8 @@ def test_stored_traffic_lookup(tmp_path, monkeypatch):
     assert bench.stored_traffic("evict_kernel") == 1.5e10
     assert bench.stored_traffic("score_kernel") is None      # sources changed since
     assert bench.stored_traffic("select_kernel") is None     # never measured
+    assert bench.stored_traffic("evict_kernel", str(tmp_path / "none.txt")) is None
+    assert bench.stored_traffic("evict_kernel", str(f)) == 1.5e10
 
 
 @pytest.mark.parametrize("dc", list(decode.DECODE_CONFIGS.values()), ids=lambda c: c.name)
