@@ -203,13 +203,13 @@ def cpu_baseline(cfg, inp, target_s: float = 10.0) -> dict:
 
 
 def _grow_sample(run_sample, n0: int, n_max: int, target_s: float):
-    """Calls run_sample(n) -> seconds with a growing sample size n until one call takes about target_s
-    (or n reaches n_max); returns the last (n, seconds)."""
+    """Calls run_sample(n) -> (items sampled, seconds) with a growing sample size n until one call takes
+    about target_s (or n reaches n_max); returns the last call's (items, seconds)."""
     n = min(n0, n_max)
     while True:
-        dt = run_sample(n)
+        got, dt = run_sample(n)
         if dt >= target_s or n >= n_max:
-            return n, dt
+            return got, dt
         n = min(n_max, max(n + n0, int(n * target_s / max(dt, 1e-3) * 1.05)))
 
 
@@ -265,11 +265,9 @@ def stream_cpu_baseline(run, target_s: float = 10.0) -> dict:
         o = O.stream(oc, *ins, st[0], st[1], b.budget, *st[2:], nthreads=threads)
         dt = time.perf_counter() - t0
         assert o["n_ev"] == 1 and o["L"] == b.budget, o
-        one.n = len(units)
-        return dt
+        return len(units), dt
 
-    _, dt = _grow_sample(one, 4 * threads, min(U, 4096), target_s)
-    ns = one.n
+    ns, dt = _grow_sample(one, 4 * threads, min(U, 4096), target_s)
     return {"value": b.batch * n / (dt * U / ns), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{ns} of {U} units, one eviction cycle ({n} decode steps, the last evicting) from the "
                       f"GPU stream's state, {dt:.1f} s wall on {threads} threads; scaled to the whole batch"}
@@ -393,12 +391,11 @@ def fps_round_cpu_baseline(b, q: dict, target_s: float = 10.0) -> dict:
                     len(t), threads)
         dt = time.perf_counter() - t0
         assert (qc == b.n_beacon).all()
-        one.n = len(t)
-        return dt
+        return len(t), dt
 
-    _, dt = _grow_sample(one, 64 * threads, nb, target_s)
-    return {"value": one.n / dt / nb, "unit": "rounds/s", "cores": threads, "kind": "oracle",
-            "sample": f"{one.n} of {nb} buffers, one sampling round each, {dt:.1f} s wall on {threads} threads; "
+    ns, dt = _grow_sample(one, 64 * threads, nb, target_s)
+    return {"value": ns / dt / nb, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "sample": f"{ns} of {nb} buffers, one sampling round each, {dt:.1f} s wall on {threads} threads; "
                       f"scaled to a round of every buffer"}
 
 
@@ -456,12 +453,11 @@ def prefill_cpu_baseline(cfg, q: torch.Tensor, target_s: float) -> dict:
         _in_threads(lambda lo, hi: O.prefill(x[lo:hi], qbuf[lo:hi], qc[lo:hi], b.n_beacon), len(t), threads)
         dt = time.perf_counter() - t0
         assert (qc == min(P, b.n_beacon)).all()
-        one.n = len(t)
-        return dt
+        return len(t), dt
 
-    _, dt = _grow_sample(one, threads, b.qbufs, target_s)
-    return {"value": one.n / dt / b.qbufs, "unit": "prefill initialisations/s", "cores": threads, "kind": "oracle",
-            "sample": f"{one.n} of {b.qbufs} buffers of the same workload, {dt:.1f} s wall on {threads} threads; "
+    ns, dt = _grow_sample(one, threads, b.qbufs, target_s)
+    return {"value": ns / dt / b.qbufs, "unit": "prefill initialisations/s", "cores": threads, "kind": "oracle",
+            "sample": f"{ns} of {b.qbufs} buffers of the same workload, {dt:.1f} s wall on {threads} threads; "
                       f"scaled to whole initialisations"}
 
 
@@ -536,13 +532,12 @@ def decode_cpu_baseline(run, n_len: int, target_s: float = 10.0) -> dict:
         _in_threads(lambda lo, hi: O.decode_attention(oc, Kh[lo:hi], Vh[lo:hi], qh[lo:hi], ph[lo:hi], n_len),
                     len(ut), threads)
         dt = time.perf_counter() - t0
-        one.n = len(ut)
-        return dt
+        return len(ut), dt
 
     n_max = min(U, max(threads, int(2e9 // (n_len * d * 4))))
-    _, dt = _grow_sample(one, threads, n_max, target_s)
-    return {"value": b.batch / (dt * U / one.n), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"attention only: {one.n} of {U} units over {n_len} cached rows, one decode step, "
+    ns, dt = _grow_sample(one, threads, n_max, target_s)
+    return {"value": b.batch / (dt * U / ns), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"attention only: {ns} of {U} units over {n_len} cached rows, one decode step, "
                       f"{dt:.1f} s wall on {threads} threads; scaled to the whole batch"}
 
 
