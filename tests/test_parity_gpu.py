@@ -375,7 +375,9 @@ def test_score_matches_oracle(cfg, n_len, flags):
 
 @pytest.mark.parametrize("n_len,budget,npf,nr", [(2176, 2048, 4, 16), (160, 128, 8, 16), (1000, 1000, 4, 16),
                                                   (4224, 4096, 4, 16), (33, 20, 0, 0), (8192, 100, 50, 50),
-                                                  (300, 20, 4, 16)])
+                                                  (300, 20, 4, 16),
+                                                  (2049, 2048, 4, 16),     # exactly one row evicted
+                                                  (100, 150, 4, 16)])      # budget above n_len: -1 padding
 def test_select_matches_oracle(n_len, budget, npf, nr):
     rng = np.random.default_rng(n_len + budget)
     U = 24
@@ -444,6 +446,8 @@ EVICT_CASES = [
     (TINY, None, 1),
     (TINY, 159, 1),
     (TINY, 128, 1),                 # nothing to evict
+    (TINY, 129, 1),                 # exactly one row evicted
+    (QWEN3_4B.scaled(n_layers=1, batch=2), 2049, 1),
     (TINY, 150, 0),
     (QWEN3_4B.scaled(n_layers=2, batch=2), None, 1),
     (R1_QWEN_7B.scaled(n_layers=1, batch=2), None, 1),
