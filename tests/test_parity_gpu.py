@@ -112,10 +112,12 @@ def test_fps_update_out_of_range_counts():
     assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
 
 
-@pytest.mark.parametrize("nb,nrq", [(32, 0), (0, 32), (31, 1), (1, 31), (4, 28), (28, 4)])
+@pytest.mark.parametrize("nb,nrq", [(32, 0), (0, 32), (31, 1), (1, 31), (4, 28), (28, 4),
+                                    (1, 0), (2, 3), (8, 8), (15, 2)])
 def test_fps_update_splits(nb, nrq):
     """Every split of the 32-row buffer, the degenerate ones included: n_recent_q = 0 (a full buffer keeps
-    all its rows) and n_beacon = 0 (a full buffer keeps none)."""
+    all its rows) and n_beacon = 0 (a full buffer keeps none); and buffers whose B_Q^max is below 32, down
+    to a single row."""
     rng = np.random.default_rng(500 + nb)
     cfg = TINY.scaled(d=128, n_layers=3, batch=5, hq=8, hkv=2, n_beacon=nb, n_recent_q=nrq)
     nbuf, qcap, d = cfg.qbufs, cfg.qcap, cfg.d
@@ -334,6 +336,7 @@ SCORE_CASES = [
     (TINY.scaled(n_beacon=0, name="nb0"), 160, 1),
     (TINY.scaled(d=128, budget=8064, n_new=128, n_prefix=4, name="n8192"), 8192, 1),
     (TINY, 10, 1),                  # fewer keys than recent queries: recent rows 0-5 see nothing
+    (TINY, 1, 1),                   # a single key: only the beacons and the last recent row see it
     # mean pooling (flags 3: causal + mean, 2: mean alone) on every workgroup layout
     (TINY, None, 3),
     (TINY, 10, 3),
