@@ -283,13 +283,14 @@ def test_fps_merge_matches_oracle(qcount):
             assert np.array_equal(g[u, h, :n], v["qbuf"][u, h, :n])
 
 
-@pytest.mark.parametrize("d,nb,batch", [(64, 16, 3), (128, 16, 1001), (128, 31, 333), (64, 4, 5)])
-def test_fps_merge_adversarial_odd_counts(d, nb, batch):
+@pytest.mark.parametrize("d,nb,batch,nrq", [(64, 16, 3, 16), (128, 16, 1001, 16), (128, 31, 333, 1),
+                                             (64, 4, 5, 28), (128, 2, 7, 3), (128, 8, 9, 8), (64, 1, 3, 1)])
+def test_fps_merge_adversarial_odd_counts(d, nb, batch, nrq):
     """Merge over an odd number of buffers (the last wave has one), with adversarial contents and counts
     from 0 to n_beacon (and some outside that range, clamped), so pairs mix sampling and non-sampling
-    buffers."""
+    buffers; B_Q^max = 32 and smaller."""
     rng = np.random.default_rng(400 + d + nb + batch)
-    cfg = TINY.scaled(d=d, n_layers=1, batch=batch, hq=3, hkv=1, n_beacon=nb, n_recent_q=32 - nb)
+    cfg = TINY.scaled(d=d, n_layers=1, batch=batch, hq=3, hkv=1, n_beacon=nb, n_recent_q=nrq)
     nbuf, G = cfg.qbufs, cfg.G
     assert nbuf % 2 == 1
     X = _adversarial_buffers(nbuf, d, cfg.qcap, rng)
