@@ -55,7 +55,7 @@ def _check(cfg, q: torch.Tensor, P: int, bufs=None, where=""):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("P", [0, 5, 16, 17, 100, 511, 512, 513, 1024, 1025, 1500, 2049, 4100])
+@pytest.mark.parametrize("P", [0, 1, 2, 5, 16, 17, 100, 511, 512, 513, 1024, 1025, 1500, 2049, 4100])
 def test_prefill_matches_oracle(d, P):
     cfg = SMALL.scaled(d=d)
     _flush(f"prefill d={d} P={P}")
