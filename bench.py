@@ -180,22 +180,21 @@ def copy_reference(stream, nbytes: int = 1 << 30, reps: int = 5) -> dict:
 
 
 def cpu_baseline(cfg, inp, target_s: float = 10.0) -> dict:
-    """The CPU oracle (as it stands) on a bounded sample of units."""
+    """The CPU oracle (as it stands) on a bounded sample of units, spread over the workload."""
     import oracle as O
     threads = O.default_threads()
     oc = O.OracleCfg(hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, cap=cfg.n_len, budget=cfg.budget, n_prefix=cfg.n_prefix,
                      n_recent_kv=cfg.n_recent_kv, n_beacon=cfg.n_beacon, n_recent_q=cfg.n_recent_q,
                      theta=cfg.theta, qcap=cfg.qcap, pool_mean=int(cfg.pool == "mean"))
-    n = max(threads, 8)
-    while True:
-        v = synth.oracle_views(cfg, inp, list(range(n)))
+
+    def one(ns):
+        v = synth.oracle_views(cfg, inp, _spread(ns, cfg.units).tolist())
         t0 = time.perf_counter()
         O.evict(oc, v["K"], v["V"], v["qbuf"], v["qcount"], v["q_recent"], v["pos_recent"], v["t"],
                 nthreads=threads)
-        dt = time.perf_counter() - t0
-        if dt >= target_s or n >= cfg.units:
-            break
-        n = min(cfg.units, max(n + threads, int(n * target_s / max(dt, 1e-3) * 1.05)))
+        return len(v["units"]), time.perf_counter() - t0
+
+    n, dt = _grow_sample(one, max(threads, 8), cfg.units, target_s)
     units_per_s = n / dt
     return {"value": units_per_s / cfg.units, "unit": "eviction steps/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {cfg.units} units of the same workload, one eviction each, {dt:.1f} s wall "

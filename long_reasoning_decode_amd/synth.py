@@ -268,6 +268,9 @@ def oracle_views(cfg: EvictConfig, inp: dict, units=None) -> dict:
     G = cfg.G
     U = L * B * Hkv
     units = list(range(U)) if units is None else list(units)
+    bad = [u for u in units if not 0 <= u < U]
+    if bad:   # checked here, before any device gather reads with them
+        raise IndexError(f"unit indices outside [0, {U}): {bad[:5]}")
     ut = torch.tensor(units, dtype=torch.long, device=inp["K"].device)
     K = inp["K"].reshape(U, -1, d).index_select(0, ut)
     V = inp["V"].reshape(U, -1, d).index_select(0, ut)

@@ -176,3 +176,13 @@ def test_prefill_cpu_baseline_on_a_sample():
     q = synth.make_prompt_queries(pc.base, pc.n_prompt, device="cpu")
     r = bench.prefill_cpu_baseline(pc, q, target_s=0.0)
     assert r["unit"] == "prefill initialisations/s" and r["value"] > 0 and f"of {pc.base.qbufs} buffers" in r["sample"]
+
+
+def test_eviction_cpu_baseline_sample_stays_within_the_units():
+    """A workload with fewer units than host threads: the sample is every unit, never an index past them."""
+    from long_reasoning_decode_amd import synth
+    inp = synth.make_evict_inputs(TINY, device="cpu")
+    r = bench.cpu_baseline(TINY, inp, target_s=0.0)
+    assert r["value"] > 0 and f"{TINY.units} of {TINY.units} units" in r["sample"]
+    with pytest.raises(IndexError):
+        synth.oracle_views(TINY, inp, [0, TINY.units])
