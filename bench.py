@@ -3,10 +3,14 @@
 One step = one bkv_evict call over every (layer, batch, KV head) unit of the
 Qwen3-4B-shaped cache: 36 layers x batch 16 x 8 KV heads = 4608 units, cache
 length 2176 -> budget 2048, head_dim 128, 32 query heads (G = 4), 16 beacons
-+ 16 recent queries per query head.  Steps run back to back, in place, on one
-stream: each step evicts 128 rows from the cache the previous step left
-(its rows [budget, n_len) still hold the earlier tail rows), so every step
-does a full eviction's work.
++ 16 recent queries per query head.  Two timings, both reported:
+  * pristine (the default for `value`): before each step, outside its timed
+    region, the original cache and buffers are restored from device copies and
+    a 512 MB scratch buffer is touched to flush the MALL; each step is timed on
+    its own between two synchronisations;
+  * back-to-back: the steps run in place on one stream, each evicting 128 rows
+    from the cache the previous step left (rows [budget, n_len) still hold the
+    earlier tail rows), so every step does a full eviction's work.
 
 Prints one JSON line (see the keys below); `value` is eviction steps/s with
 all inputs resident in HBM.  `roofline` is for the dominant kernel (the fused
@@ -44,8 +48,14 @@ KERNEL_SOURCE = {"evict_kernel": "bkv_evict.hip", "compact_kernel": "bkv_compact
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic_qwen3-4b.txt")
 
 
+def traffic_file(config: str) -> str:
+    """The counter summary of an eviction workload (the headline one is TRAFFIC_FILE)."""
+    return TRAFFIC_FILE if config == QWEN3_4B.name else os.path.join(HERE, "profiles", f"hbm_traffic_{config}.txt")
+
+
 def kernel_sources_sha256(kernel: str) -> str:
-    """sha256 over the kernel's .hip file, the local headers it includes (transitively) and build.py."""
+    """sha256 over the kernel's .hip file, the local headers it includes (transitively) and the compile
+    flags."""
     import hashlib
     import re
     dirs = [os.path.join(HERE, "long_reasoning_decode_amd", "csrc"), os.path.join(HERE, "include")]
@@ -59,7 +69,8 @@ def kernel_sources_sha256(kernel: str) -> str:
         text = open(path, "rb").read()
         h.update(f.encode() + b"\0" + text)
         todo += re.findall(r'#include "([^"]+)"', text.decode())
-    h.update(open(os.path.join(HERE, "long_reasoning_decode_amd", "build.py"), "rb").read())
+    from long_reasoning_decode_amd import build as lib_build
+    h.update(" ".join(lib_build.device_flags()).encode())
     return h.hexdigest()
 
 
@@ -127,7 +138,12 @@ def summarize_counters(fetch_dir: str, write_dir: str, calib_bytes: int) -> str:
 def alg_bytes(cfg, qcount: np.ndarray, idx: np.ndarray, n_len: int) -> dict:
     """Algorithmic bytes of one eviction: K read once for scoring, the
     observation rows read, moved K and V rows read and written, the new
-    buffers written.  qcount [units, G] before the call; idx [units, budget]."""
+    buffers written.  qcount [units, G] before the call; idx [units, budget].
+
+    The gather K^ = K[:, I_final, :] (Notes §2.3 Eq. 8) reads the moved key rows
+    that the scoring has already read; "strict" counts them once (a moved key row
+    is written, a moved value row read and written), the lower bound of any
+    implementation that reads every key at most once."""
     d2 = cfg.d * 2
     B = min(cfg.budget, n_len)
     moved = (idx[:, :B] != np.arange(B)[None, :]).sum(axis=1).astype(np.int64)
@@ -136,8 +152,9 @@ def alg_bytes(cfg, qcount: np.ndarray, idx: np.ndarray, n_len: int) -> dict:
     q_read = int(rows.sum()) * d2
     compact = int(4 * moved.sum()) * d2
     buf = cfg.qbufs * cfg.n_beacon * d2
+    strict = k_read + q_read + int(3 * moved.sum()) * d2 + buf
     return {"k_read": k_read, "q_read": q_read, "compact": compact, "buffers": buf,
-            "total": k_read + q_read + compact + buf, "moved_rows": int(moved.sum())}
+            "total": k_read + q_read + compact + buf, "total_strict": strict, "moved_rows": int(moved.sum())}
 
 
 BF16_MFMA_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix rate
@@ -258,10 +275,15 @@ def stream_cpu_baseline(run, target_s: float = 10.0) -> dict:
         oc = O.OracleCfg(hq=b.hq, hkv=b.hkv, d=d, cap=cap, budget=b.budget, n_prefix=b.n_prefix,
                          n_recent_kv=b.n_recent_kv, n_beacon=b.n_beacon, n_recent_q=b.n_recent_q, theta=b.theta,
                          qcap=b.qcap, pool_mean=int(b.pool == "mean"),
-                         beacon_src={"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM}[b.beacon],
+                         beacon_src={"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM,
+                                     "naive": O.SRC_NAIVE}[b.beacon],
                          seed=b.seed & 0xFFFFFFFF, n_layers=b.n_layers, batch=b.batch, unit_ids=units.tolist())
+        hist = {}
+        if getattr(run, "naive", False):   # the sampled units' query histories
+            hist = {"hist": synth.to_u16(run.hist.reshape(U, G, run.hcap, d).index_select(0, ut)),
+                    "hcount": i32(run.hcount.reshape(U, G).index_select(0, ut))}
         t0 = time.perf_counter()
-        o = O.stream(oc, *ins, st[0], st[1], b.budget, *st[2:], nthreads=threads)
+        o = O.stream(oc, *ins, st[0], st[1], b.budget, *st[2:], nthreads=threads, **hist)
         dt = time.perf_counter() - t0
         assert o["n_ev"] == 1 and o["L"] == b.budget, o
         return len(units), dt
@@ -324,6 +346,7 @@ def stream_bench(args) -> int:
                            "max": max(r["step_ms"]) * 1e3},
         "fps_rounds": {"per_buffer": rounds, "total": rounds * b.qbufs},
         "state_bytes": run.state_bytes(), "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
+        "beacon_state_bytes": run.beacon_state_bytes(),
     }
     if r["evict_ms"]:
         out["roofline"] = stream_evict_roofline(run, out["eviction_ms"]["mean"])
@@ -604,6 +627,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=QWEN3_4B.name, choices=sorted(EVICT_CONFIGS))
+    ap.add_argument("--timing", default="pristine", choices=["pristine", "back-to-back"],
+                    help="which timing gives value and roofline: pristine (each step on the original cache, the "
+                         "MALL flushed before it) or back-to-back (steps in place on the cache the previous one "
+                         "left); both are measured and reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -666,10 +693,11 @@ def main() -> int:
         L.evict(shape, K, V, N, qbuf, qcount, inp["q_recent"], inp["pos_recent"], inp["t"], rope,
                 idx_out=idx_steps[i], stream=stream)
 
+    # back to back: the steps run in place, each on the cache the previous one left
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"# timing {args.steps} steps back to back", file=sys.stderr, flush=True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -677,12 +705,47 @@ def main() -> int:
         step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    wall_b2b = time.perf_counter() - t0
+    ms_b2b = ev0.elapsed_time(ev1) / args.steps
+    qc0 = np.full((cfg.units, cfg.G), cfg.n_beacon, np.int64)   # qcount is n_beacon before every step
+    ab_b2b = [alg_bytes(cfg, qc0, idx_steps[i].cpu().numpy(), N) for i in range(args.warmup, total_steps)]
 
-    # algorithmic bytes of the timed steps (qcount is n_beacon before every step)
-    qc0 = np.full((cfg.units, cfg.G), cfg.n_beacon, np.int64)
-    ab = [alg_bytes(cfg, qc0, idx_steps[i].cpu().numpy(), N) for i in range(args.warmup, total_steps)]
+    # pristine: before each step (untimed) the original cache and buffers are restored from their device
+    # copies and a 512 MB scratch buffer is read, which evicts the keys from the 256 MB MALL and leaves it
+    # holding clean lines (no write-back of the restore's writes falls into the timed step); each step is
+    # timed alone, between two synchronisations
+    print(f"# timing {args.steps} pristine steps", file=sys.stderr, flush=True)
+    scratch = torch.ones(512 << 18, dtype=torch.int32, device="cuda")
+    flush_sum = torch.zeros((), dtype=torch.int64, device="cuda")
+    ms_pr = []
+    t_pr = 0.0
+    for i in range(total_steps):
+        K.copy_(inp["K"])
+        V.copy_(inp["V"])
+        qbuf.copy_(inp["qbuf"])
+        qcount.copy_(inp["qcount"])
+        flush_sum.copy_(scratch.sum(dtype=torch.int64))   # reads all 512 MB
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t1 = time.perf_counter()
+        torch.cuda._sleep(1 << 20)   # the GPU waits here while the host enqueues the step, so no gap is timed
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            t_pr += time.perf_counter() - t1
+            ms_pr.append(e0.elapsed_time(e1))
+    assert int(flush_sum) == scratch.numel()
+    del scratch
+    ab_pr = alg_bytes(cfg, inp["qcount"].reshape(cfg.units, cfg.G).cpu().numpy(),
+                      idx_steps[total_steps - 1].cpu().numpy(), N)
+    ms_pristine = float(np.mean(ms_pr))
+
+    pristine = args.timing == "pristine"
+    ms_step = ms_pristine if pristine else ms_b2b
+    wall = t_pr if pristine else wall_b2b
+    ab = [ab_pr] if pristine else ab_b2b
     step_bytes = float(np.mean([a["total"] for a in ab]))
     compact_bytes = float(np.mean([a["compact"] for a in ab]))
 
@@ -698,8 +761,11 @@ def main() -> int:
     torch.cuda.synchronize()
     merge_ms = m0.elapsed_time(m1) / args.steps
     kern_ms = {"evict_kernel": ms_step - merge_ms, "fps_merge": merge_ms}
-    evict_bytes = step_bytes - float(np.mean([x["buffers"] for x in ab]))
+    buf_bytes = float(np.mean([x["buffers"] for x in ab]))
+    evict_bytes = step_bytes - buf_bytes
     evict_ach = evict_bytes / (kern_ms["evict_kernel"] * 1e-3) / 1e9
+    strict_bytes = float(np.mean([a["total_strict"] for a in ab])) - buf_bytes
+    strict_ach = strict_bytes / (kern_ms["evict_kernel"] * 1e-3) / 1e9
     idx_b = torch.empty((cfg.units, cfg.budget), dtype=torch.int32, device="cuda")
 
     # the separate entry points, for reference
@@ -739,11 +805,25 @@ def main() -> int:
                                f"{cfg.n_recent_kv}, {cfg.n_beacon} beacons + {cfg.n_recent_q} recent queries",
                    "units": cfg.units, "n_len": N, "budget": cfg.budget},
         "roofline": {"bound": "hbm", "kernel": "evict_kernel", "achieved": evict_ach, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": evict_ach / HBM_PEAK_GBS, "traffic": stored_traffic("evict_kernel"),
-                     "alg_bytes_per_launch": evict_bytes},
+                     "unit": "GB/s", "frac": evict_ach / HBM_PEAK_GBS,
+                     "traffic": stored_traffic("evict_kernel", traffic_file(cfg.name)),
+                     "alg_bytes_per_launch": evict_bytes,
+                     "strict": {"alg_bytes_per_launch": strict_bytes, "achieved": strict_ach,
+                                "frac": strict_ach / HBM_PEAK_GBS,
+                                "counts": "every key read once: moved key rows written, moved value rows read "
+                                          "and written"}},
         "step_hbm": {"alg_bytes": step_bytes, "achieved_GBs": step_bytes / (ms_step * 1e-3) / 1e9,
                      "frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "compact_alg_bytes": compact_bytes},
+                     "compact_alg_bytes": compact_bytes,
+                     "strict_frac": (strict_bytes + buf_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "timing": args.timing,
+        "pristine": {"ms_mean": ms_pristine, "ms_median": float(np.median(ms_pr)), "ms_min": float(min(ms_pr)),
+                     "steps_per_s": 1000.0 / ms_pristine, "moved_rows_per_unit": ab_pr["moved_rows"] / cfg.units,
+                     "step_frac": ab_pr["total"] / (ms_pristine * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "back_to_back": {"ms_per_step": ms_b2b, "steps_per_s": 1000.0 / ms_b2b,
+                         "moved_rows_per_unit": float(np.mean([a["moved_rows"] for a in ab_b2b])) / cfg.units,
+                         "step_frac": float(np.mean([a["total"] for a in ab_b2b])) / (ms_b2b * 1e-3) / 1e9
+                         / HBM_PEAK_GBS},
         "kernels_ms": kern_ms,
         "separate_calls_ms": sep_ms,
         "mfma_qkt": qkt_mfma(cfg, N, kern_ms["evict_kernel"], sep_ms["score"]),

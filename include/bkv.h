@@ -37,15 +37,24 @@
  *
  * Execution.  Every device call only enqueues kernels on `stream` (a
  * hipStream_t; NULL is the null stream) and returns without synchronising.
- * The library has no global mutable state and is re-entrant; calls that
- * overlap on the same buffers race.
+ * No call needs a workspace: every kernel keeps its intermediate results
+ * (scores, keep sets, Gram matrices) on chip or in the caller's output
+ * buffers.  The only global state is a per-device, per-head-size memo of
+ * the FPS update kernel's resident workgroup count, filled by the first
+ * call that needs it (written atomically; every writer stores the same
+ * value); the library is re-entrant, and calls that overlap on the same
+ * buffers race.
  *
- * Errors.  Calls return BKV_OK or a negative code; on error nothing has been
- * enqueued.  Host-side validation covers shapes, null and misaligned
- * pointers.  Device data (qcount, positions, idx) is clamped into the range
- * the buffers allow, never trusted for addressing.  Faults of a launched
- * kernel surface at the caller's next synchronisation.  No C++ exception
- * crosses this interface.
+ * Errors.  Calls return BKV_OK or a negative code.  Validation of shapes,
+ * null and misaligned pointers, and every host query a call needs (the
+ * occupancy memo above, device attributes) happen before its first launch,
+ * so a call that fails with BKV_EINVAL, BKV_EUNSUPPORTED or BKV_ERANGE, or
+ * with BKV_EHIP from such a query, has enqueued nothing.  A call that
+ * enqueues several kernels (bkv_evict, bkv_decode_step) and gets BKV_EHIP
+ * from a later launch may leave the earlier kernels enqueued.  Device data
+ * (qcount, positions, idx) is clamped into the range the buffers allow,
+ * never trusted for addressing.  Faults of a launched kernel surface at the
+ * caller's next synchronisation.  No C++ exception crosses this interface.
  */
 #ifndef BKV_H
 #define BKV_H
@@ -57,7 +66,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 4
+#define BKV_ABI_VERSION 5
 
 typedef uint16_t bkv_bf16; /* raw bf16 bits */
 
@@ -88,6 +97,13 @@ enum {
  *     order. */
 #define BKV_BEACON_INITIAL 4u
 #define BKV_BEACON_RANDOM 8u
+/* BKV_BEACON_NAIVE (naive full-history FPS, the memory-hungry baseline of
+ * Notes §3.2 Fig. 7): the caller keeps every past query of each head in a
+ * history (bkv_history_append) and, before each eviction, fills the buffers
+ * with FPS(history, n_beacon) by bkv_fps_history.  The continual update and
+ * the merge then leave the buffers alone (fps_sel receives -1s), and
+ * bkv_decode_step touches no buffer in the collection phase. */
+#define BKV_BEACON_NAIVE 16u
 
 typedef struct bkv_shape {
     int32_t n_layers, batch, n_q_heads, n_kv_heads, head_dim; /* head_dim in {64, 128}; G <= 8 */
@@ -104,6 +120,11 @@ typedef struct bkv_shape {
 
 /* ABI version (BKV_ABI_VERSION). */
 int bkv_version(void);
+
+/* Workspace a call needs for this shape and cache length: always 0 (no
+ * kernel uses scratch memory, see Execution above).  Kept so that callers
+ * sizing a workspace before each call need no special case. */
+size_t bkv_workspace_bytes(const bkv_shape *shape, int32_t n_len);
 
 /* Static text for an error code. */
 const char *bkv_strerror(int code);
@@ -132,6 +153,17 @@ int bkv_rope_table(double theta, int32_t head_dim, int32_t p0, int32_t p1, float
 int bkv_fps_update(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
                    const bkv_bf16 *q_new, int32_t *fps_sel, void *stream);
 
+/* Compression at the freeze point of a cycle (Notes §2.2 App. Alg. 2: the
+ * beacons a cycle is scored with represent every query it collected).  Every
+ * buffer holding more than n_beacon rows (qcount clamped to [0, B_Q^max - 1]
+ * when read) becomes FPS(buffer, n_beacon) exactly as in bkv_fps_update,
+ * survivors in ascending slot order and qcount = n_beacon; other buffers are
+ * left as they are.  fps_sel (nullable) receives the selection order, or -1s
+ * where no sampling ran.  bkv_decode_step runs it on the first step of the
+ * recent phase.  A no-op under BKV_BEACON_INITIAL, _RANDOM or _NAIVE, whose
+ * buffers never hold more than n_beacon beacons. */
+int bkv_fps_compress(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount, int32_t *fps_sel, void *stream);
+
 /* Longest prompt bkv_fps_prefill takes. */
 #define BKV_PREFILL_MAX 8192
 
@@ -155,6 +187,27 @@ int bkv_fps_update(const bkv_shape *shape, bkv_bf16 *qbuf, int32_t *qcount,
  * Errors: BKV_EINVAL (null or misaligned pointer, n_prompt < 0),
  * BKV_EUNSUPPORTED (n_prompt > BKV_PREFILL_MAX). */
 int bkv_fps_prefill(const bkv_shape *shape, const bkv_bf16 *q_prompt, int32_t n_prompt,
+                    bkv_bf16 *qbuf, int32_t *qcount, int32_t *fps_sel, void *stream);
+
+/* Query history of the naive full-history beacons (BKV_BEACON_NAIVE; Notes
+ * §3.2 Fig. 7): for every buffer uq, hist[uq][hcount[uq]] = q_new[uq] and
+ * hcount[uq] grows by one, while hcount[uq] < hcap (a full history takes no
+ * more rows; a negative count reads as 0).  hist: bf16 [qbufs][hcap][head_dim];
+ * hcount: int32 [qbufs]; q_new: bf16 [qbufs][head_dim].  In/out: hist, hcount.
+ * Errors: BKV_EINVAL (null or misaligned pointer, hcap < 0). */
+int bkv_history_append(const bkv_shape *shape, bkv_bf16 *hist, int32_t hcap, int32_t *hcount,
+                       const bkv_bf16 *q_new, void *stream);
+
+/* Beacons from the whole history (BKV_BEACON_NAIVE; Notes §3.2 Fig. 7, with
+ * the FPS of App. Alg. 1): for every buffer uq, the buffer becomes
+ * FPS(hist[uq][0 : n_rows), n_beacon) exactly as bkv_fps_prefill samples a
+ * prompt (same seed rule, order and ties; survivors in ascending history
+ * order, qcount = min(n_rows, n_beacon)).  The rows of buffer uq start at
+ * hist + uq * hcap * head_dim; bkv_fps_prefill is the case hcap = n_rows.
+ * fps_sel (nullable) receives the selection order.  Errors: BKV_EINVAL (null
+ * or misaligned pointer, n_rows < 0 or > hcap), BKV_EUNSUPPORTED (n_rows >
+ * BKV_PREFILL_MAX). */
+int bkv_fps_history(const bkv_shape *shape, const bkv_bf16 *hist, int32_t hcap, int32_t n_rows,
                     bkv_bf16 *qbuf, int32_t *qcount, int32_t *fps_sel, void *stream);
 
 /* Scores of every cached key (Notes §2.1 Eq. 4-5, §2.3 Eq. 7).  Per unit,
@@ -227,7 +280,9 @@ int bkv_evict(const bkv_shape *shape, bkv_bf16 *K, bkv_bf16 *V, int32_t n_len,
  *     the last n_recent_q steps before the cache is full the buffer is left
  *     as it is (its first rows are this cycle's beacons) and the query goes
  *     to the recent ring: q_recent[uq][i] = q_new[uq], pos_recent[b][i] =
- *     pos[b], i = L - (cap - n_recent_q).
+ *     pos[b], i = L - (cap - n_recent_q).  On the first of these steps the
+ *     buffers are first compressed by bkv_fps_compress, so that the beacons
+ *     represent every query of the collection phase.
  * After the step with L = cap - 1 the cache is full; the caller then runs
  * bkv_evict with n_len = cap and t = the last step's pos, which leaves
  * L = budget.

@@ -34,7 +34,8 @@ class EvictConfig:
     seed: int = 20261202
     qcap: int = 32         # rows allocated per query buffer
     pool: str = "max"      # pooling of the weights: "max" (§2.3 Eq. 7) or "mean" (§2.1 Eq. 6, §3.3 Table 2)
-    beacon: str = "fps"    # source of the beacons: "fps" (§2.2), "initial" (§3.4 Table 3), "random" (§3.2 Fig. 6)
+    beacon: str = "fps"    # source of the beacons: "fps" (§2.2), "initial" (§3.4 Table 3), "random" (§3.2 Fig. 6),
+    #                        "naive" (FPS over the whole query history at each eviction, §3.2 Fig. 7)
 
     @property
     def n_len(self) -> int:
@@ -160,5 +161,15 @@ STREAM_SOURCES = tuple(replace(STREAM, name=f"stream-qwen3-4b-{src}", base=repla
 TINY_STREAM_SOURCES = tuple(replace(TINY_STREAM, name=f"stream-tiny-{src}", base=replace(TINY_STREAM.base, beacon=src,
                                                                                         seed=20261202 + 570 + i))
                             for i, src in enumerate(("initial", "random")))
+# Naive full-history FPS against continual FPS (§3.2 Fig. 7): every past query of every head is kept and
+# sampled at each eviction.  At batch 192 and 32K steps that history would be 1.86 TB, so the comparison runs
+# at batch 16 over 7936 decode steps (histories of up to 8192 queries, 38.7 GB, the longest the library
+# samples), beside continual FPS at the same shape.
+STREAM_NAIVE = replace(STREAM, name="stream-qwen3-4b-naive", steps=7936,
+                       base=replace(STREAM.base, batch=16, beacon="naive", seed=20261202 + 580))
+STREAM_B16 = replace(STREAM, name="stream-qwen3-4b-b16", steps=7936, base=replace(STREAM.base, batch=16,
+                                                                                 seed=20261202 + 580))
+TINY_STREAM_NAIVE = replace(TINY_STREAM, name="stream-tiny-naive", base=replace(TINY_STREAM.base, beacon="naive",
+                                                                               seed=20261202 + 590))
 STREAM_CONFIGS = {c.name: c for c in (TINY_STREAM, STREAM, TINY_STREAM_MEAN) + STREAM_SPLITS + TINY_STREAM_SPLITS
-                  + STREAM_SOURCES + TINY_STREAM_SOURCES}
+                  + STREAM_SOURCES + TINY_STREAM_SOURCES + (STREAM_NAIVE, STREAM_B16, TINY_STREAM_NAIVE)}

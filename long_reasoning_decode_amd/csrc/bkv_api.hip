@@ -27,8 +27,10 @@ int check_shape(const bkv_shape* s) {
     if (s->n_beacon + s->n_recent_q > kMaxBq) return BKV_EUNSUPPORTED;
     if (s->qcap < s->n_beacon + s->n_recent_q) return BKV_EINVAL;
     if (s->cap <= 0 || s->budget < 0 || s->n_prefix < 0 || s->n_recent_kv < 0) return BKV_EINVAL;
-    if (s->flags & ~(BKV_CAUSAL_RECENT | BKV_POOL_MEAN | BKV_BEACON_INITIAL | BKV_BEACON_RANDOM)) return BKV_EINVAL;
-    if ((s->flags & BKV_BEACON_INITIAL) && (s->flags & BKV_BEACON_RANDOM)) return BKV_EINVAL;
+    if (s->flags & ~(BKV_CAUSAL_RECENT | BKV_POOL_MEAN | BKV_BEACON_INITIAL | BKV_BEACON_RANDOM | BKV_BEACON_NAIVE))
+        return BKV_EINVAL;
+    const uint32_t src = s->flags & (BKV_BEACON_INITIAL | BKV_BEACON_RANDOM | BKV_BEACON_NAIVE);
+    if (src & (src - 1)) return BKV_EINVAL;   // at most one source
     const int64_t units = (int64_t)s->n_layers * s->batch * s->n_kv_heads;
     const int64_t qbufs = (int64_t)s->n_layers * s->batch * s->n_q_heads;
     if (units > INT32_MAX || qbufs > INT32_MAX) return BKV_ERANGE;
@@ -55,6 +57,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_EHIP; }
 int src_of(const bkv_shape* s) {
     if (s->flags & BKV_BEACON_INITIAL) return bkv::kSrcInitial;
     if (s->flags & BKV_BEACON_RANDOM) return bkv::kSrcRandom;
+    if (s->flags & BKV_BEACON_NAIVE) return bkv::kSrcNaive;
     return bkv::kSrcFps;
 }
 
@@ -72,7 +75,29 @@ bkv::FpsArgs fps_args(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const
     a.n_recent_q = s->n_recent_q;
     a.src = src_of(s);
     a.seed = s->seed;
+    a.compress = 0;
     return a;
+}
+
+// FPS over rows [0, n_rows) of every buffer of q (buffer b's rows start at b * stride rows), into the query
+// buffers: the prefill kernel, or the initial / random rules.
+int launch_sample(const bkv_shape* s, const bkv_bf16* q, int64_t stride_rows, int32_t n_rows, bkv_bf16* qbuf,
+                  int32_t* qcount, int32_t* fps_sel, hipStream_t st) {
+    bkv::PrefillArgs a;
+    a.q = q;
+    a.q_stride = stride_rows * s->head_dim;
+    a.qbuf = qbuf;
+    a.qcount = qcount;
+    a.fps_sel = fps_sel;
+    a.nbuf = qbufs_of(s);
+    a.P = n_rows;
+    a.qcap = s->qcap;
+    a.n_beacon = s->n_beacon;
+    a.src = src_of(s) == bkv::kSrcNaive ? bkv::kSrcFps : src_of(s);
+    a.seed = s->seed;
+    a.lds_bytes = 0;
+    if (a.src != bkv::kSrcFps) return hip_status(bkv::launch_prefill_src(a, s->head_dim, st));
+    return hip_status(bkv::launch_prefill(a, s->head_dim, st));
 }
 
 bkv::ScoreArgs score_args(const bkv_shape* s, const bkv_bf16* K, int32_t n_len, const bkv_bf16* qbuf,
@@ -176,20 +201,50 @@ int bkv_fps_prefill(const bkv_shape* s, const bkv_bf16* q_prompt, int32_t n_prom
     if (n_prompt > BKV_PREFILL_MAX) return BKV_EUNSUPPORTED;
     if (!aligned16(qbuf) || (q_prompt && !aligned16(q_prompt)) || !aligned4(qcount)) return BKV_EINVAL;
     if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
-    bkv::PrefillArgs a;
-    a.q = q_prompt;
-    a.qbuf = qbuf;
-    a.qcount = qcount;
-    a.fps_sel = fps_sel;
-    a.nbuf = qbufs_of(s);
-    a.P = n_prompt;
-    a.qcap = s->qcap;
-    a.n_beacon = s->n_beacon;
-    a.src = src_of(s);
-    a.seed = s->seed;
-    a.lds_bytes = 0;
-    if (a.src != bkv::kSrcFps) return hip_status(bkv::launch_prefill_src(a, s->head_dim, (hipStream_t)stream));
-    return hip_status(bkv::launch_prefill(a, s->head_dim, (hipStream_t)stream));
+    return launch_sample(s, q_prompt, n_prompt, n_prompt, qbuf, qcount, fps_sel, (hipStream_t)stream);
+}
+
+int bkv_fps_history(const bkv_shape* s, const bkv_bf16* hist, int32_t hcap, int32_t n_rows, bkv_bf16* qbuf,
+                    int32_t* qcount, int32_t* fps_sel, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (hcap < 0 || n_rows < 0 || n_rows > hcap || !qbuf || !qcount || (n_rows > 0 && !hist)) return BKV_EINVAL;
+    if (n_rows > BKV_PREFILL_MAX) return BKV_EUNSUPPORTED;
+    if (!aligned16(qbuf) || (hist && !aligned16(hist)) || !aligned4(qcount)) return BKV_EINVAL;
+    if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
+    return launch_sample(s, hist, hcap, n_rows, qbuf, qcount, fps_sel, (hipStream_t)stream);
+}
+
+int bkv_history_append(const bkv_shape* s, bkv_bf16* hist, int32_t hcap, int32_t* hcount, const bkv_bf16* q_new,
+                       void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (hcap < 0 || !hist || !hcount || !q_new) return BKV_EINVAL;
+    if (!aligned16(hist) || !aligned16(q_new) || !aligned4(hcount)) return BKV_EINVAL;
+    bkv::HistArgs a;
+    a.hist = hist;
+    a.hcount = hcount;
+    a.q_new = q_new;
+    a.qbufs = qbufs_of(s);
+    a.hcap = hcap;
+    return hip_status(bkv::launch_history_append(a, s->head_dim, (hipStream_t)stream));
+}
+
+int bkv_fps_compress(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, int32_t* fps_sel, void* stream) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (!qbuf || !qcount || !aligned16(qbuf) || !aligned4(qcount)) return BKV_EINVAL;
+    if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
+    if (src_of(s) != bkv::kSrcFps) return BKV_OK;   // only continual FPS buffers hold uncompressed rows
+    bkv::FpsArgs a = fps_args(s, qbuf, qcount, nullptr, nullptr, fps_sel);
+    a.compress = 1;
+    return hip_status(bkv::launch_fps(a, s->head_dim, false, (hipStream_t)stream));
+}
+
+size_t bkv_workspace_bytes(const bkv_shape* s, int32_t n_len) {
+    (void)s;
+    (void)n_len;
+    return 0;
 }
 
 int bkv_score(const bkv_shape* s, const bkv_bf16* K, int32_t n_len, const bkv_bf16* qbuf,
@@ -332,6 +387,13 @@ int bkv_decode_step(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t L, con
     if (ring && (!q_recent || !pos_recent || !aligned16(q_recent) || !aligned4(pos_recent))) return BKV_EINVAL;
     if (fps_sel && !aligned4(fps_sel)) return BKV_EINVAL;
     hipStream_t st = (hipStream_t)stream;
+    // the buffers' FPS kernels (the update, or the compression at the first ring step) size their grid from
+    // an occupancy query: made here, before anything is enqueued, so that its failure enqueues nothing
+    const bool fps_src = src_of(s) == bkv::kSrcFps;
+    if (fps_src && (!ring || L == ring0)) {
+        int64_t fit = 0;
+        if ((e = hip_status(bkv::fps_grid_limit(s->head_dim, &fit)))) return e;
+    }
 
     bkv::AppendArgs aa;
     aa.K = K;
@@ -348,6 +410,11 @@ int bkv_decode_step(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t L, con
     aa.rope_rows = rope_rows;
     if ((e = hip_status(bkv::launch_append(aa, s->head_dim, st)))) return e;
 
+    if (ring && L == ring0 && fps_src) {   // freeze: buffers still holding more than n_beacon rows are sampled
+        bkv::FpsArgs ca = fps_args(s, qbuf, qcount, nullptr, nullptr, nullptr);
+        ca.compress = 1;
+        if ((e = hip_status(bkv::launch_fps(ca, s->head_dim, false, st)))) return e;
+    }
     if (ring) {
         bkv::RingArgs ra;
         ra.q_recent = q_recent;

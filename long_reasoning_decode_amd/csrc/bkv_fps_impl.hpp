@@ -93,27 +93,32 @@ __device__ __forceinline__ int argmin_keys_halves(int k, int lane) {
 __device__ __forceinline__ int argmin_halves(float v, int lane) { return argmin_keys_halves(order_key(v), lane); }
 
 // Gram entries acc (as laid out by the rank-1 updates) into s.c, the norms
-// into s.nrm, then the cosines over the Gram entries in s.c.
+// into s.nrm, then the cosines over the Gram entries in s.c.  The matrices
+// are symmetric bit for bit (the products are exact and both triangles
+// accumulate them in the same order, and nrm_i nrm_j = nrm_j nrm_i), so
+// each cosine is computed once and written to both of its entries: lane i
+// of half h takes the pairs (i, (i + k) mod 32), k = 0 .. 16, of set h -- 17
+// divisions instead of 32.  An entry (i, i + k) is read as a Gram entry
+// only by lane i at step k (and its mirror (i + k, i) only by lane i + k at
+// step 32 - k, which exists for k = 16 alone); each step's reads precede its
+// writes, so no lane reads an entry another lane has already turned into a
+// cosine.
 __device__ __forceinline__ void cosines2(Smem& s, const f32x32_t& acc, int h, int i) {
 #pragma unroll
     for (int r = 0; r < 32; ++r) s.c[r / 16][8 * ((r % 16) / 4) + 4 * h + (r % 4)][i] = acc[r];
     wave_lds_sync();
-    s.nrm[h][i] = __builtin_sqrtf(s.c[h][i][i]);
+    const float ni = __builtin_sqrtf(s.c[h][i][i]);
+    s.nrm[h][i] = ni;
     wave_lds_sync();
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        const float nj = s.nrm[bb][i];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4_t ni4 = *reinterpret_cast<const f32x4_t*>(&s.nrm[bb][8 * q + 4 * h]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * bb + 4 * q + e;
-                const float ni = ni4[e];
-                const float cq = acc[r] / (ni * nj);
-                s.c[bb][8 * q + 4 * h + e][i] = ((ni == 0.0f) | (nj == 0.0f)) ? 0.0f : cq;
-            }
-        }
+#pragma unroll 2
+    for (int k = 0; k <= kMaxRows / 2; ++k) {
+        const int j = (i + k) & (kMaxRows - 1);
+        const float g = s.c[h][i][j];
+        const float nj = s.nrm[h][j];
+        const float cq = g / (ni * nj);
+        const float v = ((ni == 0.0f) | (nj == 0.0f)) ? 0.0f : cq;
+        s.c[h][i][j] = v;
+        s.c[h][j][i] = v;
     }
     wave_lds_sync();
 }
@@ -171,9 +176,14 @@ __device__ uint64_t fps2(Smem& s, int n0, int n1, int m, int lane) {
     // seed: lowest mean cosine (row sums read down the columns: the matrices are symmetric bit for bit)
     const int nmax = n0 > n1 ? n0 : n1;
     float sum = 0.0f;
-    for (int j = 0; j < nmax; ++j) {
-        const float cj = s.c[h][j][i];
-        sum = j < n ? sum + cj : sum;
+    if (n0 == kMaxRows && n1 == kMaxRows) {   // both sets full (every sampling round of a stream)
+#pragma unroll 8
+        for (int j = 0; j < kMaxRows; ++j) sum = sum + s.c[h][j][i];
+    } else {
+        for (int j = 0; j < nmax; ++j) {
+            const float cj = s.c[h][j][i];
+            sum = j < n ? sum + cj : sum;
+        }
     }
     const float v = i < n ? sum / (float)n : __builtin_inff();
     const int p = argmin_halves(v, lane);
@@ -241,32 +251,42 @@ constexpr int kMaxBuffersPerWave = 16;
 // count n_beacon.  All counts and query pieces are loaded at once (one memory
 // latency per wave), and the sampling reads each new row from q_new, so
 // nothing it reads depends on the appends' stores.
-template <int D>
+// COMPRESS: no query is appended; a buffer holding more than n_beacon rows
+// (count clamped as above) becomes FPS(buffer, n_beacon) the same way, and
+// the other buffers are left as they are.
+template <int D, bool COMPRESS>
 __device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane_in) {
     const int lane = lane_in;
     constexpr int kPieces = D / 8;                 // 16-byte pieces per row
     constexpr int kPerPass = kWave / kPieces;      // buffers per pass of the wave
     const int bqmax = a.n_beacon + a.n_recent_q;
     const int m = a.n_beacon;
+    constexpr bool compress = COMPRESS;
     const int c_l = lane < nw ? clampi(a.qcount[b0 + lane], 0, bqmax - 1) : 0;   // count of buffer b0 + lane
-    constexpr int kMaxPass = (kMaxBuffersPerWave + kPerPass - 1) / kPerPass;
-    u32x4_t piece[kMaxPass];
+    if constexpr (!compress) {
+        constexpr int kMaxPass = (kMaxBuffersPerWave + kPerPass - 1) / kPerPass;
+        u32x4_t piece[kMaxPass];
 #pragma unroll
-    for (int p = 0; p < kMaxPass; ++p) {
-        const int bi = p * kPerPass + lane / kPieces;
-        if (p * kPerPass < nw && bi < nw)
-            piece[p] = reinterpret_cast<const u32x4_t*>(a.q_new + (size_t)(b0 + bi) * D)[lane % kPieces];
-    }
+        for (int p = 0; p < kMaxPass; ++p) {
+            const int bi = p * kPerPass + lane / kPieces;
+            if (p * kPerPass < nw && bi < nw)
+                piece[p] = reinterpret_cast<const u32x4_t*>(a.q_new + (size_t)(b0 + bi) * D)[lane % kPieces];
+        }
 #pragma unroll
-    for (int p = 0; p < kMaxPass; ++p) {
-        const int bi = p * kPerPass + lane / kPieces;
-        const int c = __shfl(c_l, bi < kWave ? bi : 0, kWave);
-        if (p * kPerPass < nw && bi < nw)
-            reinterpret_cast<u32x4_t*>(a.qbuf + ((size_t)(b0 + bi) * a.qcap + c) * D)[lane % kPieces] = piece[p];
+        for (int p = 0; p < kMaxPass; ++p) {
+            const int bi = p * kPerPass + lane / kPieces;
+            const int c = __shfl(c_l, bi < kWave ? bi : 0, kWave);
+            if (p * kPerPass < nw && bi < nw)
+                reinterpret_cast<u32x4_t*>(a.qbuf + ((size_t)(b0 + bi) * a.qcap + c) * D)[lane % kPieces] = piece[p];
+        }
     }
-    const int n_l = c_l + 1;
-    const bool full = lane < nw && n_l >= bqmax && n_l > m;
-    if (lane < nw && !full) {
+    const int n_l = compress ? c_l : c_l + 1;
+    const bool full = lane < nw && (compress ? n_l > m : n_l >= bqmax && n_l > m);
+    if (compress && m == 0) {   // nothing is kept
+        if (lane < nw && n_l > 0) a.qcount[b0 + lane] = 0;
+        return;
+    }
+    if (lane < nw && !full && !compress) {
         a.qcount[b0 + lane] = n_l;
     }
     if (a.fps_sel && m > 0) {   // buffers that do not sample: -1s (all kept when n_recent_q == 0)
@@ -276,7 +296,8 @@ __device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane_
             const int bi = e < nw * m ? e / m : 0, i = e % m;
             const int n = __shfl(n_l, bi, kWave);
             const bool f = __shfl((int)full, bi, kWave) != 0;
-            if (e < nw * m && !f) a.fps_sel[(size_t)(b0 + bi) * m + i] = (n >= bqmax && i < n) ? i : -1;
+            if (e < nw * m && !f)
+                a.fps_sel[(size_t)(b0 + bi) * m + i] = (!compress && n >= bqmax && i < n) ? i : -1;
         }
     }
     uint64_t todo = __ballot(full);
@@ -291,9 +312,11 @@ __device__ void update_wave(const FpsArgs& a, int b0, int nw, Smem& s, int lane_
         const int c0 = __builtin_amdgcn_readlane(c_l, bi0), c1 = __builtin_amdgcn_readlane(c_l, bi1);
         bkv_bf16* buf0 = a.qbuf + (size_t)(b0 + bi0) * a.qcap * D;
         bkv_bf16* buf1 = a.qbuf + (size_t)(b0 + bi1) * a.qcap * D;
-        const bkv_bf16* qn0 = a.q_new + (size_t)(b0 + bi0) * D;
-        const bkv_bf16* qn1 = a.q_new + (size_t)(b0 + bi1) * D;
-        const Cand A{buf0, c0, qn0, c0 + 1}, B{buf1, c1, qn1, two ? c1 + 1 : 0};
+        // candidates: the buffer's rows, then (update) the new query
+        const bkv_bf16* qn0 = compress ? buf0 : a.q_new + (size_t)(b0 + bi0) * D;
+        const bkv_bf16* qn1 = compress ? buf1 : a.q_new + (size_t)(b0 + bi1) * D;
+        constexpr int add = compress ? 0 : 1;
+        const Cand A{buf0, c0, qn0, c0 + add}, B{buf1, c1, qn1, two ? c1 + add : 0};
         gram2<D>(s, A, B, lane_r);
         const uint64_t mask = fps2(s, A.n, B.n, m, lane_r);
         write_rows<D>(s, (uint32_t)mask, buf0, c0, qn0, lane_r);

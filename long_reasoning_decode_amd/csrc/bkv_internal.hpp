@@ -15,14 +15,16 @@ struct FpsArgs {
     const bkv_bf16* q_recent;  // [nbuf][n_recent_q][d] (merge)
     int32_t* fps_sel;          // [nbuf][n_beacon] or null
     int nbuf, qcap, n_beacon, n_recent_q;
-    int src;                   // beacon source: kSrcFps, kSrcInitial, kSrcRandom
+    int src;                   // beacon source: kSrcFps, kSrcInitial, kSrcRandom, kSrcNaive
     uint32_t seed;             // key of the random-history draws
+    int compress;              // update without an append: sample the buffers holding more than n_beacon rows
 };
 
-constexpr int kSrcFps = 0, kSrcInitial = 1, kSrcRandom = 2;
+constexpr int kSrcFps = 0, kSrcInitial = 1, kSrcRandom = 2, kSrcNaive = 3;
 
 struct PrefillArgs {
-    const bkv_bf16* q;         // [nbuf][P][d] prompt queries
+    const bkv_bf16* q;         // prompt queries: buffer b's rows are q[b * q_stride + i * d], i < P
+    int64_t q_stride;          // elements from one buffer's first row to the next buffer's
     bkv_bf16* qbuf;            // [nbuf][qcap][d]
     int32_t* qcount;           // [nbuf]
     int32_t* fps_sel;          // [nbuf][n_beacon] or null
@@ -93,6 +95,13 @@ struct RingArgs {
     int qbufs, batch, n_recent_q, slot;
 };
 
+struct HistArgs {
+    bkv_bf16* hist;            // [qbufs][hcap][d]
+    int32_t* hcount;           // [qbufs]
+    const bkv_bf16* q_new;     // [qbufs][d]
+    int qbufs, hcap;
+};
+
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t st);
 // initial / random beacon sources: one offer per buffer, the merge of the recents, the prefill
@@ -105,6 +114,9 @@ hipError_t launch_compact(const CompactArgs& a, int d, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int d, hipStream_t st);
 hipError_t launch_evict(const EvictArgs& a, int d, hipStream_t st);
 hipError_t launch_ring(const RingArgs& a, int d, hipStream_t st);
+hipError_t launch_history_append(const HistArgs& a, int d, hipStream_t st);
+// the update kernel's grid (workgroups resident at once); queried before a call's first launch
+hipError_t fps_grid_limit(int d, int64_t* out);
 hipError_t launch_attention(const AttnArgs& a, int d, hipStream_t st);
 
 }  // namespace bkv

@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     if (b >= a.nbuf) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int P = a.P, m = a.n_beacon;
-    const bkv_bf16* Q = a.q + (size_t)b * P * D;
+    const bkv_bf16* Q = a.q + (size_t)b * a.q_stride;
     bkv_bf16* buf = a.qbuf + (size_t)b * a.qcap * D;
 
     if (m <= 0) {   // no representatives kept

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void prefill_src_kernel(PrefillArgs a) {
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b >= a.nbuf) return;
     const int nb = a.n_beacon, P = a.P;
-    const bkv_bf16* Q = a.q + (size_t)b * P * D;
+    const bkv_bf16* Q = a.q + (size_t)b * a.q_stride;
     bkv_bf16* buf = a.qbuf + (size_t)b * a.qcap * D;
     if (tid < 32) last[tid] = -1;
     __syncthreads();
@@ -153,7 +153,7 @@ hipError_t launch_offer(const FpsArgs& a, int d, hipStream_t st) {
 
 hipError_t launch_offer_merge(const FpsArgs& a, int d, hipStream_t st) {
     if (a.nbuf <= 0) return hipSuccess;
-    if (a.src == kSrcInitial) {
+    if (a.src == kSrcInitial || a.src == kSrcNaive) {   // the buffer stays as it is
         if (!a.fps_sel || a.n_beacon == 0) return hipSuccess;
         const int64_t n = (int64_t)a.nbuf * a.n_beacon;
         hipLaunchKernelGGL(fill_sel_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.fps_sel, n);

@@ -71,7 +71,35 @@ __global__ __launch_bounds__(256) void ring_kernel(RingArgs a) {
     reinterpret_cast<u32x4_t*>(a.q_recent + (uq * a.n_recent_q + a.slot) * D)[piece] = v;
 }
 
+// Full-history beacons (the naive FPS of Notes §3.2 Fig. 7): thread per
+// 16-byte piece, hist[uq][hcount[uq]] = q_new[uq] and the count grows by one
+// while it is below hcap (a full history takes no more rows).  The pieces of
+// one buffer sit in one wavefront, whose count load completes before its
+// count store, so every piece sees the count from before the call.
+template <int D>
+__global__ __launch_bounds__(256) void history_kernel(HistArgs a) {
+    constexpr int kPieces = D / 8;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)a.qbufs * kPieces) return;
+    const int64_t uq = t / kPieces;
+    const int piece = (int)(t % kPieces);
+    const int n = a.hcount[uq] > 0 ? a.hcount[uq] : 0;
+    if (n >= a.hcap) return;
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(a.q_new + uq * D)[piece];
+    reinterpret_cast<u32x4_t*>(a.hist + (uq * a.hcap + n) * D)[piece] = v;
+    if (piece == 0) a.hcount[uq] = n + 1;
+}
+
 }  // namespace
+
+hipError_t launch_history_append(const HistArgs& a, int d, hipStream_t st) {
+    const int64_t threads = (int64_t)a.qbufs * (d / 8);
+    if (threads <= 0) return hipSuccess;
+    dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    if (d == 64) hipLaunchKernelGGL(history_kernel<64>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(history_kernel<128>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int d, hipStream_t st) {
     if (a.units <= 0) return hipSuccess;

@@ -24,11 +24,13 @@ BKV_CAUSAL_RECENT = 1
 BKV_POOL_MEAN = 2
 BKV_BEACON_INITIAL = 4
 BKV_BEACON_RANDOM = 8
+BKV_BEACON_NAIVE = 16
 ERRORS = {0: "BKV_OK", -1: "BKV_EINVAL", -2: "BKV_EUNSUPPORTED", -3: "BKV_ERANGE", -4: "BKV_EHIP"}
 
-EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_fps_update",
+EXPORTS = ("bkv_version", "bkv_strerror", "bkv_rope_table", "bkv_workspace_bytes", "bkv_fps_update",
            "bkv_fps_merge", "bkv_fps_prefill", "bkv_score", "bkv_select", "bkv_compact", "bkv_evict",
-           "bkv_decode_step", "bkv_append_kv", "bkv_decode_attention")
+           "bkv_decode_step", "bkv_append_kv", "bkv_decode_attention", "bkv_fps_compress", "bkv_history_append",
+           "bkv_fps_history")
 
 
 class Shape(C.Structure):
@@ -70,8 +72,13 @@ def load():
         L.bkv_decode_step.argtypes = [SP, P, P, i32, P, P, P, P, P, P, P, P, P, i32, P, st]
         L.bkv_append_kv.argtypes = [SP, P, P, i32, P, P, P, P, i32, st]
         L.bkv_decode_attention.argtypes = [SP, P, P, i32, P, P, P, i32, P, st]
-        for f in EXPORTS[3:]:
+        L.bkv_fps_compress.argtypes = [SP, P, P, P, st]
+        L.bkv_history_append.argtypes = [SP, P, i32, P, P, st]
+        L.bkv_fps_history.argtypes = [SP, P, i32, i32, P, P, P, st]
+        for f in EXPORTS[4:]:
             getattr(L, f).restype = C.c_int
+        L.bkv_workspace_bytes.argtypes = [SP, i32]
+        L.bkv_workspace_bytes.restype = C.c_size_t
         _lib = L
     return _lib
 
@@ -86,7 +93,7 @@ def version() -> int:
 
 def flags_of(cfg: EvictConfig) -> int:
     """Default flags of a workload: causal recent rows, and the pooling and beacon source it names."""
-    src = {"fps": 0, "initial": BKV_BEACON_INITIAL, "random": BKV_BEACON_RANDOM}[cfg.beacon]
+    src = {"fps": 0, "initial": BKV_BEACON_INITIAL, "random": BKV_BEACON_RANDOM, "naive": BKV_BEACON_NAIVE}[cfg.beacon]
     return BKV_CAUSAL_RECENT | (BKV_POOL_MEAN if cfg.pool == "mean" else 0) | src
 
 
@@ -174,6 +181,33 @@ def fps_prefill(shape: Shape, q_prompt, n_prompt: int, qbuf, qcount, fps_sel=Non
     _check(load().bkv_fps_prefill(C.byref(shape), _ptr(q_prompt, bf16, "q_prompt"), int(n_prompt),
                                   _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(fps_sel, i32, "fps_sel"),
                                   _stream(stream)), "bkv_fps_prefill")
+
+
+def workspace_bytes(shape: Shape, n_len: int) -> int:
+    return int(load().bkv_workspace_bytes(C.byref(shape), int(n_len)))
+
+
+def fps_compress(shape: Shape, qbuf, qcount, fps_sel=None, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, qbuf=(qbuf, Qb * shape.qcap * d), qcount=(qcount, Qb), fps_sel=(fps_sel, Qb * shape.n_beacon))
+    _check(load().bkv_fps_compress(C.byref(shape), _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"),
+                                   _ptr(fps_sel, i32, "fps_sel"), _stream(stream)), "bkv_fps_compress")
+
+
+def history_append(shape: Shape, hist, hcap: int, hcount, q_new, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, hist=(hist, Qb * hcap * d), hcount=(hcount, Qb), q_new=(q_new, Qb * d))
+    _check(load().bkv_history_append(C.byref(shape), _ptr(hist, bf16, "hist"), int(hcap), _ptr(hcount, i32, "hcount"),
+                                     _ptr(q_new, bf16, "q_new"), _stream(stream)), "bkv_history_append")
+
+
+def fps_history(shape: Shape, hist, hcap: int, n_rows: int, qbuf, qcount, fps_sel=None, stream=None) -> None:
+    U, Qb, d = _counts(shape)
+    _need(shape, hist=(hist, Qb * hcap * d), qbuf=(qbuf, Qb * shape.qcap * d), qcount=(qcount, Qb),
+          fps_sel=(fps_sel, Qb * shape.n_beacon))
+    _check(load().bkv_fps_history(C.byref(shape), _ptr(hist, bf16, "hist"), int(hcap), int(n_rows),
+                                  _ptr(qbuf, bf16, "qbuf"), _ptr(qcount, i32, "qcount"), _ptr(fps_sel, i32, "fps_sel"),
+                                  _stream(stream)), "bkv_fps_history")
 
 
 def score(shape: Shape, K, n_len: int, qbuf, qcount, q_recent, pos_recent, t, rope_cs, scores,

@@ -5,7 +5,9 @@ for the model's decode loop (Notes §2.2, App. Alg. 2; Summary, pseudocode).
 It draws every step's pre-RoPE q/k/v with ``synth.StreamGen``, hands them to
 the library one decode step at a time, and evicts whenever the cache is full.
 The library does all of the method's work; this loop only keeps the cache
-length and passes pointers.
+length and passes pointers.  Under the naive full-history source (Notes §3.2
+Fig. 7) it also hands every query to the library's history and, before each
+eviction, has the library sample the beacons from the whole history.
 
 Inputs are drawn a block of steps at a time, before the block's library calls,
 so that timing a block (``timed=True``) measures the eviction manager alone.
@@ -42,6 +44,13 @@ class StreamRun:
         self.q_recent = torch.zeros(L, B, Hq, b.n_recent_q, d, dtype=torch.bfloat16, device=dev)
         self.pos_recent = torch.zeros(B, b.n_recent_q, dtype=torch.int32, device=dev)
         self.rope = torch.from_numpy(lib.rope_table(b.theta, d, 0, scfg.rope_rows)).to(dev)
+        self.naive = b.beacon == "naive"
+        # naive full-history beacons: every past query of every head, up to the longest history the library
+        # samples (a full history takes no more rows)
+        self.hcap = lib.BKV_PREFILL_MAX if self.naive else 0
+        self.hist = torch.zeros(L, B, Hq, self.hcap, d, dtype=torch.bfloat16, device=dev) if self.naive else None
+        self.hcount = torch.zeros(L, B, Hq, dtype=torch.int32, device=dev) if self.naive else None
+        self.h_rows = 0   # rows every history holds (the streams run in lockstep)
         self.idx = torch.empty(b.units, b.budget, dtype=torch.int32, device=dev)
         self.scores = torch.empty(b.units, b.cap, dtype=torch.float32, device=dev)
         self.gen = synth.StreamGen(scfg, dev, seed)
@@ -56,26 +65,38 @@ class StreamRun:
             self.rec_b = (self.rec_units // Hkv) % B
             self.rec = {k: [] for k in ("q_new", "k_new", "v_new", "pos", "idx", "scores")}
 
-    _STATE = ("K", "V", "qbuf", "qcount", "q_recent", "pos_recent")
+    @property
+    def _STATE(self):
+        return ("K", "V", "qbuf", "qcount", "q_recent", "pos_recent") + (("hist", "hcount") if self.naive else ())
 
     def state_dict(self) -> dict:
         """Everything needed to resume the stream: the eviction manager's tensors, the cache length and
         counters, and the input generator's state."""
         st = {k: getattr(self, k).clone() for k in self._STATE}
-        st.update(L=self.L, n_ev=self.n_ev, steps_done=self.steps_done, gen=self.gen.state_dict())
+        st.update(L=self.L, n_ev=self.n_ev, steps_done=self.steps_done, h_rows=self.h_rows,
+                  gen=self.gen.state_dict())
         return st
 
     def load_state_dict(self, st: dict) -> None:
         for k in self._STATE:
             getattr(self, k).copy_(st[k])
         self.L, self.n_ev, self.steps_done = int(st["L"]), int(st["n_ev"]), int(st["steps_done"])
+        self.h_rows = int(st.get("h_rows", 0))
         self.gen.load_state_dict(st["gen"])
 
     def state_bytes(self) -> int:
-        """HBM held by the eviction manager's own state (cache, buffers, ring, table, keep-set and score copies)."""
+        """HBM held by the eviction manager's own state (cache, buffers, ring, table, keep-set and score copies,
+        and the query history under the naive source)."""
         ts = (self.K, self.V, self.qbuf, self.qcount, self.q_recent, self.pos_recent, self.rope, self.idx,
-              self.scores)
+              self.scores) + ((self.hist, self.hcount) if self.naive else ())
         return sum(t.numel() * t.element_size() for t in ts)
+
+    def beacon_state_bytes(self) -> dict:
+        """HBM of the beacon state: the query buffers (and the history, under the naive source) -- the memory
+        axis of the continual-against-naive FPS comparison (Notes §3.2 Fig. 7)."""
+        buf = self.qbuf.numel() * self.qbuf.element_size() + self.qcount.numel() * 4
+        hist = self.hist.numel() * self.hist.element_size() + self.hcount.numel() * 4 if self.naive else 0
+        return {"buffers": buf, "history": hist, "total": buf + hist}
 
     def _record_inputs(self, blk: dict, n: int) -> None:
         b = self.base
@@ -119,6 +140,9 @@ class StreamRun:
                 lib.decode_step(self.shape, self.K, self.V, self.L, blk["k_new"][i], blk["v_new"][i], blk["pos"][i],
                                 self.qbuf, self.qcount, blk["q_new"][i], self.q_recent, self.pos_recent, self.rope,
                                 stream=stream)
+                if self.naive:
+                    lib.history_append(self.shape, self.hist, self.hcap, self.hcount, blk["q_new"][i], stream=stream)
+                    self.h_rows = min(self.h_rows + 1, self.hcap)
                 self.L += 1
                 if detail:
                     step_evs.append(ev())
@@ -130,6 +154,9 @@ class StreamRun:
                     if timed:
                         evs.append((ev(), ev()))
                         evs[-1][0].record(stream)
+                    if self.naive:   # beacons: FPS over each head's history, less the cycle's recent queries
+                        lib.fps_history(self.shape, self.hist, self.hcap, max(0, self.h_rows - b.n_recent_q),
+                                        self.qbuf, self.qcount, stream=stream)
                     lib.evict(self.shape, self.K, self.V, b.cap, self.qbuf, self.qcount, self.q_recent,
                               self.pos_recent, blk["pos"][i], self.rope,
                               idx_out=self.idx if rec or keep_idx else None,
@@ -172,6 +199,9 @@ class StreamRun:
                 if qc >= bqmax:
                     rounds += 1
                     qc = b.n_beacon
+            elif L == ring0 and qc > b.n_beacon:   # compressed at the freeze point
+                rounds += 1
+                qc = b.n_beacon
             L += 1
             if L == b.cap:
                 qc = min(min(qc, b.n_beacon) + b.n_recent_q, b.n_beacon)

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-SRC_FPS, SRC_INITIAL, SRC_RANDOM = 0, 1, 2
+SRC_FPS, SRC_INITIAL, SRC_RANDOM, SRC_NAIVE = 0, 1, 2, 3
 
 
 class _Cfg(C.Structure):
@@ -51,7 +51,7 @@ class OracleCfg:
     qcap: int = 32
     causal: int = 1
     pool_mean: int = 0
-    beacon_src: int = 0   # SRC_FPS, SRC_INITIAL or SRC_RANDOM
+    beacon_src: int = 0   # SRC_FPS, SRC_INITIAL, SRC_RANDOM or SRC_NAIVE
     seed: int = 0
     n_layers: int = 1
     batch: int = 1
@@ -94,6 +94,8 @@ def lib():
         L.bkvo_fps_f64.argtypes = [P, i32, i32, i32, P, P]
         L.bkvo_fps_f64.restype = i32
         L.bkvo_fps_update.argtypes = [i32, i32, i32, i32, i32, P, P, P, P]
+        L.bkvo_fps_plain.argtypes = [P, i32, i32, i32, P, P, P, P]
+        L.bkvo_fps_plain.restype = i32
         L.bkvo_fps_long.argtypes = [P, i32, i32, i32, P]
         L.bkvo_fps_long.restype = i32
         L.bkvo_pairwise_sum.argtypes = [P, i32]
@@ -112,7 +114,8 @@ def lib():
         L.bkvo_evict.argtypes = [P, i32, i32, P, P, P, P, P, P, P, P, P, P, P, i32]
         L.bkvo_merge.argtypes = [P, i32, P, P, P, P]
         L.bkvo_compact.argtypes = [P, i32, i32, P, P, P]
-        L.bkvo_stream.argtypes = [P, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, i32, i32]
+        L.bkvo_stream.argtypes = [P, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, i32, P, P, i32, i32]
+        L.bkvo_fps_compress.argtypes = [i32, i32, i32, i32, i32, P, P, P]
         L.bkvo_stream.restype = i32
         L.bkvo_cfg_size.restype = i32
         assert L.bkvo_cfg_size() == C.sizeof(_Cfg), "oracle cfg struct mismatch"
@@ -197,6 +200,25 @@ def fps_long(X, m: int) -> list[int]:
     return sel[:got].tolist()
 
 
+def fps_plain(X, m: int, forced=None):
+    """FPS by the page's definition in fp64 (O(n^2 d) seed), optionally replaying the picks `forced`.
+    Returns (sel, regret, margin): the rows taken, and per step the fp64 value of the row taken minus the
+    best value (0 when optimal, inf for an invalid forced pick) and the gap between the two best values."""
+    X = _u16(X)
+    n, d = X.shape
+    k = max(1, min(n, m))
+    sel = np.empty(k, dtype=np.int32)
+    reg = np.empty(k, dtype=np.float64)
+    mar = np.empty(k, dtype=np.float64)
+    f = None
+    if forced is not None:
+        f = np.full(k, -1, dtype=np.int32)
+        fr = np.asarray(forced, dtype=np.int32)[:k]
+        f[:len(fr)] = fr
+    got = lib().bkvo_fps_plain(_p(X), n, d, m, _p(f), _p(sel), _p(reg), _p(mar))
+    return sel[:got].tolist(), reg[:got].copy(), mar[:got].copy()
+
+
 def pairwise_sum(x) -> float:
     x = np.ascontiguousarray(x, dtype=np.float32)
     return float(np.float32(lib().bkvo_pairwise_sum(_p(x), x.size)))
@@ -249,6 +271,16 @@ def fps_update(qbuf, qcount, q_new, n_beacon: int, n_recent_q: int) -> np.ndarra
     sel = np.empty((nbuf, n_beacon), dtype=np.int32)
     lib().bkvo_fps_update(nbuf, qcap, d, n_beacon, n_recent_q, _p(qbuf), _p(qcount), _p(q_new), _p(sel))
     return sel
+
+
+def fps_compress(qbuf, qcount, n_beacon: int, n_recent_q: int) -> np.ndarray:
+    """Freeze-point compression, in place on qbuf [nbuf, qcap, d] and qcount [nbuf]; returns sel [nbuf, n_beacon]."""
+    assert qbuf.dtype == np.uint16 and qbuf.flags["C_CONTIGUOUS"]
+    assert qcount.dtype == np.int32 and qcount.flags["C_CONTIGUOUS"]
+    nbuf, qcap, d = qbuf.shape
+    sel = np.empty((nbuf, max(n_beacon, 1)), dtype=np.int32)
+    lib().bkvo_fps_compress(nbuf, qcap, d, n_beacon, n_recent_q, _p(qbuf), _p(qcount), _p(sel))
+    return sel[:, :n_beacon]
 
 
 def row_weights(q, K, vis: int | None = None):
@@ -330,9 +362,10 @@ def decode_attention(cfg: OracleCfg, K, V, q, pos, n_len: int):
 
 
 def stream(cfg: OracleCfg, k_new, v_new, q_new, pos, K, V, L: int, qbuf, qcount, q_recent, pos_recent,
-           max_ev: int = 0, nthreads: int | None = None) -> dict:
+           max_ev: int = 0, nthreads: int | None = None, hist=None, hcount=None) -> dict:
     """Decode steps of the eviction cycle for U units in lockstep, in place on the state (K, V, qbuf,
-    qcount, q_recent, pos_recent: unit-major numpy arrays).  Step inputs are step-major:
+    qcount, q_recent, pos_recent: unit-major numpy arrays; under SRC_NAIVE also the query history
+    hist [U, G, hcap, d] and its counts hcount [U, G]).  Step inputs are step-major:
     k_new, v_new [S, U, d] (k_new pre-RoPE), q_new [S, U, G, d], pos [S, U].
     Returns the final cache length, the number of evictions and the first max_ev evictions'
     keep sets [max_ev, U, budget] and scores [max_ev, U, cap]."""
@@ -344,11 +377,18 @@ def stream(cfg: OracleCfg, k_new, v_new, q_new, pos, K, V, L: int, qbuf, qcount,
     cfg.check_units(U)
     assert k_new.shape == (S, U, cfg.d) and v_new.shape == (S, U, cfg.d)
     assert q_new.shape == (S, U, cfg.G, cfg.d)
+    hcap = 0
+    if cfg.beacon_src == SRC_NAIVE:
+        assert hist is not None and hcount is not None
+        assert hist.dtype == np.uint16 and hist.flags["C_CONTIGUOUS"] and hist.shape[:2] == (U, cfg.G)
+        assert hcount.dtype == np.int32 and hcount.flags["C_CONTIGUOUS"] and hcount.shape == (U, cfg.G)
+        hcap = hist.shape[2]
     idx = np.full((max_ev, U, cfg.budget), -1, dtype=np.int32) if max_ev > 0 else None
     sc = np.zeros((max_ev, U, cfg.cap), dtype=np.float64) if max_ev > 0 else None
     Lb = C.c_int32(int(L))
     cc = cfg.c()
     n_ev = lib().bkvo_stream(C.byref(cc), U, S, _p(k_new), _p(v_new), _p(q_new), _p(pos), _p(K), _p(V),
                              C.byref(Lb), _p(qbuf), _p(qcount), _p(q_recent), _p(pos_recent), _p(idx), _p(sc),
-                             max_ev, nthreads or default_threads())
+                             max_ev, _p(hist) if hcap else None, _p(hcount) if hcap else None, hcap,
+                             nthreads or default_threads())
     return {"L": Lb.value, "n_ev": n_ev, "idx": idx, "scores": sc}

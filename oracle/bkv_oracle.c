@@ -59,7 +59,7 @@ typedef struct {
 
 static long long global_unit(const bkvo_cfg *c, int u) { return c->unit_ids ? c->unit_ids[u] : (long long)u; }
 
-enum { BKVO_SRC_FPS = 0, BKVO_SRC_INITIAL = 1, BKVO_SRC_RANDOM = 2 };
+enum { BKVO_SRC_FPS = 0, BKVO_SRC_INITIAL = 1, BKVO_SRC_RANDOM = 2, BKVO_SRC_NAIVE = 3 };
 
 int bkvo_reservoir_slot(unsigned seed, long long uq, int n, int n_beacon);
 
@@ -386,6 +386,99 @@ int bkvo_fps_long(const uint16_t *X, int n, int d, int m, int *sel)
     return cnt;
 }
 
+/* FPS exactly as the page defines it (Notes §2.2, App. Alg. 1), in fp64,
+ * with no shortcut: every mean cosine a_i = (1/n) sum_j cos(q_i, q_j) is
+ * summed from the n cosines of row i (O(n^2 d)); the greedy steps keep
+ * S_j = max over the rows taken of cos(q_j, q_r) and take the untaken row
+ * of smallest S (lowest index on ties).  Cosines are computed on the fly
+ * (memory O(n d)).  This is the reference for FPS over many rows that does
+ * not share the fp32 operation order of bkvo_fps_long.
+ *
+ * Replay: when forced is non-NULL, step s takes forced[s] instead of its own
+ * argmin (the rows taken so far are then those of the replayed selection),
+ * and regret[s] is the fp64 value of the row taken minus the smallest value
+ * over the untaken rows (a_i at the seed, S_j afterwards): 0 where the replay
+ * takes an optimal row, +INFINITY where forced[s] is out of range or already
+ * taken (the replay then goes on from the optimal row, which sel records).
+ * margin[s] (nullable) is the gap between the smallest and the second
+ * smallest value at that step (+INFINITY with one candidate): the room fp
+ * rounding has to decide the step either way.  sel receives the rows taken.
+ * Returns the number of steps, min(n, m) (the selection 0..n-1 with zero
+ * regret and infinite margins when n <= m).                              */
+static double cos64(const double *x, const double *nrm, int d, int i, int j)
+{
+    if (nrm[i] == 0.0 || nrm[j] == 0.0) return 0.0;
+    double acc = 0.0;
+    for (int k = 0; k < d; ++k) acc += x[(size_t)i * d + k] * x[(size_t)j * d + k];
+    return acc / (nrm[i] * nrm[j]);
+}
+
+int bkvo_fps_plain(const uint16_t *X, int n, int d, int m, const int *forced, int *sel, double *regret,
+                   double *margin)
+{
+    if (n <= 0 || m <= 0) return 0;
+    if (n <= m) {
+        for (int i = 0; i < n; ++i) {
+            sel[i] = i;
+            if (regret) regret[i] = 0.0;
+            if (margin) margin[i] = INFINITY;
+        }
+        return n;
+    }
+    double *x = (double *)malloc(sizeof(double) * (size_t)n * d);
+    double *nrm = (double *)malloc(sizeof(double) * (size_t)n);
+    double *v = (double *)malloc(sizeof(double) * (size_t)n);   /* a_i, then S_j */
+    char *taken = (char *)calloc((size_t)n, 1);
+    for (size_t i = 0; i < (size_t)n * d; ++i) x[i] = (double)bf2f(X[i]);
+    for (int i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += x[(size_t)i * d + k] * x[(size_t)i * d + k];
+        nrm[i] = sqrt(acc);
+    }
+    for (int i = 0; i < n; ++i) {
+        double sum = 0.0;
+        for (int j = 0; j < n; ++j) sum += cos64(x, nrm, d, i, j);
+        v[i] = sum / n;
+    }
+    int cnt = 0;
+    while (cnt < m) {
+        /* the best and second-best untaken values (first index on ties) */
+        int best = -1;
+        double second = INFINITY;
+        for (int j = 0; j < n; ++j) {
+            if (taken[j]) continue;
+            if (best < 0 || v[j] < v[best]) {
+                if (best >= 0) second = v[best];
+                best = j;
+            } else if (v[j] < second) {
+                second = v[j];
+            }
+        }
+        int r = forced ? forced[cnt] : best;
+        double rg;
+        if (r < 0 || r >= n || taken[r]) {
+            rg = INFINITY;
+            r = best;   /* continue the replay from the optimal row */
+        } else {
+            rg = v[r] - v[best];
+        }
+        if (regret) regret[cnt] = rg;
+        if (margin) margin[cnt] = second - v[best];
+        sel[cnt++] = r;
+        taken[r] = 1;
+        if (cnt == 1) {   /* S_j starts as the cosine to the seed */
+            for (int j = 0; j < n; ++j) v[j] = cos64(x, nrm, d, j, r);
+        } else {
+            for (int j = 0; j < n; ++j) {
+                double c = cos64(x, nrm, d, j, r);
+                if (c > v[j]) v[j] = c;
+            }
+        }
+    }
+    free(x); free(nrm); free(v); free(taken);
+    return cnt;
+}
+
 /* Prefill initialisation of nbuf query buffers (global indices from buf0)
  * from their prompt queries q_prompt[b][0 .. P), under the beacon source src:
  *   FPS     -- the buffer becomes FPS_long(prompt, n_beacon), survivors in
@@ -484,6 +577,46 @@ void bkvo_fps_update(int nbuf, int qcap, int d, int n_beacon, int n_recent_q,
     free(tmp);
 }
 
+/* Compression at the freeze point of a cycle (Notes §2.2 App. Alg. 2: the
+ * beacons a cycle is scored with stand for every query it collected).  Each
+ * buffer whose count (clamped to [0, B_Q^max - 1] as in bkvo_fps_update)
+ * exceeds n_beacon becomes FPS(buffer, n_beacon), survivors in ascending slot
+ * order, count n_beacon; the others are left alone (sel_out -1s).  With
+ * n_beacon = 0 every non-empty buffer is emptied.                         */
+void bkvo_fps_compress(int nbuf, int qcap, int d, int n_beacon, int n_recent_q,
+                       uint16_t *qbuf, int32_t *qcount, int32_t *sel_out)
+{
+    int bqmax = n_beacon + n_recent_q;
+    int *sel = (int *)malloc(sizeof(int) * (size_t)(bqmax + 1));
+    uint16_t *tmp = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)qcap * d);
+    for (int b = 0; b < nbuf; ++b) {
+        uint16_t *buf = qbuf + (size_t)b * qcap * d;
+        int c = qcount[b];
+        if (c < 0) c = 0;
+        if (c > bqmax - 1) c = bqmax - 1;
+        if (sel_out)
+            for (int i = 0; i < n_beacon; ++i) sel_out[(size_t)b * n_beacon + i] = -1;
+        if (c <= n_beacon) continue;
+        if (n_beacon == 0) { qcount[b] = 0; continue; }
+        int got = bkvo_fps(buf, c, d, n_beacon, sel);
+        if (sel_out)
+            for (int i = 0; i < got; ++i) sel_out[(size_t)b * n_beacon + i] = sel[i];
+        char *keep = (char *)calloc((size_t)c, 1);
+        for (int i = 0; i < got; ++i) keep[sel[i]] = 1;
+        int w = 0;
+        for (int i = 0; i < c; ++i)
+            if (keep[i]) {
+                memcpy(tmp + (size_t)w * d, buf + (size_t)i * d, sizeof(uint16_t) * (size_t)d);
+                ++w;
+            }
+        memcpy(buf, tmp, sizeof(uint16_t) * (size_t)w * d);
+        free(keep);
+        qcount[b] = w;
+    }
+    free(sel);
+    free(tmp);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Other sources of beacons (the ablations of Notes §3.2 Fig. 6 and §3.4
  * Table 3), with the same buffer, count and cycle as continual FPS:
@@ -558,6 +691,11 @@ void bkvo_beacon_update(const bkvo_cfg *c, int nbuf, long long buf0, uint16_t *q
 {
     if (c->beacon_src == BKVO_SRC_FPS) {
         bkvo_fps_update(nbuf, c->qcap, c->d, c->n_beacon, c->n_recent_q, qbuf, qcount, q_new, sel_out);
+        return;
+    }
+    if (c->beacon_src == BKVO_SRC_NAIVE) {   /* the beacons come from the history at each eviction */
+        if (sel_out)
+            for (size_t i = 0; i < (size_t)nbuf * c->n_beacon; ++i) sel_out[i] = -1;
         return;
     }
     for (int b = 0; b < nbuf; ++b) {
@@ -752,7 +890,7 @@ static void merge_unit(const bkvo_cfg *c, int u, uint16_t *qbuf, int32_t *qcount
 {
     int d = c->d, G = c->hq / c->hkv;
     if (c->beacon_src != BKVO_SRC_FPS) {
-        /* initial: nothing changes; random: the recents are offered in ring order */
+        /* initial, naive: nothing changes; random: the recents are offered in ring order */
         for (int h = 0; h < G; ++h) {
             size_t b = (size_t)u * G + h;
             if (c->beacon_src == BKVO_SRC_RANDOM)
@@ -899,9 +1037,20 @@ void bkvo_compact(const bkvo_cfg *cfg, int U, int N, uint16_t *K, uint16_t *V, c
  *      FPS update; in the last n_recent_q steps before the cache is full the
  *      buffers stay frozen (their first rows are the cycle's beacons) and the
  *      query goes to recent slot i = L - (cap - n_recent_q) with its position;
+ *      at the first of these steps a buffer still holding more than n_beacon
+ *      rows is compressed to n_beacon by FPS (bkvo_fps_compress), so that the
+ *      beacons stand for every query the cycle collected;
  *   3. L grows by one; when it reaches cap the unit is evicted with N = cap
  *      and t = this step's position -- scores, keep set, compaction, merge
  *      FPS of beacons and recents -- and L becomes budget.
+ * Naive full-history beacons (beacon_src NAIVE, Notes §3.2 Fig. 7): every
+ * step's query is also appended to its head's history hist [U][G][hcap][d]
+ * (counts hcount [U][G]; a full history takes no more rows), the buffers are
+ * not updated in the collection phase, and at each eviction, before the
+ * scores, each buffer becomes the FPS of its history without the cycle's
+ * n_recent_q recent queries, rows [0, hcount - n_recent_q), taken as the
+ * prefill sampling takes a prompt (bkvo_fps_long; survivors in ascending
+ * history order); the merge leaves it alone.
  * State, in/out, unit-major as for bkvo_evict: K, V [U][cap][d], qbuf
  * [U][G][qcap][d], qcount [U][G], q_recent [U][G][n_recent_q][d],
  * pos_recent [U][n_recent_q]; *L_io is the shared cache length.  idx_hist
@@ -918,9 +1067,19 @@ typedef struct {
     int32_t *idx_hist;
     double *score_hist;
     int max_ev;
+    uint16_t *hist;     /* naive source: query history [U][G][hcap][d] */
+    int32_t *hcount;    /* [U][G] */
+    int hcap;
     int u0, u1;
     int n_ev, L_end;
 } stream_job;
+
+/* Buffer of one head from FPS over the first n rows of its history (the
+ * prefill sampling of bkvo_prefill). */
+static void history_beacons(const bkvo_cfg *c, const uint16_t *hist, int n, uint16_t *buf, int32_t *cnt)
+{
+    bkvo_prefill(1, n, c->d, c->n_beacon, c->qcap, BKVO_SRC_FPS, 0u, 0, hist, buf, cnt, NULL);
+}
 
 static void *run_stream_units(void *arg)
 {
@@ -940,11 +1099,24 @@ static void *run_stream_units(void *arg)
             bkvo_rope_row(J->k_new + su * d, d, c->theta, p, Ku + (size_t)L * d);
             memcpy(Vu + (size_t)L * d, J->v_new + su * d, sizeof(uint16_t) * (size_t)d);
             const uint16_t *qn = J->q_new + su * G * d;
+            if (c->beacon_src == BKVO_SRC_NAIVE)
+                for (int h = 0; h < G; ++h) {
+                    int32_t *hc = J->hcount + (size_t)u * G + h;
+                    int n = *hc < 0 ? 0 : *hc;
+                    if (n < J->hcap) {
+                        memcpy(J->hist + (((size_t)u * G + h) * J->hcap + n) * d, qn + (size_t)h * d,
+                               sizeof(uint16_t) * (size_t)d);
+                        *hc = n + 1;
+                    }
+                }
             if (L < ring0) {
                 bkvo_beacon_update(c, G, global_unit(c, u) * G, J->qbuf + (size_t)u * G * c->qcap * d,
                                    J->qcount + (size_t)u * G, qn, NULL);
             } else {
                 int i = L - ring0;
+                if (i == 0 && c->beacon_src == BKVO_SRC_FPS)   /* freeze */
+                    bkvo_fps_compress(G, c->qcap, d, c->n_beacon, nrq, J->qbuf + (size_t)u * G * c->qcap * d,
+                                      J->qcount + (size_t)u * G, NULL);
                 for (int h = 0; h < G; ++h)
                     memcpy(J->q_recent + (((size_t)u * G + h) * nrq + i) * d, qn + (size_t)h * d,
                            sizeof(uint16_t) * (size_t)d);
@@ -953,6 +1125,13 @@ static void *run_stream_units(void *arg)
             L += 1;
             if (L == c->cap) {
                 J->t[u] = p;
+                if (c->beacon_src == BKVO_SRC_NAIVE)
+                    for (int h = 0; h < G; ++h) {
+                        size_t b = (size_t)u * G + h;
+                        int n = J->hcount[b] - nrq;
+                        history_beacons(c, J->hist + b * J->hcap * d, n > 0 ? n : 0, J->qbuf + b * c->qcap * d,
+                                        J->qcount + b);
+                    }
                 score_unit(c, c->cap, u, J->K, J->qbuf, J->qcount, J->q_recent, J->pos_recent, J->t, sc);
                 bkvo_select(sc, c->cap, c->budget, c->n_prefix, c->n_recent_kv, ix);
                 compact_rows(Ku, d, c->cap, ix, c->budget);
@@ -980,7 +1159,8 @@ static void *run_stream_units(void *arg)
 int bkvo_stream(const bkvo_cfg *cfg, int U, int S, const uint16_t *k_new, const uint16_t *v_new,
                 const uint16_t *q_new, const int32_t *pos, uint16_t *K, uint16_t *V, int32_t *L_io,
                 uint16_t *qbuf, int32_t *qcount, uint16_t *q_recent, int32_t *pos_recent,
-                int32_t *idx_hist, double *score_hist, int max_ev, int nthreads)
+                int32_t *idx_hist, double *score_hist, int max_ev, uint16_t *hist, int32_t *hcount, int hcap,
+                int nthreads)
 {
     if (U <= 0) return 0;
     if (nthreads < 1) nthreads = 1;
@@ -996,6 +1176,7 @@ int bkvo_stream(const bkvo_cfg *cfg, int U, int S, const uint16_t *k_new, const 
         J->K = K; J->V = V; J->qbuf = qbuf; J->q_recent = q_recent;
         J->qcount = qcount; J->pos_recent = pos_recent; J->t = t;
         J->idx_hist = idx_hist; J->score_hist = score_hist; J->max_ev = max_ev;
+        J->hist = hist; J->hcount = hcount; J->hcap = hcap;
         J->u0 = (int)((long)U * i / nthreads);
         J->u1 = (int)((long)U * (i + 1) / nthreads);
         J->L_end = J->L0;

@@ -2,6 +2,9 @@
 the same seeded inputs, and compare element by element."""
 from __future__ import annotations
 
+import math
+import time
+
 import numpy as np
 import torch
 
@@ -14,6 +17,30 @@ SCORE_RTOL = 1e-4        # relative score tolerance
 SCORE_ATOL = 1e-30       # floor for scores that underflow
 TIE_BAND_ABS = 1e-6      # keys within this of the k-th score may swap
 TIE_BAND_REL = 2e-4      # ... and only if within twice the score tolerance
+
+
+def fps_band(d: int, n: int) -> float:
+    """Largest fp64 regret a pick of the fp32 FPS may show against the plain definition.
+
+    With u = 2^-24 and gamma_k ~= k u, the fp32 cosine dot_ij / (nrm_i nrm_j) of bf16 rows (exact products,
+    a d-term fma chain, two square roots, a product and a division) is within 2 gamma_d + 4u of the real
+    cosine; the mean cosine of the prefill seed, u_i . (pairwise sum of the unit rows) / n, is within
+    2 gamma_d + gamma_ceil(log2 n) + 7u of its real value (each bound uses |u_i . u_j| <= 1).  A greedy
+    value S_j is a maximum of cosines, so it carries the cosine bound.  When the fp32 pick r and the real
+    optimum r* differ, S32[r] <= S32[r*] gives S[r] - S[r*] <= twice the bound.  The band is that, with
+    three u to spare for the fp64 reference's own rounding."""
+    lg = max(1, math.ceil(math.log2(max(n, 2))))
+    return 2.0 * (2 * d + lg + 10) * 2.0 ** -24
+
+
+def on_threads(fn, n: int, nthreads: int | None = None) -> None:
+    """fn(slice) over [0, n) cut into contiguous slices, one per host thread (for oracle calls, which release
+    the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    nt = max(1, min(n, nthreads or O.default_threads()))
+    cuts = [i * n // nt for i in range(nt + 1)]
+    with ThreadPoolExecutor(nt) as ex:
+        list(ex.map(fn, [slice(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]))
 
 
 def ocfg(cfg: EvictConfig, n_len: int | None = None, flags: int | None = None) -> O.OracleCfg:
@@ -64,19 +91,25 @@ def check_keep(idx_gpu: np.ndarray, idx_orc: np.ndarray, s_orc: np.ndarray, n_le
     if n_len <= budget:
         assert np.array_equal(g, np.arange(n_len)), where
         return 0
-    forced = set(range(min(n_prefix, n_len))) | set(range(max(0, n_len - n_recent_kv), n_len))
-    gs, os_ = set(g.tolist()), set(o.tolist())
-    assert forced <= gs, f"{where}: forced keeps missing"
-    chosen = [j for j in os_ if j not in forced]
-    if not chosen:
-        assert gs == os_, where
+    forced = np.zeros(n_len, bool)
+    forced[:min(n_prefix, n_len)] = True
+    forced[max(0, n_len - n_recent_kv):] = True
+    gm = np.zeros(n_len, bool)
+    gm[g] = True
+    om = np.zeros(n_len, bool)
+    om[o] = True
+    assert gm[forced].all(), f"{where}: forced keeps missing"
+    chosen = om & ~forced
+    if not chosen.any():
+        assert np.array_equal(gm, om), where
         return 0
-    sk = min(s_orc[j] for j in chosen)
-    diff = gs ^ os_
-    for j in diff:
-        dj = abs(s_orc[j] - sk)
-        assert dj <= TIE_BAND_ABS and dj <= TIE_BAND_REL * sk + SCORE_ATOL, \
-            f"{where}: key {j} kept differently with score {s_orc[j]!r} vs k-th {sk!r}"
+    sk = s_orc[chosen].min()
+    diff = np.flatnonzero(gm ^ om)
+    dj = np.abs(s_orc[diff] - sk)
+    bad = (dj > TIE_BAND_ABS) | (dj > TIE_BAND_REL * sk + SCORE_ATOL)
+    if bad.any():
+        j = diff[np.argmax(bad)]
+        raise AssertionError(f"{where}: key {j} kept differently with score {s_orc[j]!r} vs k-th {sk!r}")
     return len(diff) // 2
 
 
@@ -106,8 +139,10 @@ def compare_evict(cfg: EvictConfig, inp: dict, out: dict, n_len: int, units=None
     oc = ocfg(cfg, n_len=inp["K"].shape[-2], flags=flags)
     oc.unit_ids = units   # the random history's draws are keyed by the global buffer index
     K0, V0 = v["K"].copy(), v["V"].copy()
+    t0 = time.perf_counter()
     o = O.evict(oc, v["K"], v["V"], v["qbuf"], v["qcount"], v["q_recent"], v["pos_recent"], v["t"],
                 n_len=n_len)
+    t_oracle = time.perf_counter() - t0
     ut = torch.tensor(units, dtype=torch.long, device="cuda")
     G, D = cfg.G, cfg.d
     g_scores = out["scores"].index_select(0, ut).cpu().numpy()
@@ -121,17 +156,44 @@ def compare_evict(cfg: EvictConfig, inp: dict, out: dict, n_len: int, units=None
     n_diff = 0
     B = min(cfg.budget, n_len)
     for k, u in enumerate(units):
-        w = f"{where} unit {u}"
         n_diff += check_keep(g_idx[k], o["idx"][k], o["scores"][k], n_len, cfg.budget, cfg.n_prefix,
-                             cfg.n_recent_kv, w)
-        gi = g_idx[k][:B]
-        assert np.array_equal(g_K[k, :B], K0[k][gi]), f"{w}: K rows differ from the gather"
-        assert np.array_equal(g_V[k, :B], V0[k][gi]), f"{w}: V rows differ from the gather"
-        if np.array_equal(gi, o["idx"][k][:B]):
-            assert np.array_equal(g_K[k, :B], v["K"][k, :B]) and np.array_equal(g_V[k, :B], v["V"][k, :B])
-        assert np.array_equal(g_qc[k], v["qcount"][k]), f"{w}: qcount"
-        assert np.array_equal(g_sel[k], o["fps_sel"][k]), f"{w}: merge FPS selection"
-        for h in range(G):
-            n = int(v["qcount"][k, h])
-            assert np.array_equal(g_qbuf[k, h, :n], v["qbuf"][k, h, :n]), f"{w} head {h}: merged buffer"
-    return {"n_tie_diff": n_diff, "oracle": o}
+                             cfg.n_recent_kv, f"{where} unit {u}")
+    # compacted rows: byte-identical to the gather of the original rows by the GPU's own keep set, which
+    # equals the oracle's compaction wherever the two keep sets agree
+    gi = g_idx[:, :B]
+    _first_bad(g_K[:, :B] == np.take_along_axis(K0, gi[:, :, None], axis=1), units, f"{where}: K rows differ "
+               "from the gather")
+    _first_bad(g_V[:, :B] == np.take_along_axis(V0, gi[:, :, None], axis=1), units, f"{where}: V rows differ "
+               "from the gather")
+    same = (gi == o["idx"][:, :B]).all(axis=1)
+    _first_bad((g_K[same, :B] == v["K"][same, :B]), [u for u, s_ in zip(units, same) if s_], f"{where}: K vs oracle")
+    _first_bad((g_V[same, :B] == v["V"][same, :B]), [u for u, s_ in zip(units, same) if s_], f"{where}: V vs oracle")
+    # merged buffers: counts, selections and the live rows bit-exact
+    _first_bad(g_qc == v["qcount"], units, f"{where}: qcount")
+    _first_bad(g_sel == o["fps_sel"], units, f"{where}: merge FPS selection")
+    live = np.arange(cfg.qcap)[None, None, :, None] < v["qcount"][:, :, None, None]
+    _first_bad(np.where(live, g_qbuf, 0) == np.where(live, v["qbuf"], 0), units, f"{where}: merged buffer")
+    return {"n_tie_diff": n_diff, "oracle": o, "oracle_s": t_oracle, "units": len(units)}
+
+
+def _first_bad(eq: np.ndarray, units, what: str) -> None:
+    """Raise naming the first unit whose entries of eq (unit-major) are not all true."""
+    if eq.shape[0] == 0:
+        return
+    ok = eq.reshape(eq.shape[0], -1).all(axis=1) if eq.ndim > 1 else eq
+    if not ok.all():
+        k = int(np.argmin(ok))
+        raise AssertionError(f"{what} (unit {units[k]}; {int((~ok).sum())} units differ)")
+
+
+def compare_evict_all(cfg: EvictConfig, inp: dict, out: dict, n_len: int, units=None, flags: int | None = None,
+                      where: str = "", chunk: int = 512) -> dict:
+    """compare_evict over every listed unit (default: all of the workload's), a chunk of units at a time so
+    that the host copies stay bounded.  Returns the totals: tie-band differences, units, oracle seconds."""
+    units = list(range(cfg.units)) if units is None else list(units)
+    tot = {"n_tie_diff": 0, "units": 0, "oracle_s": 0.0}
+    for c0 in range(0, len(units), chunk):
+        r = compare_evict(cfg, inp, out, n_len, units=units[c0:c0 + chunk], flags=flags, where=where)
+        for k in tot:
+            tot[k] += r[k]
+    return tot

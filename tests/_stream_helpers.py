@@ -17,26 +17,32 @@ def stream_ocfg(scfg: StreamConfig, units=None) -> O.OracleCfg:
     return O.OracleCfg(hq=b.hq, hkv=b.hkv, d=b.d, cap=b.cap, budget=b.budget, n_prefix=b.n_prefix,
                        n_recent_kv=b.n_recent_kv, n_beacon=b.n_beacon, n_recent_q=b.n_recent_q, theta=b.theta,
                        qcap=b.qcap, pool_mean=int(b.pool == "mean"),
-                       beacon_src={"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM}[b.beacon],
+                       beacon_src={"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM,
+                                   "naive": O.SRC_NAIVE}[b.beacon],
                        seed=b.seed & 0xFFFFFFFF, n_layers=b.n_layers, batch=b.batch,
                        unit_ids=None if units is None else list(units))
 
 
-def empty_state(scfg: StreamConfig, U: int) -> dict:
+def empty_state(scfg: StreamConfig, U: int, hcap: int = 0) -> dict:
     b = scfg.base
     G, d = b.G, b.d
-    return {"K": np.zeros((U, b.cap, d), np.uint16), "V": np.zeros((U, b.cap, d), np.uint16),
-            "qbuf": np.zeros((U, G, b.qcap, d), np.uint16), "qcount": np.zeros((U, G), np.int32),
-            "q_recent": np.zeros((U, G, b.n_recent_q, d), np.uint16),
-            "pos_recent": np.zeros((U, b.n_recent_q), np.int32)}
+    st = {"K": np.zeros((U, b.cap, d), np.uint16), "V": np.zeros((U, b.cap, d), np.uint16),
+          "qbuf": np.zeros((U, G, b.qcap, d), np.uint16), "qcount": np.zeros((U, G), np.int32),
+          "q_recent": np.zeros((U, G, b.n_recent_q, d), np.uint16),
+          "pos_recent": np.zeros((U, b.n_recent_q), np.int32)}
+    if b.beacon == "naive":   # the whole query history of every head
+        st["hist"] = np.zeros((U, G, hcap, d), np.uint16)
+        st["hcount"] = np.zeros((U, G), np.int32)
+    return st
 
 
 def replay(scfg: StreamConfig, k_new, v_new, q_new, pos, max_ev: int, nthreads=None, units=None) -> dict:
     """Oracle stream from an empty state over step-major inputs of U units (units: their global indices,
     when they are a sample of the workload's)."""
-    st = empty_state(scfg, pos.shape[1])
+    st = empty_state(scfg, pos.shape[1], hcap=pos.shape[0])
     o = O.stream(stream_ocfg(scfg, units), k_new, v_new, q_new, pos, st["K"], st["V"], 0, st["qbuf"], st["qcount"],
-                 st["q_recent"], st["pos_recent"], max_ev=max_ev, nthreads=nthreads)
+                 st["q_recent"], st["pos_recent"], max_ev=max_ev, nthreads=nthreads, hist=st.get("hist"),
+                 hcount=st.get("hcount"))
     o.update(st)
     return o
 

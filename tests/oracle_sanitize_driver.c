@@ -59,9 +59,16 @@ static void run_case(int hq, int hkv, int d, int N, int budget, int npf, int nrk
     bkvo_fps_f64(qbuf, 32, d, nb, sel32, mar);
     bkvo_fps(qbuf, 1, d, 1, sel32);
     bkvo_fps(qbuf, 5, d, 0, sel32);
+    double reg[33];
+    bkvo_fps_plain(qbuf, 32, d, nb, NULL, sel32, reg, mar);
+    bkvo_fps_plain(qbuf, 32, d, nb, sel32, sel32, reg, NULL);
+    bkvo_fps_plain(qbuf, 3, d, 5, NULL, sel32, NULL, NULL);
+    for (int i = 0; i < U * G; ++i) qc[i] = (i % (nb + nrq + 3)) - 1;
+    bkvo_fps_compress(U * G, c.qcap, d, nb, nrq, qbuf, qc, sel);
+    bkvo_fps_compress(U * G, c.qcap, d, 0, nrq, qbuf, qc, NULL);
 
     /* a short stream from an empty cache, under each source of beacons */
-    for (int src = 0; src < 3 && S > 0; ++src) {
+    for (int src = 0; src < 4 && S > 0; ++src) {
         c.beacon_src = src;
         c.seed = 99u;
         uint16_t *kn = malloc((size_t)S * U * d * 2), *vn = malloc((size_t)S * U * d * 2);
@@ -74,8 +81,11 @@ static void run_case(int hq, int hkv, int d, int N, int budget, int npf, int nrk
         int32_t L = 0;
         int32_t *ih = malloc(sizeof(int32_t) * 4 * U * (budget > 0 ? budget : 1));
         double *sh = malloc(sizeof(double) * 4 * U * N);
-        bkvo_stream(&c, U, S, kn, vn, qs, ps, K, V, &L, qbuf, qc, qr, pos, ih, sh, 4, 2);
-        free(kn); free(vn); free(qs); free(ps); free(ih); free(sh);
+        int hcap = S;
+        uint16_t *hist = malloc((size_t)U * G * hcap * d * 2);
+        int32_t *hc = calloc((size_t)U * G, sizeof(int32_t));
+        bkvo_stream(&c, U, S, kn, vn, qs, ps, K, V, &L, qbuf, qc, qr, pos, ih, sh, 4, hist, hc, hcap, 2);
+        free(kn); free(vn); free(qs); free(ps); free(ih); free(sh); free(hist); free(hc);
     }
     free(K); free(V); free(qbuf); free(qr); free(qc); free(pos); free(t); free(idx); free(sc);
     free(moved); free(sel); free(qn);

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(so):
 
 
 def test_version_and_strerror(so):
-    assert L.version() == 4
+    assert L.version() == 5
     for code in (0, -1, -2, -3, -4):
         assert len(L.strerror(code)) > 0
     assert L.strerror(-99) == "unknown error"
@@ -85,7 +85,8 @@ MISALIGNED = C.c_void_p(0x10002)
 
 @pytest.mark.parametrize("field,value,code", [
     ("head_dim", 96, -2), ("n_q_heads", 5, -1), ("n_kv_heads", 0, -1), ("n_q_heads", 18, -2),
-    ("n_beacon", 20, -2), ("qcap", 16, -1), ("flags", 16, -1), ("flags", 12, -1), ("cap", 0, -1),
+    ("n_beacon", 20, -2), ("qcap", 16, -1), ("flags", 32, -1), ("flags", 12, -1), ("flags", 20, -1),
+    ("flags", 24, -1), ("cap", 0, -1),
     ("n_beacon", -1, -1),
 ])
 def test_shape_validation(so, field, value, code):
@@ -130,6 +131,28 @@ def test_prefill_validation(so):
     assert so.bkv_fps_prefill(C.byref(s), FAKE, 10, None, FAKE, None, None) == -1
     assert so.bkv_fps_prefill(C.byref(s), FAKE, 10, FAKE, FAKE, MISALIGNED, None) == -1
     assert so.bkv_fps_prefill(C.byref(_shape(n_beacon=20)), FAKE, 10, FAKE, FAKE, None, None) == -2
+
+
+def test_history_compress_and_workspace_validation(so):
+    s = _shape()
+    # bkv_fps_history: rows within [0, hcap], at most the longest prompt, its pointers
+    assert so.bkv_fps_history(C.byref(s), FAKE, 100, 101, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_history(C.byref(s), FAKE, 100, -1, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_history(C.byref(s), FAKE, -1, 0, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_history(C.byref(s), FAKE, 9000, 8193, FAKE, FAKE, None, None) == -2
+    assert so.bkv_fps_history(C.byref(s), None, 100, 10, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_history(C.byref(s), MISALIGNED, 100, 10, FAKE, FAKE, None, None) == -1
+    assert so.bkv_fps_history(C.byref(s), FAKE, 100, 10, FAKE, FAKE, MISALIGNED, None) == -1
+    # bkv_history_append and bkv_fps_compress: pointers and capacity
+    assert so.bkv_history_append(C.byref(s), FAKE, -1, FAKE, FAKE, None) == -1
+    assert so.bkv_history_append(C.byref(s), None, 10, FAKE, FAKE, None) == -1
+    assert so.bkv_history_append(C.byref(s), FAKE, 10, FAKE, MISALIGNED, None) == -1
+    assert so.bkv_fps_compress(C.byref(s), None, FAKE, None, None) == -1
+    assert so.bkv_fps_compress(C.byref(s), MISALIGNED, FAKE, None, None) == -1
+    assert so.bkv_fps_compress(C.byref(_shape(head_dim=96)), FAKE, FAKE, None, None) == -2
+    # no call needs a workspace
+    for cfg in EVICT_CONFIGS.values():
+        assert L.workspace_bytes(L.shape_of(cfg), cfg.n_len) == 0
 
 
 def test_attention_and_append_validation(so):

@@ -29,6 +29,12 @@ def test_bench_eviction_tiny():
     rf = b["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
+    assert 0 < rf["strict"]["frac"] <= rf["frac"]
+    assert b["timing"] == "pristine" and abs(b["value"] - b["pristine"]["steps_per_s"]) < 1e-9
+    assert b["back_to_back"]["steps_per_s"] > 0
+    (bb,) = _bench("--config", "tiny", "--steps", "3", "--warmup", "1", "--timing", "back-to-back",
+                   "--no-cpu-baseline")
+    assert bb["timing"] == "back-to-back" and abs(bb["value"] - bb["back_to_back"]["steps_per_s"]) < 1e-9
     cb = b["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert b["copy_reference"]["GBs"] > 0

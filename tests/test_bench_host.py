@@ -33,6 +33,8 @@ def test_alg_bytes_hand_example():
     assert a["compact"] == 4 * 5 * row              # K and V, each read and written
     assert a["buffers"] == 4 * cfg.n_beacon * row
     assert a["total"] == a["k_read"] + a["q_read"] + a["compact"] + a["buffers"]
+    # every key read once: the moved key rows are not read a second time
+    assert a["total_strict"] == a["k_read"] + a["q_read"] + 3 * 5 * row + a["buffers"]
 
 
 def test_qkt_flops_match_the_counted_mfmas():
@@ -60,20 +62,24 @@ def _tree_copy(tmp_path):
 
 def test_source_hash_follows_includes(tmp_path, monkeypatch):
     """The hash that validates a stored traffic figure changes with any header the kernel includes,
-    directly or not, and with the build script; it ignores files the kernel does not include."""
+    directly or not, and with the compile flags; it ignores files the kernel does not include."""
     dst = _tree_copy(tmp_path)
     monkeypatch.setattr(bench, "HERE", str(dst))
     h0 = bench.kernel_sources_sha256("evict_kernel")
     assert h0 == bench.kernel_sources_sha256("evict_kernel")
     (dst / "long_reasoning_decode_amd" / "csrc" / "bkv_attention.hip").write_text("// not included\n")
     assert bench.kernel_sources_sha256("evict_kernel") == h0
-    for rel in ("long_reasoning_decode_amd/csrc/bkv_device.hpp", "include/bkv.h", "long_reasoning_decode_amd/build.py"):
+    for rel in ("long_reasoning_decode_amd/csrc/bkv_device.hpp", "include/bkv.h"):
         p = dst / rel
         text = p.read_text()
         p.write_text(text + "\n// changed\n")
         assert bench.kernel_sources_sha256("evict_kernel") != h0, rel
         p.write_text(text)
     assert bench.kernel_sources_sha256("evict_kernel") == h0
+    from long_reasoning_decode_amd import build as lib_build
+    flags = lib_build.device_flags()
+    monkeypatch.setattr(lib_build, "device_flags", lambda arch="gfx950": flags + ["-O2"])
+    assert bench.kernel_sources_sha256("evict_kernel") != h0
 
 
 def test_stored_traffic_lookup(tmp_path, monkeypatch):

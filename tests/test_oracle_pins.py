@@ -288,6 +288,97 @@ def test_fps_long_equals_buffer_fps_away_from_ties():
     assert checked > 150
 
 
+@pytest.mark.parametrize("case", _read_fps_cases(), ids=lambda c: c["name"])
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_fps_plain_hand_cases(case, d):
+    sel, regret, _ = O.fps_plain(rows(case["rows"], d), case["m"])
+    assert sel == case["order"] and not regret.any()
+
+
+def test_fps_plain_equals_brute_force():
+    """The plain fp64 FPS is the definition: a from-scratch numpy recomputation at every step picks the
+    same rows (margins below 1e-9 aside, where fp64 rounding decides), and its reported margins agree.  With
+    no more rows than picks nothing is sampled: the selection is every row in order."""
+    rng = np.random.default_rng(34)
+    X = bf16(rng.standard_normal((9, 16)))
+    for m in (9, 12):
+        sel, regret, mar = O.fps_plain(X, m)
+        assert sel == list(range(9)) and not regret.any() and np.isinf(mar).all()
+    checked = 0
+    for trial in range(120):
+        n = int(rng.integers(2, 90))
+        d = int(rng.choice([4, 8, 64, 128]))
+        m = int(rng.integers(1, n))
+        X = bf16(rng.standard_normal((n, d)) * rng.uniform(0.1, 10))
+        ref, margin = _fps_brute(X, m)
+        sel, regret, mar = O.fps_plain(X, m)
+        assert not regret.any()
+        if margin < 1e-9:
+            continue
+        assert sel == ref, (trial, n, d, m)
+        assert abs(mar.min() - margin) <= 1e-9 * max(1.0, abs(margin))
+        checked += 1
+    assert checked > 100
+
+
+def test_fps_plain_replay_regret():
+    """Replaying picks: its own picks have zero regret; a wrong pick's regret is its value minus the best
+    value, both recomputed here from the definition; taken or out-of-range picks read as infinite."""
+    rng = np.random.default_rng(35)
+    n, d, m = 40, 64, 10
+    X = bf16(rng.standard_normal((n, d)))
+    sel, _, _ = O.fps_plain(X, m)
+    s2, reg, _ = O.fps_plain(X, m, forced=sel)
+    assert s2 == sel and not reg.any()
+    x = f32(X).astype(np.float64)
+    nr = np.linalg.norm(x, axis=1)
+    cs = (x @ x.T) / np.outer(nr, nr)
+    for step in (0, 1, 5):
+        forced = list(sel)
+        taken = sel[:step]
+        if step == 0:
+            vals = cs.mean(axis=1)
+        else:
+            vals = np.array([cs[j, taken].max() for j in range(n)])
+        cand = [j for j in range(n) if j not in taken]
+        alt = max(cand, key=lambda j: vals[j])      # the worst row to take
+        forced[step] = alt
+        _, reg, _ = O.fps_plain(X, m, forced=forced)
+        assert not reg[:step].any()
+        assert abs(reg[step] - (vals[alt] - min(vals[j] for j in cand))) <= 1e-12
+        assert reg[step] > 0
+    bad = list(sel)
+    bad[3] = sel[1]
+    assert np.isinf(O.fps_plain(X, m, forced=bad)[1][3])
+    bad[3] = n
+    assert np.isinf(O.fps_plain(X, m, forced=bad)[1][3])
+
+
+def test_fps_long_within_band_of_plain_definition():
+    """The fp32 prefill FPS (the canonical order the kernel follows) against the plain fp64 definition on
+    prompts of hundreds to thousands of rows: replayed step by step, every pick's regret is within the band
+    derived from fp32 rounding, and most picks are the optimum itself."""
+    from _helpers import fps_band
+    rng = np.random.default_rng(36)
+    steps = optimal = 0
+    for trial in range(10):
+        n = int(rng.choice([100, 300, 1024, 2000]))
+        d = int(rng.choice([64, 128]))
+        m = 16
+        c = rng.standard_normal((8, d))
+        X = rng.standard_normal((n, d))
+        clus = rng.random(n) < 0.3
+        X[clus] = c[rng.integers(0, 8, clus.sum())] * np.sqrt(d) / np.linalg.norm(c, axis=1).mean()
+        X = bf16(X)
+        sel = O.fps_long(X, m)
+        _, reg, mar = O.fps_plain(X, m, forced=sel)
+        band = fps_band(d, n)
+        assert (reg <= band).all(), (trial, n, d, reg.max(), band)
+        steps += len(reg)
+        optimal += int((reg == 0).sum())
+    assert optimal >= 0.95 * steps
+
+
 def test_fps_long_scaling_clusters_and_duplicates():
     rng = np.random.default_rng(33)
     n, d, m = 700, 128, 16

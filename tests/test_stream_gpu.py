@@ -8,8 +8,11 @@ import torch
 
 from long_reasoning_decode_amd import lib as L
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import (STREAM, STREAM_SOURCES, STREAM_SPLITS, TINY_STREAM, TINY_STREAM_MEAN,
-                                               TINY_STREAM_SOURCES, TINY_STREAM_SPLITS)
+from dataclasses import replace
+
+from long_reasoning_decode_amd.configs import (STREAM, STREAM_NAIVE, STREAM_SOURCES, STREAM_SPLITS, TINY_STREAM,
+                                               TINY_STREAM_MEAN, TINY_STREAM_NAIVE, TINY_STREAM_SOURCES,
+                                               TINY_STREAM_SPLITS)
 from long_reasoning_decode_amd.stream import StreamRun
 
 from _stream_helpers import compare_stream, replay
@@ -93,6 +96,46 @@ def test_stream_tiny_mean_pooling():
     _check(scfg, run, units, "stream-tiny mean")
 
 
+def test_stream_tiny_naive_history():
+    """Naive full-history beacons: every query of every head kept, the beacons sampled from the whole history
+    at each eviction, against the oracle's replay (which samples them with the prefill FPS)."""
+    scfg = TINY_STREAM_NAIVE
+    units = range(scfg.base.units)
+    run = StreamRun(scfg, record_units=units, block=64)
+    run.run()
+    assert run.h_rows == scfg.steps and int(run.hcount.min()) == int(run.hcount.max()) == scfg.steps
+    _check(scfg, run, units, "stream-tiny naive")
+
+
+@pytest.mark.parametrize("n_new", [40, 23])
+def test_stream_tiny_collection_not_a_multiple(n_new):
+    """Cycles whose collection phase (n_new - n_recent_q steps) is not a multiple of n_recent_q: at the freeze
+    point the buffers hold more than n_beacon rows and are compressed, so no collected query is dropped; the
+    oracle's replay does the same."""
+    scfg = replace(TINY_STREAM, name=f"stream-tiny-new{n_new}", steps=500,
+                   base=replace(TINY_STREAM.base, n_new=n_new, seed=20261202 + 600 + n_new))
+    b = scfg.base
+    assert (b.n_new - b.n_recent_q) % b.n_recent_q != 0
+    units = range(b.units)
+    run = StreamRun(scfg, record_units=units, block=64)
+    run.run()
+    _check(scfg, run, units, scfg.name)
+
+
+def test_stream_naive_qwen3_4b_sampled_units():
+    """The naive full-history stream at its benchmark shape (Qwen3-4B, batch 16) for the first three
+    evictions, checked on units spread over layers, batch elements and KV heads."""
+    scfg = STREAM_NAIVE
+    b = scfg.base
+    steps = b.cap + 2 * b.n_new
+    units = [0, b.units - 1, 9 * b.batch * b.hkv + 5 * b.hkv + 2, 31 * b.batch * b.hkv + 12 * b.hkv + 7]
+    run = StreamRun(scfg, record_units=units)
+    r = run.run(steps)
+    assert r["evictions"] == scfg.evictions(steps) == 3
+    res = _check(scfg, run, units, "stream-qwen3-4b-naive b16", nthreads=len(units))
+    assert len(res["diverged"]) <= 2
+
+
 def test_stream_checkpoint_resume(tmp_path):
     """Stopping at a step, saving the state to a file and resuming in a fresh stream object gives the
     same stream, bit for bit, as running straight through."""
@@ -106,7 +149,7 @@ def test_stream_checkpoint_resume(tmp_path):
     c.load_state_dict(torch.load(tmp_path / "stream.pt", weights_only=True))
     c.run(335)
     assert (c.L, c.n_ev, c.steps_done) == (a.L, a.n_ev, a.steps_done)
-    for k in StreamRun._STATE:
+    for k in a._STATE:
         assert torch.equal(getattr(c, k), getattr(a, k)), k
 
 

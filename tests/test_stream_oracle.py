@@ -9,7 +9,7 @@ import pytest
 
 import oracle as O
 from long_reasoning_decode_amd import synth
-from long_reasoning_decode_amd.configs import (TINY_STREAM, TINY_STREAM_MEAN, TINY_STREAM_SOURCES,
+from long_reasoning_decode_amd.configs import (TINY_STREAM, TINY_STREAM_MEAN, TINY_STREAM_NAIVE, TINY_STREAM_SOURCES,
                                                TINY_STREAM_SPLITS)
 
 from _stream_helpers import empty_state, replay, stream_ocfg
@@ -27,8 +27,8 @@ def _inputs(scfg, S, seed=None):
             "pos": np.ascontiguousarray(blk["pos"].numpy()[:, b_of]).astype(np.int32)}
 
 
-@pytest.mark.parametrize("scfg", (TINY_STREAM, TINY_STREAM_MEAN) + TINY_STREAM_SPLITS + TINY_STREAM_SOURCES,
-                         ids=lambda c: c.name)
+@pytest.mark.parametrize("scfg", (TINY_STREAM, TINY_STREAM_MEAN, TINY_STREAM_NAIVE) + TINY_STREAM_SPLITS
+                         + TINY_STREAM_SOURCES, ids=lambda c: c.name)
 def test_stream_equals_composition_of_calls(scfg):
     b = scfg.base
     S = 260    # first eviction after 160 steps, then every 32
@@ -36,21 +36,32 @@ def test_stream_equals_composition_of_calls(scfg):
     U = b.units
     o = replay(scfg, x["k_new"], x["v_new"], x["q_new"], x["pos"], max_ev=8, nthreads=2)
 
-    st = empty_state(scfg, U)
+    st = empty_state(scfg, U, hcap=S)
+    naive = b.beacon == "naive"
     oc = stream_ocfg(scfg)
     ring0 = b.cap - b.n_recent_q
     L, idx_hist, sc_hist = 0, [], []
     for s in range(S):
         for u in range(U):
+            if naive:   # every query joins its head's history
+                st["hist"][u, :, s] = x["q_new"][s, u]
+                st["hcount"][u] += 1
             st["K"][u, L] = O.rope_row(x["k_new"][s, u], b.theta, int(x["pos"][s, u]))
             st["V"][u, L] = x["v_new"][s, u]
             if L < ring0:
                 O.beacon_update(oc, st["qbuf"][u], st["qcount"][u], x["q_new"][s, u], buf0=u * b.G)
             else:
+                if L == ring0 and b.beacon == "fps":   # freeze: the beacons stand for every collected query
+                    O.fps_compress(st["qbuf"][u], st["qcount"][u], b.n_beacon, b.n_recent_q)
                 st["q_recent"][u, :, L - ring0] = x["q_new"][s, u]
                 st["pos_recent"][u, L - ring0] = x["pos"][s, u]
         L += 1
         if L == b.cap:
+            if naive:   # the beacons: prefill sampling of each history, less the cycle's recent queries
+                n = s + 1 - b.n_recent_q
+                qb = st["qbuf"].reshape(U * b.G, b.qcap, b.d)
+                qc = st["qcount"].reshape(U * b.G)
+                O.prefill(np.ascontiguousarray(st["hist"].reshape(U * b.G, S, b.d)[:, :n]), qb, qc, b.n_beacon)
             r = O.evict(oc, st["K"], st["V"], st["qbuf"], st["qcount"], st["q_recent"], st["pos_recent"],
                         x["pos"][s].copy(), nthreads=2)
             idx_hist.append(r["idx"])
@@ -63,7 +74,7 @@ def test_stream_equals_composition_of_calls(scfg):
     assert np.array_equal(np.stack(sc_hist), o["scores"][:E])
     for k in ("K", "V"):
         assert np.array_equal(st[k][:, :L], o[k][:, :L]), k
-    for k in ("qbuf", "qcount", "q_recent", "pos_recent"):
+    for k in ("qbuf", "qcount", "q_recent", "pos_recent") + (("hist", "hcount") if naive else ()):
         assert np.array_equal(st[k], o[k]), k
 
 
@@ -151,6 +162,11 @@ def test_fps_round_count_matches_the_oracle_cycle(scfg):
                 if u == 0 and int(st["qcount"][0, 0]) < before + 1:
                     rounds += 1
             else:
+                if L == ring0:   # freeze: a buffer holding more than n_beacon rows is sampled once more
+                    before = int(st["qcount"][u, 0])
+                    O.fps_compress(st["qbuf"][u], st["qcount"][u], b.n_beacon, b.n_recent_q)
+                    if u == 0 and int(st["qcount"][0, 0]) < before:
+                        rounds += 1
                 st["q_recent"][u, :, L - ring0] = x["q_new"][s, u]
                 st["pos_recent"][u, L - ring0] = x["pos"][s, u]
         L += 1
