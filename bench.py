@@ -297,14 +297,17 @@ def stream_cpu_baseline(run, target_s: float = 10.0) -> dict:
 def stream_evict_roofline(run, evict_ms: float) -> dict:
     """HBM roofline of the stream's evictions, its dominant cost: the algorithmic bytes of one steady-state
     eviction (from one more, untimed cycle whose eviction reports its keep sets) over the timed run's mean
-    eviction time (bkv_evict: evict_kernel and the buffer merge)."""
+    eviction time (bkv_evict: evict_kernel and the buffer merge; under the naive source the timed eviction
+    also holds the FPS over every history, which these bytes do not count)."""
     b = run.base
     if run.L != b.budget:                 # advance to the start of a cycle
         run.run(b.cap - run.L)
     run.run(b.n_new, keep_idx=True)
     ab = alg_bytes(b, run.last_qcount.reshape(b.units, b.G).cpu().numpy(), run.idx.cpu().numpy(), b.cap)
     ach = ab["total"] / (evict_ms * 1e-3) / 1e9
-    return {"bound": "hbm", "kernel": "bkv_evict (evict_kernel + merge)", "achieved": ach, "peak": HBM_PEAK_GBS,
+    kern = ("bkv_fps_history + bkv_evict (history FPS, evict_kernel)" if getattr(run, "naive", False)
+            else "bkv_evict (evict_kernel + merge)")
+    return {"bound": "hbm", "kernel": kern, "achieved": ach, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None, "alg_bytes_per_launch": ab["total"],
             "moved_rows_per_unit": ab["moved_rows"] / b.units}
 
