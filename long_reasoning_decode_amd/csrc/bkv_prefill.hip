@@ -44,7 +44,7 @@ struct Pre {
     // LDS layout (bytes)
     static constexpr int kXrOff = 0;                                 // float [2][D]   picked row
     static constexpr int kXnOff = kXrOff + 2 * D * 4;                // float [2]      its norm
-    static constexpr int kWvOff = kXnOff + 16;                       // float [2][waves] wave minima
+    static constexpr int kWvOff = kXnOff + 16;                       // int [2][waves] wave minima (keys)
     static constexpr int kWiOff = kWvOff + 2 * kWaves * 4;           // int   [2][waves]
     static constexpr int kPartOff = kWiOff + 2 * kWaves * 4;         // float [waves][D] wave column sums
     static constexpr int kCsumOff = kPartOff + kWaves * D * 4;       // float [chunks][D]
@@ -184,57 +184,59 @@ __device__ __forceinline__ float wave_pairwise_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ bool less_vi(float v2, int i2, float v, int i) {
-    return v2 < v || (v2 == v && i2 < i);
+constexpr int kNoKey = 0x7FFFFFFF;   // above every candidate's key
+
+// Integer key ordered as the float v, with -0 taken as +0 (v not NaN); a
+// thread with no candidate (i == kNone) gives kNoKey.
+__device__ __forceinline__ int key_of(float v, int i) {
+    const int b = __float_as_int(v + 0.0f);
+    return i == 0x7FFFFFFF ? kNoKey : b ^ ((b >> 31) & 0x7FFFFFFF);
 }
 
 template <int CTRL>
-__device__ __forceinline__ void dpp_argmin(float& v, int& i) {
-    const float v2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-    const int i2 = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
-    const bool take = less_vi(v2, i2, v, i);
-    v = take ? v2 : v;
-    i = take ? i2 : i;
+__device__ __forceinline__ int dpp_min(int k) {
+    return min(k, __builtin_amdgcn_update_dpp(kNoKey, k, CTRL, 0xF, 0xF, false));
 }
 
-// Wave argmin of (v, i) by DPP inside each 16-lane row, then the four row
-// winners compared in order; the result is uniform (held in every lane).
-__device__ __forceinline__ void wave_argmin_dpp(float& v, int& i) {
-    dpp_argmin<0xB1>(v, i);    // quad_perm [1,0,3,2]
-    dpp_argmin<0x4E>(v, i);    // quad_perm [2,3,0,1]
-    dpp_argmin<0x141>(v, i);   // row_half_mirror
-    dpp_argmin<0x140>(v, i);   // row_mirror: every lane of a row holds the row's winner
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int row = 1; row < 4; ++row) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * row));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * row);
-        const bool take = less_vi(rv, ri, bv, bi);
-        bv = take ? rv : bv;
-        bi = take ? ri : bi;
-    }
-    v = bv;
-    i = bi;
+// The minimum of k over the wave, uniform: DPP inside each 16-lane row, then
+// the four rows' minima.
+__device__ __forceinline__ int wave_min(int k) {
+    k = dpp_min<0xB1>(k);    // quad_perm [1,0,3,2]
+    k = dpp_min<0x4E>(k);    // quad_perm [2,3,0,1]
+    k = dpp_min<0x141>(k);   // row_half_mirror
+    k = dpp_min<0x140>(k);   // row_mirror: every lane of a row holds the row's minimum
+    const int a = __builtin_amdgcn_readlane(k, 0), b = __builtin_amdgcn_readlane(k, 16);
+    const int c = __builtin_amdgcn_readlane(k, 32), d = __builtin_amdgcn_readlane(k, 48);
+    return min(min(a, b), min(c, d));
 }
 
-// Workgroup argmin of (v, i); every thread gets the winning index.
-__device__ __forceinline__ int block_argmin(float v, int i, float* wv, int* wi, int wave, int lane) {
-    wave_argmin_dpp(v, i);
+// Workgroup argmin of (v, i), each thread holding its own best row i (kNone:
+// none) and its value v: the lowest row index among the smallest values, in
+// every thread.  Values compare through their order keys, so equal values
+// (+0 and -0 included) go to the lower index.
+__device__ __forceinline__ int block_argmin(float v, int i, int* wk, int* wi, int wave, int lane) {
+    const int k = key_of(v, i);
+    const int m = wave_min(k);
+    const int idx = wave_min(k == m ? i : kNoKey);
     if (lane == 0) {
-        wv[wave] = v;
-        wi[wave] = i;
+        wk[wave] = m;
+        wi[wave] = idx;
     }
     __syncthreads();
-    float bv = wv[0];
-    int bi = wi[0];
+    int kv[kWaves], iv[kWaves];   // every wave's pair read at once, then reduced in registers
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        if (less_vi(wv[w], wi[w], bv, bi)) {
-            bv = wv[w];
-            bi = wi[w];
-        }
-    return bi;
+    for (int w = 0; w < kWaves; w += 4) {
+        const int4 a = *reinterpret_cast<const int4*>(wk + w), b = *reinterpret_cast<const int4*>(wi + w);
+        kv[w] = a.x, kv[w + 1] = a.y, kv[w + 2] = a.z, kv[w + 3] = a.w;
+        iv[w] = b.x, iv[w + 1] = b.y, iv[w + 2] = b.z, iv[w + 3] = b.w;
+    }
+    int gm = kv[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) gm = min(gm, kv[w]);
+    int gi = kNoKey;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) gi = min(gi, kv[w] == gm ? iv[w] : kNoKey);
+    return gi;
 }
 
 // Column sums of one chunk's unit rows u = x * inv into csum[c][0 .. D):
@@ -316,6 +318,16 @@ template <int D>
 __device__ __forceinline__ int lds_slot(int s, int p) {
     constexpr int kPer256 = 256 / (2 * D);   // rows per 256 bytes: 1 (d = 128) or 2 (d = 64)
     return s * (D / 8) + (p ^ ((s / kPer256) & (D / 8 - 1)));
+}
+
+// With every row past the registers in LDS and at most one per thread (the
+// fp32 path), rows are stored piece-major: piece p of row s at slot
+// p * 512 + s.  A wave's 64 lanes read 64 consecutive slots (conflict-free),
+// and the pieces of a row sit at fixed offsets from its first, so no address
+// is computed per piece.
+template <int D, bool F32>
+__device__ __forceinline__ int slot(int s, int p) {
+    return F32 ? p * kThreads + s : lds_slot<D>(s, p);
 }
 
 // Row j = RC * 512 + s outside the registers: from LDS when s < n_lds, else
@@ -451,7 +463,7 @@ __device__ __forceinline__ float fma_lds_row(const u32x4_t* lrows, int s, const 
     const Bf u = Bf::fresh();
     constexpr int NP = D / 8;
     float acc = 0.0f;
-    u32x4_t w = lrows[lds_slot<D>(s, 0)];
+    u32x4_t w = lrows[slot<D, true>(s, 0)];
     f32x4_t ya = *reinterpret_cast<const f32x4_t*>(y);
     f32x4_t yb = *reinterpret_cast<const f32x4_t*>(y + 4);
 #pragma unroll
@@ -459,7 +471,7 @@ __device__ __forceinline__ float fma_lds_row(const u32x4_t* lrows, int s, const 
         u32x4_t nw = w;
         f32x4_t na = ya, nb = yb;
         if (p + 1 < NP) {
-            nw = lrows[lds_slot<D>(s, p + 1)];
+            nw = lrows[slot<D, true>(s, p + 1)];
             na = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1));
             nb = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1) + 4);
         }
@@ -485,9 +497,10 @@ __device__ __forceinline__ float fma_lds_row(const u32x4_t* lrows, int s, const 
     return acc;
 }
 
-// F32: the register-resident rows are kept in fp32 and the LDS rows are
-// streamed piece by piece; only when every row outside the registers is in
-// LDS (no global tier), where the registers allow it.
+// F32: the register-resident rows are kept in fp32 and the LDS rows (at most
+// one per thread, piece-major) are streamed piece by piece; only when every
+// row outside the registers is in LDS (no global tier), where the registers
+// allow it.
 template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     using L = Pre<D>;
@@ -496,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float* xr = reinterpret_cast<float*>(smem + L::kXrOff);
     float* xn = reinterpret_cast<float*>(smem + L::kXnOff);
-    float* wv = reinterpret_cast<float*>(smem + L::kWvOff);
+    int* wk = reinterpret_cast<int*>(smem + L::kWvOff);
     int* wi = reinterpret_cast<int*>(smem + L::kWiOff);
     float* part = reinterpret_cast<float*>(smem + L::kPartOff);
     float* csum = reinterpret_cast<float*>(smem + L::kCsumOff);
@@ -544,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             nst[s] = nr;
             if (s < n_lds) {
 #pragma unroll
-                for (int p = 0; p < D / 8; ++p) lrows[lds_slot<D>(s, p)] = tmp[p];
+                for (int p = 0; p < D / 8; ++p) lrows[slot<D, F32>(s, p)] = tmp[p];
             }
         }
         chunk_colsum<D>(tmp, inv_of(nr), c, part, csum, wave, lane, tid);
@@ -610,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             bi = j;
         }
     }
-    int r = block_argmin(bv, bi, wv, wi, wave, lane);
+    int r = block_argmin(bv, bi, wk, wi, wave, lane);
 
     // ---- greedy steps
     float S[RC];
@@ -640,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                 if constexpr (F32) {   // piece by piece from LDS
 #pragma unroll 1
                     for (int p = 0; p < D / 8; ++p) {
-                        const u32x4_t w = lrows[lds_slot<D>(s, p)];
+                        const u32x4_t w = lrows[slot<D, true>(s, p)];
                         *reinterpret_cast<f32x4_t*>(dst + 8 * p) =
                             f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
                                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
@@ -700,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             }
         }
         const int q = (t + 1) & 1;
-        r = block_argmin(bv, bi, wv + q * kWaves, wi + q * kWaves, wave, lane);
+        r = block_argmin(bv, bi, wk + q * kWaves, wi + q * kWaves, wave, lane);
     }
 
     // ---- survivors in ascending prompt order, the selection order, the count
@@ -726,11 +739,14 @@ hipError_t launch_d(PrefillArgs a, hipStream_t st) {
     if (e != hipSuccess) return e;
     a.lds_bytes = lim < kLdsBytes ? lim : kLdsBytes;
     if ((int)Pre<D>::rows_off(a.P) > a.lds_bytes) return hipErrorInvalidValue;
-    const size_t lds = Pre<D>::bytes(a.P, a.lds_bytes);
-    if (Pre<D>::n_lds_rows(a.P, a.lds_bytes) >= Pre<D>::n_other(a.P))   // no rows re-read from memory
-        hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(a.nbuf), dim3(kThreads), lds, st, a);
+    // fp32 path: every row past the registers in LDS, at most one per thread, in a piece-major area sized
+    // for one row per thread (its slots are p * 512 + s whatever the row count)
+    const size_t f32_lds = (size_t)Pre<D>::rows_off(a.P) + (size_t)kThreads * Pre<D>::kRowBytes;
+    if (Pre<D>::n_other(a.P) <= kThreads && f32_lds <= (size_t)a.lds_bytes)
+        hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(a.nbuf), dim3(kThreads), f32_lds, st, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(a.nbuf), dim3(kThreads), lds, st, a);
+        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(a.nbuf), dim3(kThreads), Pre<D>::bytes(a.P, a.lds_bytes),
+                           st, a);
     return hipGetLastError();
 }
 
