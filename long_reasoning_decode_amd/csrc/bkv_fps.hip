@@ -21,7 +21,7 @@ constexpr int kMergeWavesPerBlock = 4;   // merge
 // kMaxBuffersPerWave at a time, so every wave has the same share (to one
 // buffer) when all of them sample.
 template <int D, bool COMPRESS>
-__global__ __launch_bounds__(64 * kWavesPerBlock, 2) void fps_kernel(FpsArgs a) {
+__global__ __launch_bounds__(64 * kWavesPerBlock, 3) void fps_kernel(FpsArgs a) {
     __shared__ fps::Smem s[kWavesPerBlock];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;

@@ -34,21 +34,47 @@ namespace fps {
 constexpr int kMaxRows = 32;
 constexpr int kHalf = kMaxRows / 2;   // rows per lane of a set: t and t + kHalf
 constexpr int kSets = 4;              // candidate sets per wave, one per 16-lane row
-constexpr int kCStride = kMaxRows + 1;                  // floats per row of a cosine matrix
-constexpr int kSetStride = kMaxRows * kCStride + 16;    // floats per matrix (the pad staggers the sets' banks)
+constexpr int kCStride = kMaxRows + 1;   // floats per row of a half-wave set's cosine matrix (bkv_fps_pair.hpp)
+// A set's symmetric 32 x 32 matrix is kept as three 16 x 16 tiles: rows 0-15 x 0-15 (D0), rows 16-31 x
+// 16-31 (D1), both in full, and rows 0-15 x 16-31 (O, rows padded to 17 floats so that reading a column
+// of it is conflict-free); rows 16-31 x 0-15 are read from O transposed.
+constexpr int kTile = kHalf * kHalf;
+constexpr int kOStride = kHalf + 1;
+constexpr int kSetStride = 2 * kTile + kHalf * kOStride;   // 784 floats per set
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kAhead = 2;   // row groups in flight ahead of the one the Gram is using
+constexpr int kAhead = 2;   // row groups in flight ahead of the one the Gram is using (half-wave sets)
+constexpr int kAhead4 = 1;  // the same for the four-set Gram, whose two rows per lane double the registers
 
 struct Smem {
     alignas(16) float c[kSets * kSetStride];   // per set: the Gram, then the cosines; then the compaction's moves
     float nrm[kSets][kMaxRows];
 };
 
-// Entry (i, j) of set g's matrix.
+// Entry (i, j) of set g's matrix (i, j < 32; (i, j) and (j, i) are the same
+// float when they lie in O or its transpose).
 __device__ __forceinline__ float& cel(Smem& s, int g, int i, int j) {
-    return s.c[g * kSetStride + i * kCStride + j];
+    const int lo_i = i < kHalf, lo_j = j < kHalf;
+    const int ii = i & (kHalf - 1), jj = j & (kHalf - 1);
+    const int idx = (lo_i & lo_j)     ? ii * kHalf + jj
+                    : !(lo_i | lo_j) ? kTile + ii * kHalf + jj
+                    : lo_i           ? 2 * kTile + ii * kOStride + jj
+                                     : 2 * kTile + jj * kOStride + ii;
+    return s.c[g * kSetStride + idx];
+}
+
+// Tiles of set g: D0[i][j] = entry (i, j), D1[i][j] = (16 + i, 16 + j), O[i][j] = (i, 16 + j), i, j < 16.
+__device__ __forceinline__ float* d0_of(Smem& s, int g) { return s.c + g * kSetStride; }
+__device__ __forceinline__ float* d1_of(Smem& s, int g) { return s.c + g * kSetStride + kTile; }
+__device__ __forceinline__ float* o_of(Smem& s, int g) { return s.c + g * kSetStride + 2 * kTile; }
+
+// Entries (r, t) and (r, 16 + t) of set g, for a row r < 32 and t < 16.
+__device__ __forceinline__ void row_pair(Smem& s, int g, int r, int t, float& a, float& b) {
+    const bool lo = r < kHalf;
+    const int rr = r & (kHalf - 1);
+    a = lo ? d0_of(s, g)[rr * kHalf + t] : o_of(s, g)[t * kOStride + rr];
+    b = lo ? o_of(s, g)[rr * kOStride + t] : d1_of(s, g)[rr * kHalf + t];
 }
 
 // The wave's LDS writes are complete and visible to its other lanes; the
@@ -94,9 +120,9 @@ __device__ __forceinline__ int argmin_set(int ka, int kb, int t) {
 template <int D>
 __device__ __forceinline__ void gram4(Smem& s, const bkv_bf16* pa, const bkv_bf16* pb, int lane) {
     constexpr int kGroups = D / 32;
-    u32x4_t ga[kAhead + 1][4], gb[kAhead + 1][4];
+    u32x4_t ga[kAhead4 + 1][4], gb[kAhead4 + 1][4];
 #pragma unroll
-    for (int gi = 0; gi < kAhead && gi < kGroups; ++gi)
+    for (int gi = 0; gi < kAhead4 && gi < kGroups; ++gi)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             ga[gi][q] = *reinterpret_cast<const u32x4_t*>(pa + gi * 32 + q * 8);
@@ -105,15 +131,15 @@ __device__ __forceinline__ void gram4(Smem& s, const bkv_bf16* pa, const bkv_bf1
     f32x16_t d0 = f32x16_t{}, d1 = f32x16_t{}, o = f32x16_t{};
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
-        u32x4_t (&ca)[4] = ga[gi % (kAhead + 1)];
-        u32x4_t (&cb)[4] = gb[gi % (kAhead + 1)];
-        if (gi + kAhead < kGroups) {
-            u32x4_t (&na)[4] = ga[(gi + kAhead) % (kAhead + 1)];
-            u32x4_t (&nb)[4] = gb[(gi + kAhead) % (kAhead + 1)];
+        u32x4_t (&ca)[4] = ga[gi % (kAhead4 + 1)];
+        u32x4_t (&cb)[4] = gb[gi % (kAhead4 + 1)];
+        if (gi + kAhead4 < kGroups) {
+            u32x4_t (&na)[4] = ga[(gi + kAhead4) % (kAhead4 + 1)];
+            u32x4_t (&nb)[4] = gb[(gi + kAhead4) % (kAhead4 + 1)];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                na[q] = *reinterpret_cast<const u32x4_t*>(pa + (gi + kAhead) * 32 + q * 8);
-                nb[q] = *reinterpret_cast<const u32x4_t*>(pb + (gi + kAhead) * 32 + q * 8);
+                na[q] = *reinterpret_cast<const u32x4_t*>(pa + (gi + kAhead4) * 32 + q * 8);
+                nb[q] = *reinterpret_cast<const u32x4_t*>(pb + (gi + kAhead4) * 32 + q * 8);
             }
         }
         asm volatile("" : "+v"(ca[0]), "+v"(ca[1]), "+v"(ca[2]), "+v"(ca[3]));
@@ -132,9 +158,9 @@ __device__ __forceinline__ void gram4(Smem& s, const bkv_bf16* pa, const bkv_bf1
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int g = r >> 2, i = 4 * q + (r & 3);
-        cel(s, g, i, j) = d0[r];
-        cel(s, g, kHalf + i, kHalf + j) = d1[r];
-        cel(s, g, i, kHalf + j) = o[r];
+        d0_of(s, g)[i * kHalf + j] = d0[r];
+        d1_of(s, g)[i * kHalf + j] = d1[r];
+        o_of(s, g)[i * kOStride + j] = o[r];
     }
     wave_lds_sync();
 }
@@ -147,46 +173,54 @@ __device__ __forceinline__ float cosine(float g, float ni, float nj) {
 // The Gram entries in s.c become cosines, the norms go to s.nrm.  The
 // matrices are symmetric bit for bit (the products are exact, both triangles
 // accumulate them in the same order, and nrm_i nrm_j = nrm_j nrm_i), so each
-// cosine is computed once and written to both of its entries.  Lane t of set
-// g takes the pairs (t, t + k), k = 0..16, and (t + 16, (t + 16 + k) mod 32),
-// k = 0..15: every unordered pair once.  A pair's Gram entry is read at
-// (t, t + k) and at ((t + 16 + k) mod 32, t + 16), entries the Gram pass wrote;
-// only the lane that owns the pair reads or writes its two entries, and it
-// reads before it writes.
+// cosine is computed once and written to the entries that hold it.  Lane t
+// of set g takes, in D0, the pairs (t, (t + k) mod 16), k = 0..8, writing
+// both (t, c) and (c, t) (the pair (t, t + 8) by both of its lanes, which
+// write the same value); the same in D1; and row t of O, all 16 of its
+// entries.  Every lane reads the Gram entries of a tile before any lane
+// writes a cosine into it.
 __device__ __forceinline__ void cosines4(Smem& s, int lane) {
     const int g = lane >> 4, t = lane & 15;
-    const float na = __builtin_sqrtf(cel(s, g, t, t));
-    const float nb = __builtin_sqrtf(cel(s, g, kHalf + t, kHalf + t));
+    float* D0 = d0_of(s, g);
+    float* D1 = d1_of(s, g);
+    float* O = o_of(s, g);
+    const float na = __builtin_sqrtf(D0[t * kHalf + t]);
+    const float nb = __builtin_sqrtf(D1[t * kHalf + t]);
     s.nrm[g][t] = na;
     s.nrm[g][kHalf + t] = nb;
     wave_lds_sync();
-    // every Gram entry and norm the lane needs first (one LDS latency), then the divisions, then the writes
-    float ga[kHalf + 1], gb[kHalf], ma[kHalf + 1], mb[kHalf];
+    constexpr int kDiag = kHalf / 2 + 1;   // 9 pairs per lane in each diagonal tile
 #pragma unroll
-    for (int k = 0; k <= kHalf; ++k) {
-        ga[k] = cel(s, g, t, t + k);
-        ma[k] = s.nrm[g][t + k];
+    for (int tile = 0; tile < 2; ++tile) {
+        float* T = tile ? D1 : D0;
+        const float ni = tile ? nb : na;
+        const float* nr = s.nrm[g] + tile * kHalf;
+        float gv[kDiag], nv[kDiag];
+#pragma unroll
+        for (int k = 0; k < kDiag; ++k) {
+            const int c = (t + k) & (kHalf - 1);
+            gv[k] = T[t * kHalf + c];
+            nv[k] = nr[c];
+        }
+        wave_lds_sync();   // every lane's reads of the tile are done before the first cosine overwrites it
+#pragma unroll
+        for (int k = 0; k < kDiag; ++k) gv[k] = cosine(gv[k], ni, nv[k]);
+#pragma unroll
+        for (int k = 0; k < kDiag; ++k) {
+            const int c = (t + k) & (kHalf - 1);
+            T[t * kHalf + c] = gv[k];
+            T[c * kHalf + t] = gv[k];
+        }
     }
+    {
+        float gv[kHalf], nv[kHalf];
 #pragma unroll
-    for (int k = 0; k < kHalf; ++k) {
-        const int j = (t + kHalf + k) & (kMaxRows - 1);
-        gb[k] = cel(s, g, j, kHalf + t);
-        mb[k] = s.nrm[g][j];
-    }
+        for (int j = 0; j < kHalf; ++j) {
+            gv[j] = O[t * kOStride + j];
+            nv[j] = s.nrm[g][kHalf + j];
+        }
 #pragma unroll
-    for (int k = 0; k <= kHalf; ++k) ga[k] = cosine(ga[k], na, ma[k]);
-#pragma unroll
-    for (int k = 0; k < kHalf; ++k) gb[k] = cosine(gb[k], nb, mb[k]);
-#pragma unroll
-    for (int k = 0; k <= kHalf; ++k) {
-        cel(s, g, t, t + k) = ga[k];
-        cel(s, g, t + k, t) = ga[k];
-    }
-#pragma unroll
-    for (int k = 0; k < kHalf; ++k) {
-        const int j = (t + kHalf + k) & (kMaxRows - 1);
-        cel(s, g, kHalf + t, j) = gb[k];
-        cel(s, g, j, kHalf + t) = gb[k];
+        for (int j = 0; j < kHalf; ++j) O[t * kOStride + j] = cosine(gv[j], na, nv[j]);
     }
     wave_lds_sync();
 }
@@ -210,12 +244,15 @@ __device__ __forceinline__ Picks fps4(Smem& s, int n, int m, int lane) {
     if (__ballot((n != kMaxRows) & (n != 0)) == 0) {   // every set full (every sampling round of a stream)
 #pragma unroll 8
         for (int j = 0; j < kMaxRows; ++j) {
-            sa = sa + cel(s, g, j, t);
-            sb = sb + cel(s, g, j, kHalf + t);
+            float ca, cb;
+            row_pair(s, g, j, t, ca, cb);
+            sa = sa + ca;
+            sb = sb + cb;
         }
     } else {
         for (int j = 0; j < kMaxRows; ++j) {
-            const float ca = cel(s, g, j, t), cb = cel(s, g, j, kHalf + t);
+            float ca, cb;
+            row_pair(s, g, j, t, ca, cb);
             sa = j < n ? sa + ca : sa;
             sb = j < n ? sb + cb : sb;
         }
@@ -227,8 +264,10 @@ __device__ __forceinline__ Picks fps4(Smem& s, int n, int m, int lane) {
     // r, equal to column r), kOut once taken or past n.  The maximum of two keys is the key of the larger
     // cosine, and keys compare as the cosines do.
     constexpr int kOut = 0x7FFFFFFF;   // above every finite value's key
-    int ka = ((t < n) & (t != p)) ? order_key(cel(s, g, p, t)) : kOut;
-    int kb = ((kHalf + t < n) & (kHalf + t != p)) ? order_key(cel(s, g, p, kHalf + t)) : kOut;
+    float pa_, pb_;
+    row_pair(s, g, p, t, pa_, pb_);
+    int ka = ((t < n) & (t != p)) ? order_key(pa_) : kOut;
+    int kb = ((kHalf + t < n) & (kHalf + t != p)) ? order_key(pb_) : kOut;
     Picks pk;
     pk.pa = p;
     pk.pb = p;
@@ -236,7 +275,9 @@ __device__ __forceinline__ Picks fps4(Smem& s, int n, int m, int lane) {
         const int r = argmin_set(ka, kb, t);
         pk.pa = t == it ? r : pk.pa;
         pk.pb = kHalf + t == it ? r : pk.pb;
-        const int ca = order_key(cel(s, g, r, t)), cb = order_key(cel(s, g, r, kHalf + t));
+        float ra_, rb_;
+        row_pair(s, g, r, t, ra_, rb_);
+        const int ca = order_key(ra_), cb = order_key(rb_);
         ka = t == r ? kOut : max(ka, ca);
         kb = kHalf + t == r ? kOut : max(kb, cb);
     }
@@ -312,7 +353,7 @@ __device__ __forceinline__ void compact4(Smem& s, uint32_t mask, bkv_bf16* dst, 
     wave_lds_sync();   // the list's reads are done before the next use of the area
 }
 
-constexpr int kMaxBuffersPerWave = 32;
+constexpr int kMaxBuffersPerWave = 16;
 
 // The continual FPS buffer update (Notes §2.2, Eq. 9) of the nw buffers
 // b0 .. b0 + nw - 1 (nw <= kMaxBuffersPerWave) by one wave: append each buffer's new query at
