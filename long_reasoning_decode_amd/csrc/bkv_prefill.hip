@@ -497,6 +497,60 @@ __device__ __forceinline__ float fma_lds_row(const u32x4_t* lrows, int s, const 
     return acc;
 }
 
+// A greedy step's chains on the fp32 path: the register rows and this
+// thread's LDS row (slot s) against y in one loop over pieces, so that each
+// piece of y is read once for all of them and the chains interleave.  Each
+// chain is the same as fma_rows' and fma_lds_row's.
+template <int D, int R>
+__device__ __forceinline__ void fma_rows_lds(const float (&x)[R][D], const u32x4_t* lrows, int s, const float* y,
+                                             float (&acc)[R], float& acc_l) {
+    const Bf u = Bf::fresh();
+    constexpr int NP = D / 8;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    float al = 0.0f;
+    u32x4_t w = lrows[slot<D, true>(s, 0)];
+    f32x4_t ya = *reinterpret_cast<const f32x4_t*>(y);
+    f32x4_t yb = *reinterpret_cast<const f32x4_t*>(y + 4);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        u32x4_t nw = w;
+        f32x4_t na = ya, nb = yb;
+        if (p + 1 < NP) {
+            nw = lrows[slot<D, true>(s, p + 1)];
+            na = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1));
+            nb = *reinterpret_cast<const f32x4_t*>(y + 8 * (p + 1) + 4);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float a = acc[r];
+            a = __builtin_fmaf(x[r][8 * p + 0], ya[0], a);
+            a = __builtin_fmaf(x[r][8 * p + 1], ya[1], a);
+            a = __builtin_fmaf(x[r][8 * p + 2], ya[2], a);
+            a = __builtin_fmaf(x[r][8 * p + 3], ya[3], a);
+            a = __builtin_fmaf(x[r][8 * p + 4], yb[0], a);
+            a = __builtin_fmaf(x[r][8 * p + 5], yb[1], a);
+            a = __builtin_fmaf(x[r][8 * p + 6], yb[2], a);
+            a = __builtin_fmaf(x[r][8 * p + 7], yb[3], a);
+            piece_fence(a);
+            acc[r] = a;
+        }
+        al = __builtin_fmaf(u.lo(w[0]), ya[0], al);
+        al = __builtin_fmaf(u.hi(w[0]), ya[1], al);
+        al = __builtin_fmaf(u.lo(w[1]), ya[2], al);
+        al = __builtin_fmaf(u.hi(w[1]), ya[3], al);
+        al = __builtin_fmaf(u.lo(w[2]), yb[0], al);
+        al = __builtin_fmaf(u.hi(w[2]), yb[1], al);
+        al = __builtin_fmaf(u.lo(w[3]), yb[2], al);
+        al = __builtin_fmaf(u.hi(w[3]), yb[3], al);
+        piece_fence(al);
+        w = nw;
+        ya = na;
+        yb = nb;
+    }
+    acc_l = al;
+}
+
 // F32: the register-resident rows are kept in fp32 and the LDS rows (at most
 // one per thread, piece-major) are streamed piece by piece; only when every
 // row outside the registers is in LDS (no global tier), where the registers
@@ -674,9 +728,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         const float ny = xn[par];
         bv = __builtin_inff();
         bi = kNone;
+        // fp32 path with a row in LDS per thread (C = RC + 1): that row's chain runs with the register rows'
+        float dl = 0.0f;
         {
             float dt[RC];
-            fma_rows<D, RC, false>(xv, y, nullptr, dt);
+            if constexpr (F32) {
+                if (C > RC) fma_rows_lds<D, RC>(xv, lrows, tid, y, dt, dl);
+                else fma_rows<D, RC, false>(xv, y, nullptr, dt);
+            } else {
+                fma_rows<D, RC, false>(xv, y, nullptr, dt);
+            }
 #pragma unroll
             for (int c = 0; c < RC; ++c) {
                 const int j = c * kThreads + tid;
@@ -696,10 +757,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             float sv = Sst[s];
             if (sv != sv) continue;   // taken
             float cs;
-            if constexpr (F32) {
+            if constexpr (F32) {   // s == tid: the row's chain ran above
                 const float nx = nst[s];
-                const float dt = fma_lds_row<D, false>(lrows, s, y + opaque_zero(), 0.0f);
-                cs = (nx == 0.0f || ny == 0.0f) ? 0.0f : dt / (nx * ny);
+                cs = (nx == 0.0f || ny == 0.0f) ? 0.0f : dl / (nx * ny);
             } else {
                 u32x4_t tmp[D / 8];
                 fetch_row<D>(Q, P, j, s, n_lds, lrows, tmp);
