@@ -240,21 +240,37 @@ struct Picks {
 __device__ __forceinline__ Picks fps4(Smem& s, int n, int m, int lane) {
     const int g = lane >> 4, t = lane & 15;
     // seed: lowest mean cosine (row sums read down the columns: the matrices are symmetric bit for bit)
+    // Rows j < 16 hold (j, t) in D0 and (j, 16 + t) in O; rows 16 + j hold (16 + j, t) = O[t][j] and
+    // (16 + j, 16 + t) in D1: one loop per half, so that every address is a fixed offset.
+    const float* D0 = d0_of(s, g);
+    const float* D1 = d1_of(s, g);
+    const float* O = o_of(s, g);
     float sa = 0.0f, sb = 0.0f;
     if (__ballot((n != kMaxRows) & (n != 0)) == 0) {   // every set full (every sampling round of a stream)
-#pragma unroll 8
-        for (int j = 0; j < kMaxRows; ++j) {
-            float ca, cb;
-            row_pair(s, g, j, t, ca, cb);
-            sa = sa + ca;
-            sb = sb + cb;
+#pragma unroll
+        for (int j = 0; j < kHalf; ++j) {
+            sa = sa + D0[j * kHalf + t];
+            sb = sb + O[j * kOStride + t];
         }
-    } else {
-        for (int j = 0; j < kMaxRows; ++j) {
-            float ca, cb;
-            row_pair(s, g, j, t, ca, cb);
+#pragma unroll
+        for (int j = 0; j < kHalf; ++j) {
+            sa = sa + O[t * kOStride + j];
+            sb = sb + D1[j * kHalf + t];
+        }
+    } else {   // the reads are made unconditional (opaque), so that they are not turned into branches
+#pragma unroll
+        for (int j = 0; j < kHalf; ++j) {
+            float ca = D0[j * kHalf + t], cb = O[j * kOStride + t];
+            asm volatile("" : "+v"(ca), "+v"(cb));
             sa = j < n ? sa + ca : sa;
             sb = j < n ? sb + cb : sb;
+        }
+#pragma unroll
+        for (int j = 0; j < kHalf; ++j) {
+            float ca = O[t * kOStride + j], cb = D1[j * kHalf + t];
+            asm volatile("" : "+v"(ca), "+v"(cb));
+            sa = kHalf + j < n ? sa + ca : sa;
+            sb = kHalf + j < n ? sb + cb : sb;
         }
     }
     const float va = t < n ? sa / (float)n : __builtin_inff();
