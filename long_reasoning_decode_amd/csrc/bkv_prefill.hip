@@ -5,10 +5,12 @@
 //
 // One 512-thread workgroup per buffer (one per CU: eight waves of up to 256
 // VGPRs); thread tid owns rows j = c * 512 + tid (chunk c).  The rows of the
-// first 128 / d chunks stay in registers as packed bf16 (64 VGPRs); the next
+// first 256 / d chunks stay in registers as packed bf16 (128 VGPRs); the next
 // ones stay in LDS (bf16, swizzled so that a wave's row reads are
 // conflict-free), up to the 160 KB a CU has; rows beyond that (prompts of
 // several thousand queries) are re-read from global memory on every pass.
+// Prompts whose rows past the first 128 / d chunks fit in LDS at one per
+// thread take the fp32 path instead (those chunks in registers in fp32).
 // The norms and S values of rows outside the registers live in LDS.
 //
 // Arithmetic, in one fixed fp32 order (bit-identical selections):
@@ -37,9 +39,10 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunks = BKV_PREFILL_MAX / kThreads;
 constexpr int kLdsBytes = 160 * 1024;   // LDS of one CU (the most a workgroup is given)
 
-template <int D>
+template <int D, bool F32 = true>
 struct Pre {
-    static constexpr int kRegChunks = 128 / D;          // chunks of rows in registers (64 VGPRs)
+    // chunks of rows in registers: 128 VGPRs of them, in fp32 (F32) or packed bf16
+    static constexpr int kRegChunks = (F32 ? 128 : 256) / D;
     static constexpr int kRegRows = kRegChunks * kThreads;
     // LDS layout (bytes)
     static constexpr int kXrOff = 0;                                 // float [2][D]   picked row
@@ -557,7 +560,7 @@ __device__ __forceinline__ void fma_rows_lds(const float (&x)[R][D], const u32x4
 // allow it.
 template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
-    using L = Pre<D>;
+    using L = Pre<D, F32>;
     constexpr int RC = L::kRegChunks;
     constexpr int RR = L::kRegRows;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -798,15 +801,17 @@ hipError_t launch_d(PrefillArgs a, hipStream_t st) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return e;
     a.lds_bytes = lim < kLdsBytes ? lim : kLdsBytes;
-    if ((int)Pre<D>::rows_off(a.P) > a.lds_bytes) return hipErrorInvalidValue;
     // fp32 path: every row past the registers in LDS, at most one per thread, in a piece-major area sized
     // for one row per thread (its slots are p * 512 + s whatever the row count)
-    const size_t f32_lds = (size_t)Pre<D>::rows_off(a.P) + (size_t)kThreads * Pre<D>::kRowBytes;
-    if (Pre<D>::n_other(a.P) <= kThreads && f32_lds <= (size_t)a.lds_bytes)
+    using F = Pre<D, true>;
+    using B = Pre<D, false>;
+    const size_t f32_lds = (size_t)F::rows_off(a.P) + (size_t)kThreads * F::kRowBytes;
+    if (F::n_other(a.P) <= kThreads && f32_lds <= (size_t)a.lds_bytes) {
         hipLaunchKernelGGL((prefill_kernel<D, true>), dim3(a.nbuf), dim3(kThreads), f32_lds, st, a);
-    else
-        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(a.nbuf), dim3(kThreads), Pre<D>::bytes(a.P, a.lds_bytes),
-                           st, a);
+    } else {
+        if ((int)B::rows_off(a.P) > a.lds_bytes) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((prefill_kernel<D, false>), dim3(a.nbuf), dim3(kThreads), B::bytes(a.P, a.lds_bytes), st, a);
+    }
     return hipGetLastError();
 }
 
