@@ -69,13 +69,24 @@ __device__ __forceinline__ float* d0_of(Smem& s, int g) { return s.c + g * kSetS
 __device__ __forceinline__ float* d1_of(Smem& s, int g) { return s.c + g * kSetStride + kTile; }
 __device__ __forceinline__ float* o_of(Smem& s, int g) { return s.c + g * kSetStride + 2 * kTile; }
 
-// Entries (r, t) and (r, 16 + t) of set g, for a row r < 32 and t < 16.
-__device__ __forceinline__ void row_pair(Smem& s, int g, int r, int t, float& a, float& b) {
-    const bool lo = r < kHalf;
-    const int rr = r & (kHalf - 1);
-    a = lo ? d0_of(s, g)[rr * kHalf + t] : o_of(s, g)[t * kOStride + rr];
-    b = lo ? o_of(s, g)[rr * kOStride + t] : d1_of(s, g)[rr * kHalf + t];
-}
+// Entries (r, t) and (r, 16 + t) of set g, for a row r < 32 and t < 16:
+// (r, t) is D0[r][t] or O[t][r - 16], (r, 16 + t) is O[r][t] or D1[r - 16][t],
+// each at a lane base plus a multiple of r (16-lane reads stay on distinct
+// banks: consecutive t, or rows of stride 17).
+struct RowPair {
+    const float* a_lo;   // D0 + t
+    const float* a_hi;   // O + 17 t - 16
+    const float* b_lo;   // O + t
+    const float* b_hi;   // D1 + t - 256
+    __device__ __forceinline__ RowPair(Smem& s, int g, int t)
+        : a_lo(d0_of(s, g) + t), a_hi(o_of(s, g) + t * kOStride - kHalf), b_lo(o_of(s, g) + t),
+          b_hi(d1_of(s, g) + t - kHalf * kHalf) {}
+    __device__ __forceinline__ void read(int r, float& a, float& b) const {
+        const bool lo = r < kHalf;
+        a = lo ? a_lo[r * kHalf] : a_hi[r];
+        b = lo ? b_lo[r * kOStride] : b_hi[r * kHalf];
+    }
+};
 
 // The wave's LDS writes are complete and visible to its other lanes; the
 // compiler does not move LDS accesses across this point.
@@ -280,8 +291,9 @@ __device__ __forceinline__ Picks fps4(Smem& s, int n, int m, int lane) {
     // r, equal to column r), kOut once taken or past n.  The maximum of two keys is the key of the larger
     // cosine, and keys compare as the cosines do.
     constexpr int kOut = 0x7FFFFFFF;   // above every finite value's key
+    const RowPair rows(s, g, t);
     float pa_, pb_;
-    row_pair(s, g, p, t, pa_, pb_);
+    rows.read(p, pa_, pb_);
     int ka = ((t < n) & (t != p)) ? order_key(pa_) : kOut;
     int kb = ((kHalf + t < n) & (kHalf + t != p)) ? order_key(pb_) : kOut;
     Picks pk;
@@ -292,7 +304,7 @@ __device__ __forceinline__ Picks fps4(Smem& s, int n, int m, int lane) {
         pk.pa = t == it ? r : pk.pa;
         pk.pb = kHalf + t == it ? r : pk.pb;
         float ra_, rb_;
-        row_pair(s, g, r, t, ra_, rb_);
+        rows.read(r, ra_, rb_);
         const int ca = order_key(ra_), cb = order_key(rb_);
         ka = t == r ? kOut : max(ka, ca);
         kb = kHalf + t == r ? kOut : max(kb, cb);
