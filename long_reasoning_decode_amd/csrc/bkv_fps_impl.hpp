@@ -52,18 +52,6 @@ struct Smem {
     float nrm[kSets][kMaxRows];
 };
 
-// Entry (i, j) of set g's matrix (i, j < 32; (i, j) and (j, i) are the same
-// float when they lie in O or its transpose).
-__device__ __forceinline__ float& cel(Smem& s, int g, int i, int j) {
-    const int lo_i = i < kHalf, lo_j = j < kHalf;
-    const int ii = i & (kHalf - 1), jj = j & (kHalf - 1);
-    const int idx = (lo_i & lo_j)     ? ii * kHalf + jj
-                    : !(lo_i | lo_j) ? kTile + ii * kHalf + jj
-                    : lo_i           ? 2 * kTile + ii * kOStride + jj
-                                     : 2 * kTile + jj * kOStride + ii;
-    return s.c[g * kSetStride + idx];
-}
-
 // Tiles of set g: D0[i][j] = entry (i, j), D1[i][j] = (16 + i, 16 + j), O[i][j] = (i, 16 + j), i, j < 16.
 __device__ __forceinline__ float* d0_of(Smem& s, int g) { return s.c + g * kSetStride; }
 __device__ __forceinline__ float* d1_of(Smem& s, int g) { return s.c + g * kSetStride + kTile; }
