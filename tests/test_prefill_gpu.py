@@ -75,8 +75,12 @@ def _check(cfg, q: torch.Tensor, P: int, bufs=None, where=""):
     return t_oracle
 
 
+# Across the kernel's layouts: every row in registers (up to 512 or 1024 rows at d = 128 or 64 on the fp32
+# path, up to 1024 or 2048 on the packed path), one row per thread in LDS (fp32 path), several LDS rows,
+# and rows re-read from memory; each boundary from both sides.
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("P", [0, 1, 2, 5, 16, 17, 100, 511, 512, 513, 1024, 1025, 1500, 2049, 4100])
+@pytest.mark.parametrize("P", [0, 1, 2, 5, 16, 17, 100, 511, 512, 513, 1024, 1025, 1500, 1536, 1537, 1600, 2048,
+                               2049, 4100])
 def test_prefill_matches_oracle(d, P):
     cfg = SMALL.scaled(d=d)
     _flush(f"prefill d={d} P={P}")
