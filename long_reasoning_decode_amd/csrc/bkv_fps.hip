@@ -2,12 +2,14 @@
 // end-of-cycle merge (Notes §2.2, Eq. 9 and App. Alg. 1-2), independent
 // wavefronts in both.  The update (and the compression at the freeze point)
 // appends each buffer's query and samples the buffers that filled up, four
-// per wave at a time, a run of buffers per wave (bkv_fps_impl.hpp; its LDS of
-// about 17 KB per wave makes LDS the occupancy limit, two waves per SIMD).
-// The merge samples beacons ++ recents, two buffers per wave and four waves
-// per SIMD (bkv_fps_pair.hpp).
+// per wave at a time, a run of buffers per wave (bkv_fps_impl.hpp; 13 KB of
+// LDS and at most 168 VGPRs per wave, three waves per SIMD).  In a decode
+// step the update also appends the step's key and value rows, so that the
+// step is one launch.  The merge samples beacons ++ recents, two buffers per
+// wave and four waves per SIMD (bkv_fps_pair.hpp).
 #include <atomic>
 
+#include "bkv_append_impl.hpp"
 #include "bkv_fps_pair.hpp"
 
 namespace bkv {
@@ -26,6 +28,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, 3) void fps_kernel(FpsArgs a) 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
+    if (!COMPRESS && a.append) {   // the step's key and value rows: wave w takes a contiguous share of pieces
+        constexpr int T = D / 8;
+        const int64_t n = (int64_t)a.app.units * T;
+        const int64_t p1 = (w + 1) * n / n_waves;
+        for (int64_t p = w * n / n_waves + lane; p < p1; p += 64) append_piece<D>(a.app, p / T, (int)(p % T));
+    }
     const int64_t lo = w * a.nbuf / n_waves, hi = (w + 1) * a.nbuf / n_waves;
     for (int64_t b0 = lo; b0 < hi; b0 += fps::kMaxBuffersPerWave) {
         const int nw = (int)(hi - b0 < fps::kMaxBuffersPerWave ? hi - b0 : fps::kMaxBuffersPerWave);

@@ -369,7 +369,7 @@ __device__ __forceinline__ void compact4(Smem& s, uint32_t mask, bkv_bf16* dst, 
     wave_lds_sync();   // the list's reads are done before the next use of the area
 }
 
-constexpr int kMaxBuffersPerWave = 16;
+constexpr int kMaxBuffersPerWave = 32;
 
 // The continual FPS buffer update (Notes §2.2, Eq. 9) of the nw buffers
 // b0 .. b0 + nw - 1 (nw <= kMaxBuffersPerWave) by one wave: append each buffer's new query at

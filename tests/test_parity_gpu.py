@@ -174,7 +174,7 @@ def test_fps_update_splits(nb, nrq):
 @pytest.mark.parametrize("d,nbuf,nb", [(64, 100_000, 16), (128, 30_000, 16), (128, 30_000, 31)])
 def test_fps_update_several_buffers_per_wave(d, nbuf, nb):
     """More buffers than the chip holds waves at once, so each wave updates a run of them (one or more
-    passes of up to 16, whose full buffers are sampled four at a time): full and non-full buffers mixed
+    passes of up to 32, whose full buffers are sampled four at a time): full and non-full buffers mixed
     within a run, so that the groups of four are ragged, adversarial contents in the first few hundred."""
     rng = np.random.default_rng(300 + d + nb)
     cfg = TINY.scaled(d=d, n_layers=1, batch=nbuf // 8, hq=8, hkv=2, n_beacon=nb, n_recent_q=32 - nb)
