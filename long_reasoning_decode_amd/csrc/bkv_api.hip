@@ -7,6 +7,7 @@
 
 #include "bkv.h"
 #include "bkv_internal.hpp"
+#include "bkv_step.hpp"
 
 namespace {
 
@@ -76,8 +77,6 @@ bkv::FpsArgs fps_args(const bkv_shape* s, bkv_bf16* qbuf, int32_t* qcount, const
     a.src = src_of(s);
     a.seed = s->seed;
     a.compress = 0;
-    a.append = 0;
-    a.app = bkv::AppendArgs{};
     return a;
 }
 
@@ -411,10 +410,8 @@ int bkv_decode_step(const bkv_shape* s, bkv_bf16* K, bkv_bf16* V, int32_t L, con
     aa.hkv = s->n_kv_heads;
     aa.rope_rows = rope_rows;
     if (!ring && fps_src) {   // collection phase: the buffer update appends the key and value in the same launch
-        bkv::FpsArgs fa = fps_args(s, qbuf, qcount, q_new, nullptr, fps_sel);
-        fa.append = 1;
-        fa.app = aa;
-        return hip_status(bkv::launch_fps(fa, s->head_dim, false, st));
+        const bkv::FpsArgs fa = fps_args(s, qbuf, qcount, q_new, nullptr, fps_sel);
+        return hip_status(bkv::launch_fps_step(fa, aa, s->head_dim, st));
     }
     if ((e = hip_status(bkv::launch_append(aa, s->head_dim, st)))) return e;
 

@@ -11,6 +11,7 @@
 
 #include "bkv_append_impl.hpp"
 #include "bkv_fps_pair.hpp"
+#include "bkv_step.hpp"
 
 namespace bkv {
 
@@ -23,16 +24,16 @@ constexpr int kMergeWavesPerBlock = 4;   // merge
 // kMaxBuffersPerWave at a time, so every wave has the same share (to one
 // buffer) when all of them sample.
 template <int D, bool COMPRESS>
-__global__ __launch_bounds__(64 * kWavesPerBlock, 3) void fps_kernel(FpsArgs a) {
+__global__ __launch_bounds__(64 * kWavesPerBlock, 3) void fps_kernel(FpsArgs a, AppendArgs app) {
     __shared__ fps::Smem s[kWavesPerBlock];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wave;
     const int64_t n_waves = (int64_t)gridDim.x * kWavesPerBlock;
-    if (!COMPRESS && a.append) {   // the step's key and value rows: wave w takes a contiguous share of pieces
+    if (!COMPRESS && app.units > 0) {   // the step's key and value rows: wave w takes a contiguous share of pieces
         constexpr int T = D / 8;
-        const int64_t n = (int64_t)a.app.units * T;
+        const int64_t n = (int64_t)app.units * T;
         const int64_t p1 = (w + 1) * n / n_waves;
-        for (int64_t p = w * n / n_waves + lane; p < p1; p += 64) append_piece<D>(a.app, p / T, (int)(p % T));
+        for (int64_t p = w * n / n_waves + lane; p < p1; p += 64) append_piece<D>(app, p / T, (int)(p % T));
     }
     const int64_t lo = w * a.nbuf / n_waves, hi = (w + 1) * a.nbuf / n_waves;
     for (int64_t b0 = lo; b0 < hi; b0 += fps::kMaxBuffersPerWave) {
@@ -89,6 +90,35 @@ hipError_t fps_grid_limit(int d, int64_t* out) {
     return hipSuccess;
 }
 
+namespace {
+
+// The update or the compression kernel over every buffer (with app.units > 0, the update also appends
+// app's key and value rows).
+hipError_t launch_update(const FpsArgs& a, const AppendArgs& app, int d, hipStream_t st) {
+    // at most one buffer per wave, and at most the workgroups the chip holds at once
+    int64_t blocks = (a.nbuf + kWavesPerBlock - 1) / kWavesPerBlock;
+    int64_t fit = 0;
+    const hipError_t e = fps_grid_limit(d, &fit);
+    if (e != hipSuccess) return e;
+    if (blocks > fit) blocks = fit;
+    dim3 grid((unsigned)blocks), block(64 * kWavesPerBlock);
+    if (d == 64) {
+        if (a.compress) hipLaunchKernelGGL((fps_kernel<64, true>), grid, block, 0, st, a, app);
+        else hipLaunchKernelGGL((fps_kernel<64, false>), grid, block, 0, st, a, app);
+    } else {
+        if (a.compress) hipLaunchKernelGGL((fps_kernel<128, true>), grid, block, 0, st, a, app);
+        else hipLaunchKernelGGL((fps_kernel<128, false>), grid, block, 0, st, a, app);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fps_step(const FpsArgs& a, const AppendArgs& app, int d, hipStream_t st) {
+    if (a.nbuf <= 0) return hipSuccess;
+    return launch_update(a, app, d, st);
+}
+
 hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st) {
     if (a.nbuf <= 0) return hipSuccess;
     if (a.src == kSrcNaive)   // the beacons come from the history at each eviction: fps_sel only receives -1s
@@ -101,21 +131,9 @@ hipError_t launch_fps(const FpsArgs& a, int d, bool merge, hipStream_t st) {
         else hipLaunchKernelGGL((merge_kernel<128>), grid, block, 0, st, a);
         return hipGetLastError();
     }
-    // at most one buffer per wave, and at most the workgroups the chip holds at once
-    int64_t blocks = (a.nbuf + kWavesPerBlock - 1) / kWavesPerBlock;
-    int64_t fit = 0;
-    const hipError_t e = fps_grid_limit(d, &fit);
-    if (e != hipSuccess) return e;
-    if (blocks > fit) blocks = fit;
-    dim3 grid((unsigned)blocks), block(64 * kWavesPerBlock);
-    if (d == 64) {
-        if (a.compress) hipLaunchKernelGGL((fps_kernel<64, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((fps_kernel<64, false>), grid, block, 0, st, a);
-    } else {
-        if (a.compress) hipLaunchKernelGGL((fps_kernel<128, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((fps_kernel<128, false>), grid, block, 0, st, a);
-    }
-    return hipGetLastError();
+    AppendArgs none{};
+    none.units = 0;
+    return launch_update(a, none, d, st);
 }
 
 }  // namespace bkv

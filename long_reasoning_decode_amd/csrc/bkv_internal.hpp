@@ -8,16 +8,6 @@
 
 namespace bkv {
 
-struct AppendArgs {
-    bkv_bf16* K;               // [units][cap][d]
-    bkv_bf16* V;
-    const bkv_bf16* k_new;     // [units][d] pre-RoPE
-    const bkv_bf16* v_new;     // [units][d]
-    const int32_t* pos;        // [batch]
-    const float* rope_cs;      // [rope_rows][d/2][2]
-    int units, cap, L, batch, hkv, rope_rows;
-};
-
 struct FpsArgs {
     bkv_bf16* qbuf;            // [nbuf][qcap][d]
     int32_t* qcount;           // [nbuf]
@@ -28,8 +18,6 @@ struct FpsArgs {
     int src;                   // beacon source: kSrcFps, kSrcInitial, kSrcRandom, kSrcNaive
     uint32_t seed;             // key of the random-history draws
     int compress;              // update without an append: sample the buffers holding more than n_beacon rows
-    int append;                // update: also run the step's key and value append `app` (one launch per step)
-    AppendArgs app;
 };
 
 constexpr int kSrcFps = 0, kSrcInitial = 1, kSrcRandom = 2, kSrcNaive = 3;
@@ -79,6 +67,15 @@ struct EvictArgs {
     int budget, n_prefix, n_recent_kv;
 };
 
+struct AppendArgs {
+    bkv_bf16* K;               // [units][cap][d]
+    bkv_bf16* V;
+    const bkv_bf16* k_new;     // [units][d] pre-RoPE
+    const bkv_bf16* v_new;     // [units][d]
+    const int32_t* pos;        // [batch]
+    const float* rope_cs;      // [rope_rows][d/2][2]
+    int units, cap, L, batch, hkv, rope_rows;
+};
 
 struct AttnArgs {
     const bkv_bf16* K;         // [units][cap][d] post-RoPE
