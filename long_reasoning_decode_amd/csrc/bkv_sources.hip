@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void offer_merge_kernel(FpsArgs a) {
     }
     if (a.fps_sel)
         for (int i = lane; i < nb; i += 64) a.fps_sel[b * nb + i] = -1;
-    if (lane == 0) a.qcount[b] = n0 + nrq;
+    if (lane == 0 && nrq > 0) a.qcount[b] = n0 + nrq;   // no recents: nothing offered, the count stays
 }
 
 // fps_sel of the initial source's merge (nothing else changes).

@@ -1,0 +1,180 @@
+"""GPU parity over seeded random shapes: every field of bkv_shape drawn within
+the library's limits (head size, query heads per KV head 1..8, every split of
+the query buffer, buffer strides qcap above B_Q^max, forced keeps from 0,
+budgets below and above the cache length, causal or not, max or mean pooling,
+each beacon source), with query counts that include out-of-range values.
+Bars as in the other parity tests: selections, keep sets (up to the tie band)
+and buffers exact, scores within 1e-4 relative, compacted rows byte-identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from long_reasoning_decode_amd import lib as L
+from long_reasoning_decode_amd import synth
+from long_reasoning_decode_amd.configs import TINY
+
+import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+_SRC = {"fps": 0, "initial": L.BKV_BEACON_INITIAL, "random": L.BKV_BEACON_RANDOM}
+
+
+def _split(rng: np.random.Generator) -> tuple:
+    """(n_beacon, n_recent_q) with 1 <= n_beacon + n_recent_q <= 32; the edges (no beacons, no recents, a full
+    32) drawn often."""
+    k = rng.integers(0, 5)
+    if k == 0:
+        return 0, int(rng.integers(1, 33))
+    if k == 1:
+        return int(rng.integers(1, 33)), 0
+    if k == 2:
+        nb = int(rng.integers(1, 32))
+        return nb, 32 - nb
+    nb = int(rng.integers(0, 32))
+    return nb, int(rng.integers(1 if nb == 0 else 0, 33 - nb))
+
+
+def _evict_cases(n: int, seed: int) -> list:
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.integers(1, 4))
+        G = int(rng.integers(1, 9))
+        nb, nrq = _split(rng)
+        qcap = nb + nrq + int(rng.choice([0, 0, 1, 3, 9]))
+        npf = int(rng.choice([0, 1, 4, 8, 16]))
+        nrk = int(rng.choice([0, 1, 16, 32]))
+        budget = npf + nrk + int(rng.integers(1, 700))
+        n_new = int(rng.integers(1, 300))
+        cap = budget + n_new
+        kind = rng.integers(0, 6)
+        N = {0: cap, 1: budget + 1, 2: max(1, budget), 3: max(1, budget - int(rng.integers(0, 40)))}.get(
+            int(kind), int(rng.integers(budget + 1, cap + 1)))
+        N = min(N, cap)
+        flags = (L.BKV_CAUSAL_RECENT if rng.random() < 0.7 else 0) | (L.BKV_POOL_MEAN if rng.random() < 0.3 else 0)
+        src = str(rng.choice(["fps", "fps", "initial", "random"]))
+        flags |= _SRC[src]
+        t_lo = int(rng.integers(40, 9000))
+        t_hi = t_lo + int(rng.integers(0, 24000))
+        cfg = TINY.scaled(name=f"r{i}", d=d, hq=hkv * G, hkv=hkv, n_layers=int(rng.integers(1, 3)),
+                          batch=int(rng.integers(1, 4)), theta=float(rng.choice([1e4, 1e6])), budget=budget,
+                          n_new=n_new, n_prefix=npf, n_recent_kv=nrk, n_beacon=nb, n_recent_q=nrq, qcap=qcap,
+                          t_lo=t_lo, t_hi=t_hi, mix=str(rng.choice(["clusters8", "tight3"])),
+                          seed=int(rng.integers(1, 1 << 31)), beacon=src)
+        out.append((cfg, N, flags))
+    # two long caches, one workgroup each
+    for i, (d, G) in enumerate([(128, 5), (64, 8)]):
+        nb, nrq = _split(rng)
+        cfg = TINY.scaled(name=f"long{i}", d=d, hq=G, hkv=1, budget=int(rng.integers(4000, 8000)), n_new=0,
+                          n_prefix=4, n_recent_kv=16, n_beacon=nb, n_recent_q=nrq, qcap=nb + nrq + 2,
+                          t_lo=9000, t_hi=30000, mix="clusters8", seed=int(rng.integers(1, 1 << 31)))
+        cfg = cfg.scaled(n_new=8192 - cfg.budget)
+        out.append((cfg, 8192, L.BKV_CAUSAL_RECENT))
+    return out
+
+
+EVICT = _evict_cases(40, 20261202)
+
+
+def _id(c) -> str:
+    cfg, N, flags = c
+    return (f"{cfg.name}-d{cfg.d}-g{cfg.G}x{cfg.hkv}-q{cfg.n_beacon}+{cfg.n_recent_q}/{cfg.qcap}"
+            f"-k{cfg.n_prefix}+{cfg.n_recent_kv}-b{cfg.budget}-n{N}-f{flags}")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+    yield
+
+
+@pytest.mark.parametrize("case", EVICT, ids=[_id(c) for c in EVICT])
+def test_evict_random_shape(case):
+    cfg, N, flags = case
+    print(f"evict {_id(case)}", flush=True)
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    rng = np.random.default_rng(cfg.seed)
+    qc = rng.integers(-2, cfg.qcap + 3, inp["qcount"].shape).astype(np.int32)
+    inp["qcount"] = torch.from_numpy(qc).cuda()
+    out = H.run_evict_gpu(cfg, inp, N, flags=flags)
+    H.compare_evict(cfg, inp, out, N, flags=flags, where=_id(case))
+
+
+def _buffer_cases(n: int, seed: int) -> list:
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        nb, nrq = _split(rng)
+        out.append((int(rng.choice([64, 128])), nb, nrq, nb + nrq + int(rng.choice([0, 1, 5])),
+                    int(rng.integers(1, 300)), int(rng.integers(1, 1 << 31))))
+    return out
+
+
+BUFFERS = _buffer_cases(16, 4242)
+
+
+def _bid(c) -> str:
+    d, nb, nrq, qcap, nbuf, _ = c
+    return f"d{d}-q{nb}+{nrq}/{qcap}-x{nbuf}"
+
+
+def _rows(rng, n, r, d):
+    return torch.from_numpy(rng.standard_normal((n, r, d)).astype(np.float32)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", BUFFERS, ids=[_bid(c) for c in BUFFERS])
+def test_fps_update_random_shape(case):
+    """One decode step's buffer update over buffers of a random stride and split, counts from below 0 to
+    past the stride (clamped on entry)."""
+    d, nb, nrq, qcap, nbuf, seed = case
+    print(f"fps_update {_bid(case)}", flush=True)
+    rng = np.random.default_rng(seed)
+    cfg = TINY.scaled(d=d, n_layers=1, batch=nbuf, hq=1, hkv=1, n_beacon=nb, n_recent_q=nrq, qcap=qcap)
+    qb, qn = _rows(rng, nbuf, qcap, d), _rows(rng, nbuf, 1, d)[:, 0]
+    bqmax = nb + nrq
+    qc = np.where(rng.random(nbuf) < 0.5, bqmax - 1, rng.integers(-2, qcap + 3, nbuf)).astype(np.int32)
+    qbuf_h, qc_h = synth.to_u16(qb).copy(), qc.copy()
+    sel_o = O.fps_update(qbuf_h, qc_h, synth.to_u16(qn), nb, nrq)
+    qbuf_d, qc_d = qb.cuda(), torch.from_numpy(qc).cuda()
+    sel_d = torch.full((nbuf, max(nb, 1)), -7, dtype=torch.int32, device="cuda")
+    L.fps_update(L.shape_of(cfg), qbuf_d, qc_d, qn.cuda(), sel_d if nb > 0 else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(qc_d.cpu().numpy(), qc_h)
+    if nb > 0:
+        assert np.array_equal(sel_d.cpu().numpy(), sel_o)
+    g = synth.to_u16(qbuf_d)
+    live = np.arange(qcap)[None, :, None] < qc_h[:, None, None]
+    assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
+
+
+@pytest.mark.parametrize("case", BUFFERS, ids=[_bid(c) for c in BUFFERS])
+def test_fps_merge_random_shape(case):
+    """The end-of-cycle merge over buffers of a random stride and split, beacon counts out of range
+    included."""
+    d, nb, nrq, qcap, nbuf, seed = case
+    print(f"fps_merge {_bid(case)}", flush=True)
+    rng = np.random.default_rng(seed + 1)
+    cfg = TINY.scaled(d=d, n_layers=1, batch=nbuf, hq=1, hkv=1, n_beacon=nb, n_recent_q=nrq, qcap=qcap)
+    qb, qr = _rows(rng, nbuf, qcap, d), _rows(rng, nbuf, nrq, d)
+    qc = rng.integers(-2, qcap + 3, nbuf).astype(np.int32)
+    qbuf_h = synth.to_u16(qb).reshape(nbuf, 1, qcap, d).copy()
+    qc_h = qc.reshape(nbuf, 1).copy()
+    sel_o = O.merge(H.ocfg(cfg), qbuf_h, qc_h, synth.to_u16(qr).reshape(nbuf, 1, nrq, d))
+    qbuf_d, qc_d = qb.cuda(), torch.from_numpy(qc).cuda()
+    sel_d = torch.full((nbuf, max(nb, 1)), -7, dtype=torch.int32, device="cuda")
+    L.fps_merge(L.shape_of(cfg), qbuf_d, qc_d, qr.cuda() if nrq > 0 else None, sel_d if nb > 0 else None)
+    torch.cuda.synchronize()
+    if nb > 0:
+        assert np.array_equal(sel_d.cpu().numpy().reshape(nbuf, 1, -1), sel_o)
+    assert np.array_equal(qc_d.cpu().numpy().reshape(nbuf, 1), qc_h)
+    g = synth.to_u16(qbuf_d).reshape(nbuf, 1, qcap, d)
+    live = np.arange(qcap)[None, None, :, None] < qc_h[:, :, None, None]
+    assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
