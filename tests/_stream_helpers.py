@@ -3,8 +3,10 @@ comparison with the GPU stream."""
 from __future__ import annotations
 
 import numpy as np
+import torch
 
 import oracle as O
+from long_reasoning_decode_amd import synth
 from long_reasoning_decode_amd.configs import StreamConfig
 
 from _helpers import check_keep, check_scores
@@ -81,3 +83,29 @@ def compare_stream(scfg: StreamConfig, o: dict, g_idx, g_scores, g_state: dict, 
         assert np.array_equal(g_state["q_recent"][k], o["q_recent"][k]), f"{w}: recent ring"
         assert np.array_equal(g_state["pos_recent"][k], o["pos_recent"][k]), f"{w}: ring positions"
     return {"diverged": diverged}
+
+
+def gpu_state(run, units) -> dict:
+    """Host copies of the listed units' cache, buffers and ring (unit-major)."""
+    b = run.base
+    U, G, d = b.units, b.G, b.d
+    ut = torch.tensor(list(units), dtype=torch.long, device="cuda")
+    bt = (ut // b.hkv) % b.batch
+    return {"K": synth.to_u16(run.K.reshape(U, b.cap, d).index_select(0, ut)),
+            "V": synth.to_u16(run.V.reshape(U, b.cap, d).index_select(0, ut)),
+            "qbuf": synth.to_u16(run.qbuf.reshape(U, G, b.qcap, d).index_select(0, ut)),
+            "qcount": run.qcount.reshape(U, G).index_select(0, ut).cpu().numpy(),
+            "q_recent": synth.to_u16(run.q_recent.reshape(U, G, b.n_recent_q, d).index_select(0, ut)),
+            "pos_recent": run.pos_recent.index_select(0, bt).cpu().numpy()}
+
+
+def check_run(scfg, run, units, where, nthreads=None):
+    """The recorded units of a GPU stream (a StreamRun) against the oracle's replay of the same inputs."""
+    h = run.history()
+    u16 = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    o = replay(scfg, u16(h["k_new"]), u16(h["v_new"]), u16(h["q_new"]), h["pos"].numpy().astype(np.int32),
+               max_ev=run.n_ev, nthreads=nthreads, units=units)
+    assert o["n_ev"] == run.n_ev and o["L"] == run.L
+    res = compare_stream(scfg, o, h["idx"].numpy(), h["scores"].numpy(), gpu_state(run, units), where)
+    print(f"{where}: {run.n_ev} evictions, L={run.L}, tie-band divergences {res['diverged']}", flush=True)
+    return res

@@ -18,6 +18,7 @@ from long_reasoning_decode_amd import synth
 from long_reasoning_decode_amd.configs import TINY
 
 import _helpers as H
+from _stream_helpers import check_run
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +179,51 @@ def test_fps_merge_random_shape(case):
     g = synth.to_u16(qbuf_d).reshape(nbuf, 1, qcap, d)
     live = np.arange(qcap)[None, None, :, None] < qc_h[:, :, None, None]
     assert np.array_equal(np.where(live, g, 0), np.where(live, qbuf_h, 0))
+
+
+def _stream_cases(n: int, seed: int) -> list:
+    """Short decode streams of random shape: every source (naive full history included), both poolings,
+    strides above B_Q^max, at least three evictions each."""
+    from dataclasses import replace
+    from long_reasoning_decode_amd.configs import TINY_STREAM
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        hkv = int(rng.integers(1, 3))
+        G = int(rng.integers(1, 9))
+        nb, nrq = _split(rng)
+        npf = int(rng.choice([0, 2, 8]))
+        nrk = int(rng.choice([0, 1, 16]))
+        budget = npf + nrk + int(rng.integers(1, 160))
+        n_new = nrq + int(rng.integers(1, 60))
+        src = str(rng.choice(["fps", "fps", "initial", "random", "naive"]))
+        base = replace(TINY, name=f"s{i}", d=d, hq=hkv * G, hkv=hkv, batch=int(rng.integers(1, 3)),
+                       budget=budget, n_new=n_new, n_prefix=npf, n_recent_kv=nrk, n_beacon=nb, n_recent_q=nrq,
+                       qcap=nb + nrq + int(rng.choice([0, 2, 7])), pool=str(rng.choice(["max", "mean"])),
+                       beacon=src, mix=str(rng.choice(["clusters8", "tight3"])), seed=int(rng.integers(1, 1 << 31)))
+        steps = base.cap + 3 * n_new + int(rng.integers(0, n_new))
+        out.append(replace(TINY_STREAM, name=f"stream-s{i}", base=base, steps=steps, drift_every=64,
+                           p0_max=int(rng.integers(1, 5000))))
+    return out
+
+
+STREAMS = _stream_cases(14, 777)
+
+
+def _sid(s) -> str:
+    b = s.base
+    return (f"{s.name}-d{b.d}-g{b.G}x{b.hkv}-q{b.n_beacon}+{b.n_recent_q}/{b.qcap}-k{b.n_prefix}+{b.n_recent_kv}"
+            f"-b{b.budget}+{b.n_new}-{b.beacon}-{b.pool}")
+
+
+@pytest.mark.parametrize("scfg", STREAMS, ids=[_sid(s) for s in STREAMS])
+def test_stream_random_shape(scfg):
+    """Decode steps and evictions from an empty cache, every unit recorded, against the oracle's replay."""
+    from long_reasoning_decode_amd.stream import StreamRun
+    print(f"stream {_sid(scfg)} steps {scfg.steps}", flush=True)
+    units = range(scfg.base.units)
+    run = StreamRun(scfg, record_units=units, block=40)
+    r = run.run()
+    assert r["evictions"] == scfg.evictions() >= 3
+    check_run(scfg, run, units, _sid(scfg))

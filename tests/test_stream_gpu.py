@@ -2,46 +2,21 @@
 cache is full) against the oracle's replay of the same per-step inputs."""
 from __future__ import annotations
 
-import numpy as np
+from dataclasses import replace
+
 import pytest
 import torch
 
 from long_reasoning_decode_amd import lib as L
-from long_reasoning_decode_amd import synth
-from dataclasses import replace
 
 from long_reasoning_decode_amd.configs import (STREAM, STREAM_NAIVE, STREAM_SOURCES, STREAM_SPLITS, TINY_STREAM,
                                                TINY_STREAM_MEAN, TINY_STREAM_NAIVE, TINY_STREAM_SOURCES,
                                                TINY_STREAM_SPLITS)
 from long_reasoning_decode_amd.stream import StreamRun
 
-from _stream_helpers import compare_stream, replay
+from _stream_helpers import check_run as _check
 
 pytestmark = pytest.mark.gpu
-
-
-def _gpu_state(run: StreamRun, units) -> dict:
-    b = run.base
-    U, G, d = b.units, b.G, b.d
-    ut = torch.tensor(list(units), dtype=torch.long, device="cuda")
-    bt = (ut // b.hkv) % b.batch
-    return {"K": synth.to_u16(run.K.reshape(U, b.cap, d).index_select(0, ut)),
-            "V": synth.to_u16(run.V.reshape(U, b.cap, d).index_select(0, ut)),
-            "qbuf": synth.to_u16(run.qbuf.reshape(U, G, b.qcap, d).index_select(0, ut)),
-            "qcount": run.qcount.reshape(U, G).index_select(0, ut).cpu().numpy(),
-            "q_recent": synth.to_u16(run.q_recent.reshape(U, G, b.n_recent_q, d).index_select(0, ut)),
-            "pos_recent": run.pos_recent.index_select(0, bt).cpu().numpy()}
-
-
-def _check(scfg, run: StreamRun, units, where, nthreads=None):
-    h = run.history()
-    u16 = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
-    o = replay(scfg, u16(h["k_new"]), u16(h["v_new"]), u16(h["q_new"]), h["pos"].numpy().astype(np.int32),
-               max_ev=run.n_ev, nthreads=nthreads, units=units)
-    assert o["n_ev"] == run.n_ev and o["L"] == run.L
-    res = compare_stream(scfg, o, h["idx"].numpy(), h["scores"].numpy(), _gpu_state(run, units), where)
-    print(f"{where}: {run.n_ev} evictions, L={run.L}, tie-band divergences {res['diverged']}", flush=True)
-    return res
 
 
 def test_stream_tiny_all_units():
