@@ -227,3 +227,88 @@ def test_stream_random_shape(scfg):
     r = run.run()
     assert r["evictions"] == scfg.evictions() >= 3
     check_run(scfg, run, units, _sid(scfg))
+
+
+def _prefill_cases(n: int, seed: int) -> list:
+    """Prompt sampling of random shape: every split (n_beacon 0 to 32), strides above B_Q^max, prompt lengths
+    from empty to the longest taken, each source; and the same sampling from a history of random stride."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        nb, nrq = _split(rng)
+        k = int(rng.integers(0, 7))
+        P = [0, 1, nb, nb + 1, int(rng.integers(2, 600)), int(rng.integers(600, 2200)),
+             int(rng.integers(2200, L.BKV_PREFILL_MAX + 1))][k]
+        hkv = int(rng.integers(1, 3))
+        cfg = TINY.scaled(name=f"p{i}", d=d, n_layers=1, batch=int(rng.integers(1, 3)), hq=hkv * int(rng.integers(1, 3)),
+                          hkv=hkv, n_beacon=nb, n_recent_q=nrq, qcap=nb + nrq + int(rng.choice([0, 3])),
+                          beacon=str(rng.choice(["fps", "fps", "initial", "random"])),
+                          seed=int(rng.integers(1, 1 << 31)))
+        hcap = P + int(rng.choice([0, 1, 37]))
+        out.append((cfg, P, hcap))
+    return out
+
+
+PREFILLS = _prefill_cases(24, 99)
+
+
+def _pid(c) -> str:
+    cfg, P, hcap = c
+    return f"{cfg.name}-d{cfg.d}-x{cfg.qbufs}-q{cfg.n_beacon}+{cfg.n_recent_q}/{cfg.qcap}-P{P}-h{hcap}-{cfg.beacon}"
+
+
+def _oracle_sample(cfg, qn: np.ndarray) -> tuple:
+    """The oracle's prompt sampling of every buffer of qn [nbuf, P, d] under the workload's source."""
+    nbuf = qn.shape[0]
+    ob = np.full((nbuf, cfg.qcap, cfg.d), 0x7F7F, np.uint16)
+    oc = np.zeros(nbuf, np.int32)
+    src = {"fps": O.SRC_FPS, "initial": O.SRC_INITIAL, "random": O.SRC_RANDOM}[cfg.beacon]
+    osel = O.prefill(qn, ob, oc, cfg.n_beacon, src=src, seed=cfg.seed)
+    return ob, oc, osel
+
+
+def _check_sampled(cfg, qbuf, qc, sel, ob, oc, osel, where) -> None:
+    g_buf, g_qc = synth.to_u16(qbuf), qc.cpu().numpy()
+    assert np.array_equal(g_qc, oc), where
+    if cfg.n_beacon > 0:
+        assert np.array_equal(sel.cpu().numpy(), osel), where
+    for b in range(cfg.qbufs):
+        n = int(oc[b])
+        assert np.array_equal(g_buf[b, :n], ob[b, :n]), f"{where} buffer {b}: rows"
+        assert np.all(g_buf[b, n:] == 0x7F7F), f"{where} buffer {b}: rows past the count were written"
+
+
+def _outputs(cfg):
+    qbuf = torch.full((cfg.qbufs, cfg.qcap, cfg.d), 0x7F7F, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    qc = torch.full((cfg.qbufs,), -5, dtype=torch.int32, device="cuda")
+    sel = torch.full((cfg.qbufs, max(cfg.n_beacon, 1)), -7, dtype=torch.int32, device="cuda")
+    return qbuf, qc, sel
+
+
+@pytest.mark.parametrize("case", PREFILLS, ids=[_pid(c) for c in PREFILLS])
+def test_prefill_random_shape(case):
+    cfg, P, _ = case
+    print(f"prefill {_pid(case)}", flush=True)
+    q = synth.make_prompt_queries(cfg, P, device="cuda", seed=cfg.seed)
+    qbuf, qc, sel = _outputs(cfg)
+    L.fps_prefill(L.shape_of(cfg), q, P, qbuf, qc, sel if cfg.n_beacon > 0 else None)
+    torch.cuda.synchronize()
+    ob, oc, osel = _oracle_sample(cfg, synth.to_u16(q).reshape(cfg.qbufs, P, cfg.d))
+    _check_sampled(cfg, qbuf, qc, sel, ob, oc, osel, _pid(case))
+
+
+@pytest.mark.parametrize("case", [c for c in PREFILLS if c[0].beacon == "fps"],
+                         ids=[_pid(c) for c in PREFILLS if c[0].beacon == "fps"])
+def test_fps_history_random_shape(case):
+    """The naive source's sampling of the first n_rows of a history of stride hcap (the later rows hold
+    NaNs and must not be read)."""
+    cfg, n_rows, hcap = case
+    print(f"fps_history {_pid(case)}", flush=True)
+    q = synth.make_prompt_queries(cfg, hcap, device="cuda", seed=cfg.seed + 1).reshape(cfg.qbufs, hcap, cfg.d)
+    q[:, n_rows:] = float("nan")
+    qbuf, qc, sel = _outputs(cfg)
+    L.fps_history(L.shape_of(cfg), q, hcap, n_rows, qbuf, qc, sel if cfg.n_beacon > 0 else None)
+    torch.cuda.synchronize()
+    ob, oc, osel = _oracle_sample(cfg, np.ascontiguousarray(synth.to_u16(q)[:, :n_rows]))
+    _check_sampled(cfg, qbuf, qc, sel, ob, oc, osel, _pid(case))
