@@ -312,3 +312,76 @@ def test_fps_history_random_shape(case):
     torch.cuda.synchronize()
     ob, oc, osel = _oracle_sample(cfg, np.ascontiguousarray(synth.to_u16(q)[:, :n_rows]))
     _check_sampled(cfg, qbuf, qc, sel, ob, oc, osel, _pid(case))
+
+
+SEPARATE = EVICT[::2]
+
+
+@pytest.mark.parametrize("case", SEPARATE, ids=[_id(c) for c in SEPARATE])
+def test_separate_calls_random_shape(case):
+    """bkv_score against the oracle, bkv_select on those scores against the oracle's ranking of the same
+    fp32 values, bkv_compact against the gather, bkv_fps_merge after them; and bkv_evict equal to the four
+    calls bit for bit."""
+    cfg, N, flags = case
+    print(f"separate calls {_id(case)}", flush=True)
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    rng = np.random.default_rng(cfg.seed + 3)
+    inp["qcount"] = torch.from_numpy(rng.integers(-2, cfg.qcap + 3, inp["qcount"].shape).astype(np.int32)).cuda()
+    rope = H.rope_dev(cfg)
+    shape = L.shape_of(cfg, cap=inp["K"].shape[-2], flags=flags)
+    sep = {k: v.clone() for k, v in inp.items()}
+    U, B = cfg.units, cfg.budget
+    scores = torch.empty((U, N), dtype=torch.float32, device="cuda")
+    idx = torch.full((U, B), -7, dtype=torch.int32, device="cuda")
+    sel = torch.full((cfg.qbufs, max(cfg.n_beacon, 1)), -7, dtype=torch.int32, device="cuda")
+    L.score(shape, sep["K"], N, sep["qbuf"], sep["qcount"], sep["q_recent"], sep["pos_recent"], sep["t"], rope, scores)
+    L.select(shape, scores, N, idx)
+    L.compact(shape, sep["K"], sep["V"], N, idx)
+    L.fps_merge(shape, sep["qbuf"], sep["qcount"], sep["q_recent"] if cfg.n_recent_q > 0 else None,
+                sel if cfg.n_beacon > 0 else None)
+    fused = H.run_evict_gpu(cfg, inp, N, flags=flags, rope=rope)
+    torch.cuda.synchronize()
+    v = synth.oracle_views(cfg, inp)
+    o = O.score(H.ocfg(cfg, n_len=inp["K"].shape[-2], flags=flags), v["K"], v["qbuf"], v["qcount"], v["q_recent"],
+                v["pos_recent"], v["t"], n_len=N)
+    g_s = scores.cpu().numpy()
+    H.check_scores(g_s, o, _id(case))
+    g_idx = idx.cpu().numpy()
+    for u in range(U):
+        ref, _ = O.select(g_s[u].astype(np.float64), B, cfg.n_prefix, cfg.n_recent_kv)
+        assert np.array_equal(g_idx[u], ref), f"{_id(case)} unit {u}: keep set"
+    m = min(N, B)
+    K0 = synth.to_u16(inp["K"]).reshape(U, -1, cfg.d)
+    V0 = synth.to_u16(inp["V"]).reshape(U, -1, cfg.d)
+    gi = g_idx[:, :m]
+    assert np.array_equal(synth.to_u16(sep["K"]).reshape(U, -1, cfg.d)[:, :m], np.take_along_axis(K0, gi[:, :, None], 1))
+    assert np.array_equal(synth.to_u16(sep["V"]).reshape(U, -1, cfg.d)[:, :m], np.take_along_axis(V0, gi[:, :, None], 1))
+    assert torch.equal(fused["scores"], scores) and torch.equal(fused["idx"], idx)
+    if cfg.n_beacon > 0:
+        assert torch.equal(fused["fps_sel"], sel)
+    for k in ("K", "V", "qbuf", "qcount"):
+        assert torch.equal(fused[k], sep[k]), k
+
+
+@pytest.mark.parametrize("case", SEPARATE, ids=[_id(c) for c in SEPARATE])
+def test_decode_attention_random_shape(case):
+    """Decode attention of one query per head over the first n_len rows, at three cache lengths, against the
+    oracle (|gpu - oracle| <= 1e-4 sum_j w_j |v_j| + 1e-6, the bar of the attention tests)."""
+    cfg, N, _ = case
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    rng = np.random.default_rng(cfg.seed + 5)
+    shape = L.shape_of(cfg, cap=inp["K"].shape[-2])
+    rope = H.rope_dev(cfg)
+    q = inp["q_recent"][..., 0, :].contiguous() if cfg.n_recent_q > 0 else inp["qbuf"][..., 0, :].contiguous()
+    U, G, D = cfg.units, cfg.G, cfg.d
+    oc = H.ocfg(cfg, n_len=inp["K"].shape[-2])
+    v = synth.oracle_views(cfg, inp)
+    qn = synth.to_u16(q).reshape(U, G, D)
+    for n in sorted({1, N, int(rng.integers(1, cfg.n_len + 1))}):
+        print(f"attention {_id(case)} n_len={n}", flush=True)
+        out = torch.full((cfg.qbufs, D), float("nan"), dtype=torch.float32, device="cuda")
+        L.decode_attention(shape, inp["K"], inp["V"], n, q, inp["t"], rope, out)
+        torch.cuda.synchronize()
+        o, scale = O.decode_attention(oc, v["K"], v["V"], np.ascontiguousarray(qn), v["t"], n)
+        err = np.abs(out.reshape(U, G, D).cpu().numpy().astype(np.float64) - o)
+        assert (err <= 1e-4 * scale + 1e-6).all(), f"{_id(case)} n_len={n}"
