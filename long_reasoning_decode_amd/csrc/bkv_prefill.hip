@@ -18,8 +18,8 @@
 //   inv_j = 1 / nrm_j (0 if nrm_j is 0), u_j[k] = x_j[k] * inv_j;
 //   s[k]  = pairwise sum of u_j[k] over j: a balanced binary tree over the
 //           row index, padded with zero rows to a power of two.  Lanes form
-//           the low six levels (DPP), waves the next three (LDS), chunks
-//           the rest;
+//           the low six levels (an LDS transpose, then DPP), waves the next
+//           three (LDS), chunks the rest;
 //   a_j   = (fma chain of u_j[k] * s[k]) / P, the mean cosine of row j to all
 //           rows (cos is the dot product of unit rows), seed p = argmin a;
 //   then n_beacon - 1 steps: S_j = max(S_j, cos(x_j, x_r)) for the last pick
@@ -50,7 +50,8 @@ struct Pre {
     static constexpr int kWvOff = kXnOff + 16;                       // int [2][waves] wave minima (keys)
     static constexpr int kWiOff = kWvOff + 2 * kWaves * 4;           // int   [2][waves]
     static constexpr int kPartOff = kWiOff + 2 * kWaves * 4;         // float [waves][D] wave column sums
-    static constexpr int kCsumOff = kPartOff + kWaves * D * 4;       // float [chunks][D]
+    static constexpr int kSlabOff = kPartOff + kWaves * D * 4;       // float [waves][4][64] column transposes
+    static constexpr int kCsumOff = kSlabOff + kWaves * 256 * 4;     // float [chunks][D]
     static constexpr int kSsumOff = kCsumOff + kMaxChunks * D * 4;   // float [D]
     static constexpr int kSelOff = kSsumOff + D * 4;                 // int [32]
     static constexpr int kOtherOff = kSelOff + 32 * 4;               // float nrm[n_other], S[n_other]; then rows
@@ -174,17 +175,30 @@ __device__ __forceinline__ float dpp_add(float v) {
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
 
-// Pairwise sum over the 64 lanes: lane pairs (2i, 2i+1), then blocks of 4, 8,
-// 16 inside each 16-lane row, then rows (0 + 1) and (2 + 3), then the two
-// halves.  Lanes 48..63 receive the total.
-__device__ __forceinline__ float wave_pairwise_sum(float v) {
-    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
-    v = dpp_add<0x140, 0xF>(v);   // row_mirror
-    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-    return v;
+// Sums of four columns over the wave's 64 rows (row = lane; v0..v3 are the
+// lane's entries of the four columns), as a pairwise tree over the lane
+// index: the values pass through the wave's own 1 KB of LDS (column k at
+// words 64 k .. 64 k + 63, so that the writes and the reads are
+// conflict-free); lane 16 c + m adds rows 4m .. 4m + 3 of column c in pairs,
+// then the 16 lanes of its DPP row finish the tree over m: pairs of lanes,
+// blocks of 4, halves (mirrored lanes hold the same block sums), the whole
+// row.  Lane 16 c writes column c's sum to dst[c].  A wave's LDS accesses
+// complete in order, so the reads see this call's writes and the next call's
+// writes follow these reads.
+__device__ __forceinline__ void col4_sum(float v0, float v1, float v2, float v3, float* slab, float* dst,
+                                         int lane) {
+    slab[lane] = v0;
+    slab[64 + lane] = v1;
+    slab[128 + lane] = v2;
+    slab[192 + lane] = v3;
+    const int c = lane >> 4, m = lane & 15;
+    const f32x4_t r = *reinterpret_cast<const f32x4_t*>(slab + 64 * c + 4 * m);
+    float v = (r[0] + r[1]) + (r[2] + r[3]);
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]: blocks of 8 rows
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]: 16 rows
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror: 32 rows
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror: all 64
+    if (m == 0) dst[c] = v;
 }
 
 constexpr int kNoKey = 0x7FFFFFFF;   // above every candidate's key
@@ -243,25 +257,20 @@ __device__ __forceinline__ int block_argmin(float v, int i, int* wk, int* wi, in
 }
 
 // Column sums of one chunk's unit rows u = x * inv into csum[c][0 .. D):
-// pairwise over the lanes (DPP), then over the waves.  All threads call it.
+// pairwise over the lanes (col4_sum), then over the waves.  All threads call
+// it.
 template <int D>
-__device__ __forceinline__ void chunk_colsum(const u32x4_t (&x)[D / 8], float inv, int c, float* part, float* csum,
-                                             int wave, int lane, int tid) {
+__device__ __forceinline__ void chunk_colsum(const u32x4_t (&x)[D / 8], float inv, int c, float* part, float* slab,
+                                             float* csum, int wave, int lane, int tid) {
     const Bf u = Bf::fresh();
+    float* sl = slab + wave * 256;
 #pragma unroll
     for (int p = 0; p < D / 8; ++p) {
         const u32x4_t w = x[p];
-        float s8[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s8[2 * e] = wave_pairwise_sum(u.lo(w[e]) * inv);
-            s8[2 * e + 1] = wave_pairwise_sum(u.hi(w[e]) * inv);
-        }
-        if (lane == 63) {
-            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p) = f32x4_t{s8[0], s8[1], s8[2], s8[3]};
-            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p + 4) = f32x4_t{s8[4], s8[5], s8[6], s8[7]};
-        }
-        asm volatile("" ::: "memory");
+        col4_sum(u.lo(w[0]) * inv, u.hi(w[0]) * inv, u.lo(w[1]) * inv, u.hi(w[1]) * inv, sl, part + wave * D + 8 * p,
+                 lane);
+        col4_sum(u.lo(w[2]) * inv, u.hi(w[2]) * inv, u.lo(w[3]) * inv, u.hi(w[3]) * inv, sl,
+                 part + wave * D + 8 * p + 4, lane);
     }
     __syncthreads();
     if (tid < D) {
@@ -430,19 +439,12 @@ __device__ __forceinline__ void fma_rows(const float (&x)[R][D], const float* y,
 }
 
 template <int D>
-__device__ __forceinline__ void chunk_colsum(const float (&x)[D], float inv, int c, float* part, float* csum, int wave,
-                                             int lane, int tid) {
+__device__ __forceinline__ void chunk_colsum(const float (&x)[D], float inv, int c, float* part, float* slab,
+                                             float* csum, int wave, int lane, int tid) {
+    float* sl = slab + wave * 256;
 #pragma unroll
-    for (int p = 0; p < D / 8; ++p) {
-        float s8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s8[e] = wave_pairwise_sum(x[8 * p + e] * inv);
-        if (lane == 63) {
-            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p) = f32x4_t{s8[0], s8[1], s8[2], s8[3]};
-            *reinterpret_cast<f32x4_t*>(part + wave * D + 8 * p + 4) = f32x4_t{s8[4], s8[5], s8[6], s8[7]};
-        }
-        asm volatile("" ::: "memory");
-    }
+    for (int k = 0; k < D; k += 4)
+        col4_sum(x[k] * inv, x[k + 1] * inv, x[k + 2] * inv, x[k + 3] * inv, sl, part + wave * D + k, lane);
     __syncthreads();
     if (tid < D) {
         const float* q = part + tid;
@@ -569,6 +571,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     int* wk = reinterpret_cast<int*>(smem + L::kWvOff);
     int* wi = reinterpret_cast<int*>(smem + L::kWiOff);
     float* part = reinterpret_cast<float*>(smem + L::kPartOff);
+    float* slab = reinterpret_cast<float*>(smem + L::kSlabOff);
     float* csum = reinterpret_cast<float*>(smem + L::kCsumOff);
     float* ssum = reinterpret_cast<float*>(smem + L::kSsumOff);
     int* sel = reinterpret_cast<int*>(smem + L::kSelOff);
@@ -617,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                 for (int p = 0; p < D / 8; ++p) lrows[slot<D, F32>(s, p)] = tmp[p];
             }
         }
-        chunk_colsum<D>(tmp, inv_of(nr), c, part, csum, wave, lane, tid);
+        chunk_colsum<D>(tmp, inv_of(nr), c, part, slab, csum, wave, lane, tid);
     }
     typename RegRows<D, RC, F32>::type xv;
     float nrm[RC];
@@ -631,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     for (int c = 0; c < RC; ++c) nrm[c] = norm_of<D>(xv[c]);
 #pragma unroll
     for (int c = 0; c < RC; ++c)
-        if (c < C) chunk_colsum<D>(xv[c], inv_of(nrm[c]), c, part, csum, wave, lane, tid);
+        if (c < C) chunk_colsum<D>(xv[c], inv_of(nrm[c]), c, part, slab, csum, wave, lane, tid);
     // pairwise over the chunks, bottom-up in place; chunks past the last are zero
     if (tid < D) {
         int Cp = 1;
