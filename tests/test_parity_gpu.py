@@ -584,6 +584,46 @@ def test_evict_rejects_bad_shapes_without_launching():
     assert e.value.code == -3
 
 
+def test_positions_outside_the_table_are_clamped():
+    """Positions below 0 or past the RoPE table read its first or last row: the eviction (beacons at t, recents
+    at their own positions), the key append and decode attention give bit for bit what they give with the
+    positions clamped into the table."""
+    cfg = TINY.scaled(name="clamp", n_layers=2, batch=3)
+    rope = H.rope_dev(cfg)
+    R = rope.shape[0]
+    inp = synth.make_evict_inputs(cfg, device="cuda")
+    bad = {k: v.clone() for k, v in inp.items()}
+    bad["t"] = torch.tensor([-7, R + 100, 5], dtype=torch.int32, device="cuda")
+    pr = bad["pos_recent"].clone()
+    pr[0, :5] = torch.arange(-5, 0, dtype=torch.int32, device="cuda")
+    pr[1, -3:] = R + torch.arange(3, dtype=torch.int32, device="cuda")
+    pr[2, 0] = -(1 << 30)
+    pr[2, 1] = (1 << 31) - 1
+    bad["pos_recent"] = pr
+    good = {k: v.clone() for k, v in inp.items()}
+    good["t"] = bad["t"].clamp(0, R - 1)
+    good["pos_recent"] = bad["pos_recent"].clamp(0, R - 1)
+    ob = H.run_evict_gpu(cfg, bad, cfg.n_len, rope=rope)
+    og = H.run_evict_gpu(cfg, good, cfg.n_len, rope=rope)
+    for k in ("scores", "idx", "fps_sel", "K", "V", "qbuf", "qcount"):
+        assert torch.equal(ob[k].view(torch.uint8), og[k].view(torch.uint8)), k
+    shape = L.shape_of(cfg)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    kn = torch.randn(cfg.units, cfg.d, generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(cfg.units, cfg.d, generator=g, device="cuda").to(torch.bfloat16)
+    Kb, Vb, Kg, Vg = inp["K"].clone(), inp["V"].clone(), inp["K"].clone(), inp["V"].clone()
+    L.append_kv(shape, Kb, Vb, cfg.n_len - 2, kn, vn, bad["t"], rope)
+    L.append_kv(shape, Kg, Vg, cfg.n_len - 2, kn, vn, good["t"], rope)
+    q = inp["q_recent"][..., 0, :].contiguous()
+    ab = torch.empty((cfg.qbufs, cfg.d), dtype=torch.float32, device="cuda")
+    ag = torch.empty_like(ab)
+    L.decode_attention(shape, inp["K"], inp["V"], cfg.n_len, q, bad["t"], rope, ab)
+    L.decode_attention(shape, inp["K"], inp["V"], cfg.n_len, q, good["t"], rope, ag)
+    torch.cuda.synchronize()
+    assert torch.equal(Kb.view(torch.uint8), Kg.view(torch.uint8)) and torch.equal(Vb, Vg)
+    assert torch.equal(ab.view(torch.uint8), ag.view(torch.uint8))
+
+
 @pytest.mark.parametrize("cfg", [TINY, QWEN3_4B.scaled(n_layers=2, batch=2), R1_QWEN_7B.scaled(n_layers=1, batch=2),
                                  QWEN3_4B_MEAN.scaled(n_layers=2, batch=2), TINY.scaled(name="tiny-mean", pool="mean")],
                          ids=lambda c: c.name)
