@@ -556,6 +556,72 @@ __device__ __forceinline__ void fma_rows_lds(const float (&x)[R][D], const u32x4
     acc_l = al;
 }
 
+// Publishes pick r (uniform): its norm at xn[par] and its row in fp32 at
+// xr[par] for the greedy step, and marks it taken.  A row held in bf16 (in
+// LDS, in memory, or, on the packed path, in its lane's registers, staged
+// through xr[1 - par], which no thread reads in this step) is converted by
+// the first D / 8 lanes of its owner's wave, one 16-byte piece each, rather
+// than by the owner alone; an fp32 register row is stored by its lane.
+template <int D, bool F32, int RC, typename Rows>
+__device__ __forceinline__ void publish(int r, int par, float* xr, float* xn, const Rows& xv, const float (&nrm)[RC],
+                                        uint32_t& taken, const float* nst, float* Sst, const u32x4_t* lrows, int n_lds,
+                                        const bkv_bf16* Q, int wave, int lane, int tid) {
+    constexpr int RR = RC * kThreads;
+    const int owner = r & (kThreads - 1), c_r = r / kThreads;
+    float* dst = xr + par * D;
+    if (F32 && c_r < RC) {   // an fp32 register row
+        if (tid == owner) {
+#pragma unroll
+            for (int cc = 0; cc < RC; ++cc)
+                if (cc == c_r) {
+                    taken |= 1u << cc;
+                    xn[par] = nrm[cc];
+                    store_row_f32<D>(xv[cc], dst);
+                }
+        }
+        return;
+    }
+    if (wave != owner / kWave) return;
+    const bool me = lane == (owner & (kWave - 1));
+    u32x4_t w = u32x4_t{0u, 0u, 0u, 0u};
+    if (c_r < RC) {   // packed register row (the packed path only)
+        if constexpr (!F32) {
+            u32x4_t* stage = reinterpret_cast<u32x4_t*>(xr + (1 - par) * D);
+            if (me) {
+#pragma unroll
+                for (int cc = 0; cc < RC; ++cc)
+                    if (cc == c_r) {
+                        taken |= 1u << cc;
+                        xn[par] = nrm[cc];
+#pragma unroll
+                        for (int p = 0; p < D / 8; ++p) stage[p] = xv[cc][p];
+                    }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the stage is written before its pieces are read
+            if (lane < D / 8) w = stage[lane];
+        }
+    } else {
+        const int s = r - RR;
+        if (me) {
+            xn[par] = nst[s];
+            Sst[s] = __builtin_nanf("");
+        }
+        if (lane < D / 8) {
+            if constexpr (F32)   // every row past the registers is in LDS
+                w = lrows[slot<D, true>(s, lane)];
+            else
+                w = s < n_lds ? lrows[slot<D, false>(s, lane)] : reinterpret_cast<const u32x4_t*>(Q + (size_t)r * D)[lane];
+        }
+    }
+    if (lane < D / 8) {
+        float* dp = dst + 8 * lane;
+        *reinterpret_cast<f32x4_t*>(dp) = f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                                                  __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+        *reinterpret_cast<f32x4_t*>(dp + 4) = f32x4_t{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                                                      __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u)};
+    }
+}
+
 // F32: the register-resident rows are kept in fp32 and the LDS rows (at most
 // one per thread, piece-major) are streamed piece by piece; only when every
 // row outside the registers is in LDS (no global tier), where the registers
@@ -695,39 +761,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         const int par = t & 1;
         // publish pick t: the selection order, its row and norm for the update
         if (tid == 0) sel[t] = r;
-        if (tid == (r & (kThreads - 1))) {
-            const int c = r / kThreads;
-            float* dst = xr + par * D;
-            if (c < RC) {
-#pragma unroll
-                for (int cc = 0; cc < RC; ++cc)
-                    if (cc == c) {
-                        taken |= 1u << cc;
-                        xn[par] = nrm[cc];
-                        store_row_f32<D>(xv[cc], dst);
-                    }
-            } else {
-                const int s = r - RR;
-                xn[par] = nst[s];
-                Sst[s] = __builtin_nanf("");
-                if constexpr (F32) {   // piece by piece from LDS
-#pragma unroll 1
-                    for (int p = 0; p < D / 8; ++p) {
-                        const u32x4_t w = lrows[slot<D, true>(s, p)];
-                        *reinterpret_cast<f32x4_t*>(dst + 8 * p) =
-                            f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
-                                    __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
-                        *reinterpret_cast<f32x4_t*>(dst + 8 * p + 4) =
-                            f32x4_t{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
-                                    __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u)};
-                    }
-                } else {
-                    u32x4_t tmp[D / 8];
-                    fetch_row<D>(Q, P, r, s, n_lds, lrows, tmp);
-                    store_row_f32<D>(tmp, dst);
-                }
-            }
-        }
+        publish<D, F32>(r, par, xr, xn, xv, nrm, taken, nst, Sst, lrows, n_lds, Q, wave, lane, tid);
         __syncthreads();
         if (t + 1 == m) break;
         const float* y = xr + par * D;
