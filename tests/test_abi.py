@@ -173,3 +173,30 @@ def test_all_configs_are_supported_shapes():
         assert cfg.d in (64, 128) and cfg.hq % cfg.hkv == 0 and cfg.G <= 8
         assert cfg.n_beacon + cfg.n_recent_q <= 32 <= cfg.qcap
         assert cfg.n_len <= 8192 and cfg.budget >= cfg.n_prefix + cfg.n_recent_kv
+
+
+def test_binding_refuses_to_run_without_the_library():
+    """No fallback: with libbkv.so absent, loading and every call through the binding raise instead of
+    computing anything on the host (checked in a fresh interpreter, so this process's loaded library is
+    untouched)."""
+    import subprocess
+    import sys
+    code = ("import torch\n"
+            "from long_reasoning_decode_amd import lib as L\n"
+            "from long_reasoning_decode_amd import synth\n"
+            "from long_reasoning_decode_amd.configs import TINY\n"
+            "L.LIB_PATH = '/nonexistent/libbkv.so'\n"
+            "i = synth.make_evict_inputs(TINY)\n"
+            "rope = torch.zeros(TINY.rope_rows, TINY.d)\n"
+            "ev = lambda: L.evict(L.shape_of(TINY), i['K'], i['V'], TINY.n_len, i['qbuf'], i['qcount'],\n"
+            "                     i['q_recent'], i['pos_recent'], i['t'], rope)\n"
+            "for name, call in (('load', L.load), ('rope_table', lambda: L.rope_table(1e4, 64, 0, 8)),\n"
+            "                   ('evict', ev)):\n"
+            "    try:\n"
+            "        call()\n"
+            "        print(name, 'ran')\n"
+            "    except ImportError as e:\n"
+            "        print(name, 'refused:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    lines = r.stdout.strip().splitlines()
+    assert len(lines) == 3 and all("refused:" in ln and "missing" in ln for ln in lines), (r.stdout, r.stderr)
