@@ -8,6 +8,8 @@ and buffers exact, scores within 1e-4 relative, compacted rows byte-identical.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,6 +23,9 @@ import _helpers as H
 from _stream_helpers import check_run
 
 pytestmark = pytest.mark.gpu
+
+# The draws are fixed; BKV_RANDOM_SHAPES_SEED (default 0) offsets every generator's seed, for further sweeps.
+_OFF = int(os.environ.get("BKV_RANDOM_SHAPES_SEED", "0"))
 
 _SRC = {"fps": 0, "initial": L.BKV_BEACON_INITIAL, "random": L.BKV_BEACON_RANDOM}
 
@@ -80,7 +85,7 @@ def _evict_cases(n: int, seed: int) -> list:
     return out
 
 
-EVICT = _evict_cases(40, 20261202)
+EVICT = _evict_cases(40, 20261202 + _OFF)
 
 
 def _id(c) -> str:
@@ -119,7 +124,7 @@ def _buffer_cases(n: int, seed: int) -> list:
     return out
 
 
-BUFFERS = _buffer_cases(16, 4242)
+BUFFERS = _buffer_cases(16, 4242 + _OFF)
 
 
 def _bid(c) -> str:
@@ -208,7 +213,7 @@ def _stream_cases(n: int, seed: int) -> list:
     return out
 
 
-STREAMS = _stream_cases(14, 777)
+STREAMS = _stream_cases(14, 777 + _OFF)
 
 
 def _sid(s) -> str:
@@ -250,7 +255,7 @@ def _prefill_cases(n: int, seed: int) -> list:
     return out
 
 
-PREFILLS = _prefill_cases(24, 99)
+PREFILLS = _prefill_cases(24, 99 + _OFF)
 
 
 def _pid(c) -> str:
