@@ -366,18 +366,26 @@ def stream_bench(args) -> int:
 FP32_MFMA_PEAK_TFS = 157.3   # MI355X dense fp32 matrix rate
 
 
-def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10, name: str = "") -> dict:
+def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10, name: str = "", timing: str = "pristine") -> dict:
     """One sampling round of every buffer: bkv_fps_update with every count at B_Q^max - 1, on a copy of
     the given buffers, timed alone with HIP events (the counts are reset between the timed calls).
+    timing "pristine": before each round (untimed) a 512 MB scratch buffer is read, as the eviction bench
+    does before each step, so that each round starts after memory-bound work, as in a decode stream, where
+    fifteen decode steps separate two rounds; "back-to-back": the rounds follow each other (the chip's clock
+    then drops under the sustained fp32 matrix load).
     Roofline: the Gram matrices are the matrix-core work, 2 n^2 d flops per buffer (all n^2 dot products,
     as the definition takes them; n = B_Q^max), against the dense fp32 MFMA rate."""
     n = b.n_beacon + b.n_recent_q
     qbuf = qbuf_src.clone()
     qc = torch.empty(b.qbufs, dtype=torch.int32, device=qbuf.device)
     stream = torch.cuda.current_stream()
+    scratch = torch.ones(512 << 18, dtype=torch.int32, device=qbuf.device) if timing == "pristine" else None
+    flush_sum = torch.zeros((), dtype=torch.int64, device=qbuf.device)
     ms = []
     for i in range(reps + 2):
         qc.fill_(n - 1)
+        if scratch is not None:
+            flush_sum.copy_(scratch.sum(dtype=torch.int64))   # reads all 512 MB
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         L.fps_update(shape, qbuf, qc, q_new, None, stream=stream)
@@ -388,8 +396,10 @@ def fps_round_bench(b, shape, qbuf_src, q_new, reps: int = 10, name: str = "") -
     t = float(np.mean(ms))
     flops = 2.0 * n * n * b.d * b.qbufs
     achieved = flops / (t * 1e-3) / 1e12
-    del qbuf, qc
-    return {"buffers": b.qbufs, "rows": n, "ms": t, "ms_min": float(min(ms)),
+    if scratch is not None:
+        assert int(flush_sum) == scratch.numel()
+    del qbuf, qc, scratch
+    return {"buffers": b.qbufs, "rows": n, "timing": timing, "ms": t, "ms_min": float(min(ms)),
             "roofline": {"bound": "mfma", "kernel": "fps_kernel (update, every buffer sampling)",
                          "achieved": achieved, "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": achieved / FP32_MFMA_PEAK_TFS, "flops_per_launch": flops,
@@ -432,7 +442,8 @@ def fps_round_main(args) -> int:
     L.load()
     print(f"# fps round {scfg.name}: {b.qbufs} buffers", file=sys.stderr, flush=True)
     q = synth.make_query_buffers(b, device="cuda")
-    r = fps_round_bench(b, L.shape_of(b), q["qbuf"], q["q_new"], reps=args.steps, name=scfg.name)
+    r = fps_round_bench(b, L.shape_of(b), q["qbuf"], q["q_new"], reps=args.steps, name=scfg.name,
+                        timing=args.timing)
     out = {"metric": "FPS sampling round of every query buffer (bkv_fps_update, every buffer full)",
            "value": 1000.0 / r["ms"], "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
            "higher_is_better": True, "dtype": "f32 (bf16 rows)", "data": "synthetic",
@@ -633,7 +644,8 @@ def main() -> int:
     ap.add_argument("--timing", default="pristine", choices=["pristine", "back-to-back"],
                     help="which timing gives value and roofline: pristine (each step on the original cache, the "
                          "MALL flushed before it) or back-to-back (steps in place on the cache the previous one "
-                         "left); both are measured and reported")
+                         "left); both are measured and reported.  With --fps-round: pristine (a 512 MB read before "
+                         "each round) or back-to-back rounds, only the one asked for")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
