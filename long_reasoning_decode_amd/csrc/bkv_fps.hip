@@ -18,7 +18,7 @@ namespace bkv {
 namespace {
 
 constexpr int kWavesPerBlock = 2;        // update and compression
-constexpr int kMergeWavesPerBlock = 4;   // merge
+constexpr int kMergeWavesPerBlock = 2;   // merge
 
 // Wave w of W takes the contiguous buffers [w nbuf / W, (w + 1) nbuf / W),
 // kMaxBuffersPerWave at a time, so every wave has the same share (to one
