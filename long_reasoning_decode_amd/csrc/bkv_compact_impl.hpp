@@ -108,35 +108,66 @@ __device__ __forceinline__ void wg_barrier() {
 // index among them), in windows of NW chunks: wave w moves chunk w of each
 // window.  Every wave's loads of a window complete before any of the window's
 // stores (a wait and a barrier), so no source row is overwritten before it
-// is read.  A window's stores and the next window's loads touch disjoint
-// rows -- the next window's sources lie at or after its destinations, which
-// follow this window's -- so the next loads are issued before this window's
-// stores.  All NW waves, and any other waves of the workgroup, must call it
-// with the same first and B (they meet the same barriers).
+// is read.  A window's stores and the loads of any later window touch
+// disjoint rows -- a later window's sources lie at or after its destinations,
+// which follow this window's -- so each wave keeps two windows of loads in
+// flight: the loads of window n + 2 are issued before the stores of window n
+// (three chunks of registers in rotation).  All NW waves, and any other waves
+// of the workgroup, must call it with the same first and B (they meet the
+// same barriers).
+// load_chunk with every row past B replaced by row B - 1, so that all kPer
+// load instructions issue (the wait counts below rely on it); the extra rows
+// are never stored.
+template <int D>
+__device__ __forceinline__ void load_chunk_all(Chunk<D>& c, const bkv_bf16* X, const uint16_t* src, int r0, int B,
+                                               int lane) {
+#pragma unroll
+    for (int j = 0; j < Chunk<D>::kPer; ++j) {
+        const int p = lane + 64 * j;
+        const int row = min(r0 + p / Chunk<D>::kPieces, B - 1);
+        const int col = p % Chunk<D>::kPieces;
+        c.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(X + (size_t)src[row] * D + col * 8));
+    }
+}
+
+// One window: window a's loads are done in every wave.  Issue the loads of
+// window a + 2 kWin into `nxt`, store window a from `cur`, then wait until
+// this wave's loads of window a + kWin (issued one step earlier) are done
+// and meet at the barrier.  Returns false when window a was the last.
+template <int D, int NW>
+__device__ __forceinline__ bool window_step(Chunk<D>& cur, Chunk<D>& nxt, bkv_bf16* X, const uint16_t* src, int a,
+                                            int B, int w, int lane) {
+    constexpr int kWin = NW * kChunkRows;
+    constexpr int kPer = Chunk<D>::kPer;
+    const bool ahead = a + 2 * kWin < B;
+    if (ahead) load_chunk_all<D>(nxt, X, src, a + 2 * kWin + w * kChunkRows, B, lane);
+    store_chunk<D>(cur, X, a + w * kChunkRows, B, lane);
+    if (a + kWin >= B) return false;
+    // issued after window a + kWin's loads: at least window a's kPer stores (all its rows are below B),
+    // and kPer loads of window a + 2 kWin when ahead
+    if (ahead) wait_vm<2 * kPer>();
+    else wait_vm<kPer>();
+    wg_barrier();
+    return true;
+}
+
 template <int D, int NW>
 __device__ void move_rows_wg(bkv_bf16* X, const uint16_t* src, int first, int B, int w, int lane) {
     if (first >= B) return;
     constexpr int kWin = NW * kChunkRows;
-    constexpr int kPer = Chunk<D>::kPer;
-    Chunk<D> c0, c1;
+    Chunk<D> c0, c1, c2;
     int a = first;
     load_chunk<D>(c0, X, src, a + w * kChunkRows, B, lane);
     wait_vm<0>();
     wg_barrier();
+    if (a + kWin < B) load_chunk<D>(c1, X, src, a + kWin + w * kChunkRows, B, lane);
     while (true) {
-        const int n1 = a + kWin;
-        if (n1 < B) load_chunk<D>(c1, X, src, n1 + w * kChunkRows, B, lane);
-        store_chunk<D>(c0, X, a + w * kChunkRows, B, lane);
-        if (n1 >= B) break;
-        wait_vm<kPer>();   // the window's loads (issued before the kPer stores) are done
-        wg_barrier();
-        const int n2 = n1 + kWin;
-        if (n2 < B) load_chunk<D>(c0, X, src, n2 + w * kChunkRows, B, lane);
-        store_chunk<D>(c1, X, n1 + w * kChunkRows, B, lane);
-        if (n2 >= B) break;
-        wait_vm<kPer>();
-        wg_barrier();
-        a = n2;
+        if (!window_step<D, NW>(c0, c2, X, src, a, B, w, lane)) break;
+        a += kWin;
+        if (!window_step<D, NW>(c1, c0, X, src, a, B, w, lane)) break;
+        a += kWin;
+        if (!window_step<D, NW>(c2, c1, X, src, a, B, w, lane)) break;
+        a += kWin;
     }
 }
 
