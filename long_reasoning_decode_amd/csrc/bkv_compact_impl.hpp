@@ -104,17 +104,6 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Move rows [first, B) of X by NW waves of one workgroup (w = this wave's
-// index among them), in windows of NW chunks: wave w moves chunk w of each
-// window.  Every wave's loads of a window complete before any of the window's
-// stores (a wait and a barrier), so no source row is overwritten before it
-// is read.  A window's stores and the loads of any later window touch
-// disjoint rows -- a later window's sources lie at or after its destinations,
-// which follow this window's -- so each wave keeps two windows of loads in
-// flight: the loads of window n + 2 are issued before the stores of window n
-// (three chunks of registers in rotation).  All NW waves, and any other waves
-// of the workgroup, must call it with the same first and B (they meet the
-// same barriers).
 // load_chunk with every row past B replaced by row B - 1, so that all kPer
 // load instructions issue (the wait counts below rely on it); the extra rows
 // are never stored.
@@ -151,6 +140,17 @@ __device__ __forceinline__ bool window_step(Chunk<D>& cur, Chunk<D>& nxt, bkv_bf
     return true;
 }
 
+// Move rows [first, B) of X by NW waves of one workgroup (w = this wave's
+// index among them), in windows of NW chunks: wave w moves chunk w of each
+// window.  Every wave's loads of a window complete before any of the window's
+// stores (a wait and a barrier), so no source row is overwritten before it
+// is read.  A window's stores and the loads of any later window touch
+// disjoint rows -- a later window's sources lie at or after its destinations,
+// which follow this window's -- so each wave keeps two windows of loads in
+// flight: the loads of window n + 2 are issued before the stores of window n
+// (three chunks of registers in rotation).  All NW waves, and any other waves
+// of the workgroup, must call it with the same first and B (they meet the
+// same barriers).
 template <int D, int NW>
 __device__ void move_rows_wg(bkv_bf16* X, const uint16_t* src, int first, int B, int w, int lane) {
     if (first >= B) return;
